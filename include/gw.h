@@ -1,0 +1,220 @@
+/*
+ * gw.h -- paged hybrid-KV decode attention for MI355X (gfx950), C ABI.
+ *
+ * The operation: batched attention of query rows over paged KV caches of
+ * the two attention families of the Gemma 4 hybrid stack (pegainfer
+ * "Gemma 4" page, intro and Architecture notes):
+ *   - local layers: sliding window (1024 tokens), head dim 256, grouped
+ *     query heads (16 q heads over 8 KV heads), K rotated on all 256 dims
+ *     (theta 1e4); K/V stored as bf16, or as e4m3 at scale 1.0 (pegainfer
+ *     PR #1012, Description);
+ *   - global layers: whole context, head dim 512, one KV head shared by
+ *     every q head; K and V are tied and only the first 128 dims of K are
+ *     rotated (theta 1e6, frequency denominator 512), so a page may store V
+ *     plus the rotated quarter of K only -- 0.625x the bytes -- and K is
+ *     rebuilt exactly inside the kernel (Gewell post, "the Why").
+ * Both families use 16-token pages and one page table each (pegainfer
+ * "Gemma 4" page, Scheduling).
+ *
+ * Conventions for every entry point:
+ *   - All pointer arguments are DEVICE pointers unless marked (host).
+ *   - The caller owns all memory: the library never allocates or frees
+ *     device memory and never synchronizes.  Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL = the legacy default stream).
+ *   - Every host-checkable argument is validated before any HIP call; a
+ *     rejected call returns a negative gw_status and launches nothing.
+ *   - gw_last_error() then holds a message that starts with the name of the
+ *     entry point that ran (thread-local; valid until the next call on the
+ *     same thread).
+ *   - Device-resident preconditions are the caller's contract and are not
+ *     checked: seq_lens[s] >= 1; every page a call touches has a valid
+ *     page-table entry in [0, num_pages); no two tokens of one append call
+ *     write the same slot; positions < the rotary table length.
+ *   - Reentrant; no mutable global state beyond the thread-local message.
+ */
+#ifndef GW_H
+#define GW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+typedef enum gw_status {
+  GW_OK = 0,
+  GW_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum value   */
+  GW_ERR_UNSUPPORTED = -2, /* valid but not served (e.g. e4m3 global pool)  */
+  GW_ERR_GEOMETRY = -3,    /* shape does not match the family's layout      */
+  GW_ERR_WORKSPACE = -4,   /* workspace smaller than gw_attn_workspace_bytes */
+  GW_ERR_HIP = -5          /* a HIP launch failed; message has the reason   */
+} gw_status;
+
+/* --------------------------------------------------------------- enums -- */
+/* No zero value on purpose: an unset field is rejected, never defaulted. */
+typedef enum gw_family {
+  GW_FAMILY_LOCAL = 1,             /* sliding-window local layers           */
+  GW_FAMILY_GLOBAL_COMPRESSED = 2, /* global layers, V + rotated K quarter  */
+  GW_FAMILY_GLOBAL_FULL = 3        /* global layers, full K and V records   */
+} gw_family;
+
+typedef enum gw_kv_dtype {
+  GW_KV_BF16 = 1, /* 2-byte bfloat16                                        */
+  GW_KV_E4M3 = 2  /* 1-byte OCP e4m3 (E4M3FN), scale 1.0; local family only */
+} gw_kv_dtype;
+
+/* ------------------------------------------------------------ the pool -- */
+/*
+ * One layer's paged KV pool.  `base` points at num_pages * page_bytes bytes
+ * (gw_pool_page_bytes).  Logical token t of a sequence lives in physical page
+ * page_table[seq * pt_stride + t / 16] at slot t % 16.
+ *
+ * Geometry served:
+ *   LOCAL:             page_size 16, head_dim 256, rot_dim 256 (or 0 = K is
+ *                      stored as given), num_kv_heads >= 1, bf16 or e4m3.
+ *   GLOBAL_COMPRESSED: page_size 16, head_dim 512, rot_dim 128, one KV head,
+ *                      bf16.
+ *   GLOBAL_FULL:       as GLOBAL_COMPRESSED.
+ *
+ * Element order inside a page (elements of kv_dtype):
+ *   LOCAL page = [num_kv_heads][K block, V block], block = 16 x 256:
+ *     bf16 K: element ((k*16 + t)*4 + c)*8 + e   holds K[t][64c + 8k + e]
+ *             (k < 8, t < 16, c < 4, e < 8)
+ *     bf16 V: element ((u*64 + l)*4 + j)*2 + i   holds V[2u + i][4l + j]
+ *             (u < 8, l < 64, j < 4, i < 2)
+ *     e4m3 K: element ((k*16 + t)*4 + c)*16 + e  holds K[t][64c + 16k + e]
+ *             (k < 4, t < 16, c < 4, e < 16)
+ *     e4m3 V: element ((u*64 + l)*4 + j)*4 + i   holds V[4u + i][4l + j]
+ *             (u < 4, l < 64, j < 4, i < 4)
+ *   GLOBAL_COMPRESSED page = V block [16][512], then K_rot block [16][128]
+ *   GLOBAL_FULL page       = K block [16][512], then V block [16][512]
+ *     each block chunk-major: element (c*16 + t)*8 + e holds X[t][8c + e].
+ * (The orders put the 16 bytes one GPU lane loads next to the 16 bytes its
+ * neighbour lane loads, so every page is read with whole 1 KiB wave loads.)
+ */
+typedef struct gw_pool_desc {
+  int32_t family;       /* gw_family                                      */
+  int32_t kv_dtype;     /* gw_kv_dtype                                    */
+  int32_t page_size;    /* tokens per page; must be 16                    */
+  int32_t num_kv_heads; /* local: >= 1; global: 1                         */
+  int32_t head_dim;     /* local: 256; global: 512                        */
+  int32_t rot_dim;      /* rotated dims of K: local 256 or 0; global 128  */
+  int64_t num_pages;    /* physical pages behind base                     */
+  void* base;           /* device pointer to page 0                       */
+} gw_pool_desc;
+
+/* ------------------------------------------------------------- queries -- */
+/* Library version string (static storage). */
+const char* gw_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gw_last_error(void);
+
+/*
+ * Bytes of one physical page of `pool` (host-only; no HIP call), or a
+ * negative gw_status if the descriptor is invalid.  LOCAL: 16 * 2 *
+ * num_kv_heads * 256 * elem_bytes; GLOBAL_COMPRESSED: 16 * 640 * 2;
+ * GLOBAL_FULL: 16 * 1024 * 2 (Gewell post, "the Why": 640/1024 = 0.625).
+ */
+int64_t gw_pool_page_bytes(const gw_pool_desc* pool /* host */);
+
+/* --------------------------------------------------------- rotary table -- */
+/*
+ * Fill cos/sin tables for RoPE (pegainfer "Gemma 4" page, Architecture
+ * notes: local "full 256, theta 10k"; global "proportional 128/512, theta
+ * 1M", the frequency denominator staying the full head dimension):
+ *   cos_out[p * (rot_dim/2) + i] = cos(p * theta^(-2i/head_dim)), i < rot_dim/2
+ *   sin_out[...]                 = sin(...)
+ * for p in [0, max_pos), computed in fp64 on the device, stored as fp32.
+ * rot_dim even, 2 <= rot_dim <= head_dim, theta > 0, max_pos >= 1.
+ */
+int gw_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t rot_dim,
+                  int32_t head_dim, double theta, void* stream);
+
+/* --------------------------------------------------------------- append -- */
+/*
+ * Write n_tok new tokens' K/V into `pool` (the prep step before attention:
+ * pegainfer PR #1012, Description -- the prep kernel rotates and stores K/V
+ * with the store type as a parameter; Gewell post, "the Why" -- the global
+ * record is V plus the rotated quarter of K).
+ *
+ *   k_raw : bf16 [n_tok][num_kv_heads][head_dim], K before rotation.
+ *           LOCAL only; must be NULL for the GLOBAL families (K is V).
+ *   v     : bf16 [n_tok][num_kv_heads][head_dim].
+ *   seq_idx, pos : int32 [n_tok]; token i goes to sequence seq_idx[i] at
+ *           position pos[i], i.e. page page_table[seq_idx[i]*pt_stride +
+ *           pos[i]/16], slot pos[i] % 16.
+ *   rope_cos, rope_sin : fp32 [max_pos][rot_dim/2] from gw_rope_table, or
+ *           both NULL to store K unrotated (LOCAL with rot_dim 0 requires
+ *           NULL; rot_dim > 0 requires tables).
+ * Per element, in fp32: rotate the first rot_dim dims of K as pairs
+ * (i, i + rot_dim/2) by angle pos*inv_freq_i:
+ *   y_i = x_i*cos - x_{i+R/2}*sin,  y_{i+R/2} = x_{i+R/2}*cos + x_i*sin,
+ * round to bf16 (nearest-even); for e4m3 round that bf16 value once more to
+ * e4m3 (nearest-even, saturating to +-448, NaN kept).
+ *   LOCAL:             K block <- rotated K, V block <- V.
+ *   GLOBAL_COMPRESSED: V block <- V, K_rot block <- rotated V[0:128].
+ *   GLOBAL_FULL:       K block <- [rotated V[0:128], V[128:512]], V <- V.
+ * E4M3 with a GLOBAL family: GW_ERR_UNSUPPORTED ("gw_kv_append: e4m3
+ * supports only the local family").  n_tok == 0 is a no-op returning GW_OK.
+ */
+int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const void* v,
+                 const int32_t* seq_idx, const int32_t* pos, int32_t n_tok,
+                 const int32_t* page_table, int32_t pt_stride, const float* rope_cos,
+                 const float* rope_sin, void* stream);
+
+/* ------------------------------------------------------------ attention -- */
+/*
+ * Query rows and sequences (pegainfer "Gemma 4" page, Scheduling: every
+ * active request advances one token per step, and a new prompt's rows are
+ * computed in the same step):
+ *   num_seqs sequences; sequence s has seq_lens[s] tokens in the pool (its
+ *   current tokens included) and q_len_s = q_indptr[s+1] - q_indptr[s] query
+ *   rows, rows q_indptr[s] .. q_indptr[s+1]-1, the last q_len_s tokens of the
+ *   sequence: row r of s is at position seq_lens[s] - q_len_s + r.
+ *   q_indptr NULL means one row per sequence (num_rows == num_seqs).
+ *   A row at position p attends keys j with lo <= j <= p, lo = max(0,
+ *   p - window + 1) for LOCAL and 0 for GLOBAL; q head h reads KV head
+ *   h / (num_q_heads / num_kv_heads).
+ *   out[row][h][:] = sum_j softmax_j(scale * q[row][h] . K[j]) V[j], fp32.
+ * Host sizing arguments (upper bounds used to size grids; a device value
+ * beyond them is a contract violation): num_rows = q_indptr[num_seqs];
+ * max_q_len >= every q_len_s; max_seq_len >= every seq_lens[s].
+ *
+ *   q   : bf16 [num_rows][num_q_heads][head_dim], already rotated.
+ *   out : fp32 [num_rows][num_q_heads][head_dim].
+ *   workspace : at least gw_attn_workspace_bytes(...) bytes (may be NULL
+ *   when that is 0), 256-byte aligned; contents on entry are ignored.
+ *
+ * Results are deterministic, and each row's result depends only on that
+ * row's query, its sequence's length and K/V, the window and the scale --
+ * not on the other rows of the call, their order, or where pages sit.
+ */
+size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_rows,
+                               int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                               int32_t window, int32_t max_q_len);
+
+/* Local family (pool->family == GW_FAMILY_LOCAL; bf16 or e4m3).
+ * num_q_heads a multiple of num_kv_heads, group size 1, 2 or 4; window >= 1. */
+int gw_decode_attn_local(const gw_pool_desc* pool /* host */, const void* q,
+                         int32_t num_q_heads, const int32_t* q_indptr, const int32_t* seq_lens,
+                         const int32_t* page_table, int32_t pt_stride, int32_t num_seqs,
+                         int32_t num_rows, int32_t max_q_len, int32_t max_seq_len,
+                         int32_t window, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16).
+ * num_q_heads 16 or 32.  The two layouts give bit-identical results. */
+int gw_decode_attn_global(const gw_pool_desc* pool /* host */, const void* q,
+                          int32_t num_q_heads, const int32_t* q_indptr, const int32_t* seq_lens,
+                          const int32_t* page_table, int32_t pt_stride, int32_t num_seqs,
+                          int32_t num_rows, int32_t max_q_len, int32_t max_seq_len, float scale,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GW_H */

@@ -67,29 +67,42 @@ def attend(q, K, V, q_pos, scale: float, window: int | None = None,
     assert (q_pos < L).all() and (q_pos >= 0).all()
 
     out = np.empty((R, Hq, D), dtype=np.float64)
-    weights = np.empty((R, Hq, L), dtype=np.float64) if return_weights else None
-    j = np.arange(L)
-    # rows in blocks so that the materialised logits stay bounded in memory
+    weights = np.zeros((R, Hq, L), dtype=np.float64) if return_weights else None
+    lo_all = np.array([window_lo(int(p), window) for p in q_pos], dtype=np.int64)
+    # Only keys inside a row's own range [lo, p] enter its sum; keys outside
+    # are never read, so unwritten (NaN) slots elsewhere cannot leak in.
+    # Rows go in blocks over the union of their ranges; a block whose union
+    # holds a non-finite key or value falls back to one row at a time.
     rows_per_block = max(1, max_elems // max(1, Hq * L))
     for r0 in range(0, R, rows_per_block):
         r1 = min(R, r0 + rows_per_block)
-        pos = q_pos[r0:r1]
-        lo = np.array([window_lo(int(p), window) for p in pos])
-        allowed = (j[None, :] >= lo[:, None]) & (j[None, :] <= pos[:, None])  # [r, L]
-        for g in range(Hkv):
-            qg = q[r0:r1, g * G:(g + 1) * G, :]               # [r, G, D]
-            Kg = K[:, g, :]                                    # [L, D]
-            z = scale * (qg @ Kg.T)                            # [r, G, L]
-            z = np.where(allowed[:, None, :], z, -np.inf)
-            zmax = z.max(axis=-1, keepdims=True)
-            e = np.exp(z - zmax)                               # exactly 0 where masked
-            w = e / e.sum(axis=-1, keepdims=True)
-            out[r0:r1, g * G:(g + 1) * G, :] = w @ V[:, g, :]
-            if return_weights:
-                weights[r0:r1, g * G:(g + 1) * G, :] = w
+        ja, jb = int(lo_all[r0:r1].min()), int(q_pos[r0:r1].max()) + 1
+        if np.isfinite(K[ja:jb]).all() and np.isfinite(V[ja:jb]).all():
+            _attend_block(q, K, V, q_pos, lo_all, scale, G, r0, r1, ja, jb, out, weights)
+        else:
+            for r in range(r0, r1):
+                _attend_block(q, K, V, q_pos, lo_all, scale, G, r, r + 1,
+                              int(lo_all[r]), int(q_pos[r]) + 1, out, weights)
     if return_weights:
         return out, weights
     return out
+
+
+def _attend_block(q, K, V, q_pos, lo_all, scale, G, r0, r1, ja, jb, out, weights):
+    """Rows r0..r1-1 over keys ja..jb-1 (the union of their ranges)."""
+    Hkv = K.shape[1]
+    j = np.arange(ja, jb)
+    allowed = (j[None, :] >= lo_all[r0:r1, None]) & (j[None, :] <= q_pos[r0:r1, None])  # [r, n]
+    for g in range(Hkv):
+        qg = q[r0:r1, g * G:(g + 1) * G, :]               # [r, G, D]
+        z = scale * (qg @ K[ja:jb, g, :].T)               # [r, G, n]
+        z = np.where(allowed[:, None, :], z, -np.inf)
+        zmax = z.max(axis=-1, keepdims=True)
+        e = np.exp(z - zmax)                              # exactly 0 where masked
+        w = e / e.sum(axis=-1, keepdims=True)
+        out[r0:r1, g * G:(g + 1) * G, :] = w @ V[ja:jb, g, :]
+        if weights is not None:
+            weights[r0:r1, g * G:(g + 1) * G, ja:jb] = w
 
 
 def attend_scalar(q, K, V, q_pos, scale: float, window: int | None = None):

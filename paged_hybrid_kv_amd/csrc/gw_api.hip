@@ -1,0 +1,334 @@
+// C ABI of the gw library: argument validation (before any HIP call), split
+// planning and kernel launches.  Declarations and contracts: include/gw.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gw.h"
+#include "gw_kernels.h"
+#include "gw_plan.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fn, const char* fmt, ...) {
+  int n = snprintf(g_err, sizeof(g_err), "%s: ", fn);
+  if (n < 0) n = 0;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err + n, sizeof(g_err) - (size_t)n, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GW_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_local(int f) { return f == GW_FAMILY_LOCAL; }
+bool is_global(int f) { return f == GW_FAMILY_GLOBAL_COMPRESSED || f == GW_FAMILY_GLOBAL_FULL; }
+
+// Geometry of a descriptor, without looking at base / num_pages.
+int check_geometry(const gw_pool_desc* p, const char* fn) {
+  if (!p) return fail(GW_ERR_INVALID_ARG, fn, "pool descriptor is null");
+  if (!is_local(p->family) && !is_global(p->family))
+    return fail(GW_ERR_INVALID_ARG, fn, "unknown family %d", p->family);
+  switch (p->kv_dtype) {
+    case GW_KV_BF16:
+    case GW_KV_E4M3:
+      break;
+    default:
+      return fail(GW_ERR_INVALID_ARG, fn, "unknown kv_dtype %d", p->kv_dtype);
+  }
+  if (p->page_size != 16) return fail(GW_ERR_GEOMETRY, fn, "page_size %d (must be 16)", p->page_size);
+  if (is_local(p->family)) {
+    if (p->head_dim != 256) return fail(GW_ERR_GEOMETRY, fn, "local head_dim %d (must be 256)", p->head_dim);
+    if (p->rot_dim != 0 && p->rot_dim != 256)
+      return fail(GW_ERR_GEOMETRY, fn, "local rot_dim %d (must be 256 or 0)", p->rot_dim);
+    if (p->num_kv_heads < 1 || p->num_kv_heads > 65535)
+      return fail(GW_ERR_GEOMETRY, fn, "local num_kv_heads %d", p->num_kv_heads);
+  } else {
+    if (p->kv_dtype != GW_KV_BF16)
+      return fail(GW_ERR_UNSUPPORTED, fn, "e4m3 supports only the local family");
+    if (p->head_dim != 512) return fail(GW_ERR_GEOMETRY, fn, "global head_dim %d (must be 512)", p->head_dim);
+    if (p->rot_dim != 128) return fail(GW_ERR_GEOMETRY, fn, "global rot_dim %d (must be 128)", p->rot_dim);
+    if (p->num_kv_heads != 1)
+      return fail(GW_ERR_GEOMETRY, fn, "global num_kv_heads %d (must be 1)", p->num_kv_heads);
+  }
+  return GW_OK;
+}
+
+int64_t page_bytes_of(const gw_pool_desc* p) {
+  const int64_t eb = p->kv_dtype == GW_KV_E4M3 ? 1 : 2;
+  switch (p->family) {
+    case GW_FAMILY_LOCAL: return 16LL * 2 * p->num_kv_heads * 256 * eb;
+    case GW_FAMILY_GLOBAL_COMPRESSED: return 16LL * (512 + 128) * 2;
+    case GW_FAMILY_GLOBAL_FULL: return 16LL * 1024 * 2;
+  }
+  return -1;
+}
+
+int check_pool(const gw_pool_desc* p, const char* fn) {
+  int rc = check_geometry(p, fn);
+  if (rc != GW_OK) return rc;
+  if (!p->base) return fail(GW_ERR_INVALID_ARG, fn, "pool base is null");
+  if (p->num_pages < 1) return fail(GW_ERR_INVALID_ARG, fn, "num_pages %lld", (long long)p->num_pages);
+  return GW_OK;
+}
+
+// Largest split count of any decode row of a call.
+int max_splits_for(int family, int max_seq_len, int window) {
+  if (family == GW_FAMILY_LOCAL) return gw::local_nsplit(gw::local_max_range_pages(max_seq_len, window));
+  const int tiles = gw::cdiv_i(gw::cdiv_i(max_seq_len, 16), gw::kGlobalTilePages);
+  return gw::global_nsplit(tiles);
+}
+
+struct WsPlan {
+  int max_splits;
+  size_t acc_bytes, ml_bytes, total;
+};
+
+WsPlan plan_workspace(int family, int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                      int window) {
+  WsPlan w{};
+  w.max_splits = max_splits_for(family, max_seq_len, window);
+  if (w.max_splits <= 1 || num_seqs <= 0) return w;
+  const size_t units = (size_t)num_seqs * num_q_heads * w.max_splits;
+  w.acc_bytes = align_up(units * head_dim * sizeof(float));
+  w.ml_bytes = align_up(units * 2 * sizeof(float));
+  w.total = w.acc_bytes + w.ml_bytes;
+  return w;
+}
+
+// Arguments common to both attention entry points.
+int check_attn_common(const char* fn, const void* q, int num_q_heads, const int32_t* q_indptr,
+                      const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
+                      int num_seqs, int num_rows, int max_q_len, int max_seq_len, float scale,
+                      const float* out) {
+  if (num_seqs < 0 || num_seqs > 65535) return fail(GW_ERR_INVALID_ARG, fn, "num_seqs %d", num_seqs);
+  if (num_rows < 0) return fail(GW_ERR_INVALID_ARG, fn, "num_rows %d", num_rows);
+  if (num_q_heads < 1) return fail(GW_ERR_INVALID_ARG, fn, "num_q_heads %d", num_q_heads);
+  if (max_q_len < 1) return fail(GW_ERR_INVALID_ARG, fn, "max_q_len %d", max_q_len);
+  if (max_seq_len < 1) return fail(GW_ERR_INVALID_ARG, fn, "max_seq_len %d", max_seq_len);
+  if (max_q_len > max_seq_len)
+    return fail(GW_ERR_INVALID_ARG, fn, "max_q_len %d exceeds max_seq_len %d", max_q_len, max_seq_len);
+  if (!isfinite(scale)) return fail(GW_ERR_INVALID_ARG, fn, "scale is not finite");
+  if (!q_indptr && num_rows != num_seqs)
+    return fail(GW_ERR_INVALID_ARG, fn, "q_indptr is null but num_rows %d != num_seqs %d", num_rows, num_seqs);
+  if (!q_indptr && max_q_len != 1)
+    return fail(GW_ERR_INVALID_ARG, fn, "q_indptr is null but max_q_len %d != 1", max_q_len);
+  if (max_q_len > 1)
+    return fail(GW_ERR_UNSUPPORTED, fn, "query rows with q_len > 1 are not served by this build");
+  if (pt_stride < gw::cdiv_i(max_seq_len, 16))
+    return fail(GW_ERR_INVALID_ARG, fn, "pt_stride %d < pages of max_seq_len %d", pt_stride, max_seq_len);
+  if (num_seqs == 0 || num_rows == 0) return GW_OK;
+  if (!q || !seq_lens || !page_table || !out)
+    return fail(GW_ERR_INVALID_ARG, fn, "null q, seq_lens, page_table or out");
+  return GW_OK;
+}
+
+int hip_fail(const char* fn, hipError_t e) {
+  return fail(GW_ERR_HIP, fn, "%s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gw_version(void) { return "gw 0.1.0 (gfx950, paged hybrid-KV decode attention)"; }
+
+const char* gw_last_error(void) { return g_err; }
+
+int64_t gw_pool_page_bytes(const gw_pool_desc* pool) {
+  int rc = check_geometry(pool, "gw_pool_page_bytes");
+  if (rc != GW_OK) return rc;
+  ok();
+  return page_bytes_of(pool);
+}
+
+int gw_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t rot_dim, int32_t head_dim,
+                  double theta, void* stream) {
+  const char* fn = "gw_rope_table";
+  if (!cos_out || !sin_out) return fail(GW_ERR_INVALID_ARG, fn, "null output table");
+  if (max_pos < 1) return fail(GW_ERR_INVALID_ARG, fn, "max_pos %d", max_pos);
+  if (rot_dim < 2 || (rot_dim & 1) || rot_dim > head_dim)
+    return fail(GW_ERR_INVALID_ARG, fn, "rot_dim %d with head_dim %d", rot_dim, head_dim);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(GW_ERR_INVALID_ARG, fn, "theta must be > 0");
+  hipError_t e = gw::launch_rope_table(cos_out, sin_out, max_pos, rot_dim, head_dim, theta,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int gw_kv_append(const gw_pool_desc* pool, const void* k_raw, const void* v, const int32_t* seq_idx,
+                 const int32_t* pos, int32_t n_tok, const int32_t* page_table, int32_t pt_stride,
+                 const float* rope_cos, const float* rope_sin, void* stream) {
+  const char* fn = "gw_kv_append";
+  int rc = check_pool(pool, fn);
+  if (rc != GW_OK) return rc;
+  if (n_tok < 0) return fail(GW_ERR_INVALID_ARG, fn, "n_tok %d", n_tok);
+  if (pt_stride < 1) return fail(GW_ERR_INVALID_ARG, fn, "pt_stride %d", pt_stride);
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
+  const bool rope = rope_cos != nullptr;
+  if (is_local(pool->family)) {
+    if (pool->rot_dim == 0 && rope)
+      return fail(GW_ERR_INVALID_ARG, fn, "rot_dim 0 takes no rotary tables");
+    if (pool->rot_dim != 0 && !rope)
+      return fail(GW_ERR_INVALID_ARG, fn, "rot_dim %d needs rotary tables", pool->rot_dim);
+  } else {
+    if (k_raw) return fail(GW_ERR_INVALID_ARG, fn, "k_raw must be null for the global family (K is V)");
+    if (!rope) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
+  }
+  if (n_tok == 0) return ok();
+  if (!v || !seq_idx || !pos || !page_table)
+    return fail(GW_ERR_INVALID_ARG, fn, "null v, seq_idx, pos or page_table");
+  if (is_local(pool->family) && !k_raw) return fail(GW_ERR_INVALID_ARG, fn, "k_raw is null");
+
+  gw::AppendArgs a{};
+  a.pool = static_cast<uint8_t*>(pool->base);
+  a.page_bytes = page_bytes_of(pool);
+  a.head_bytes = (int32_t)(a.page_bytes / pool->num_kv_heads);
+  a.k_raw = static_cast<const uint16_t*>(k_raw);
+  a.v = static_cast<const uint16_t*>(v);
+  a.seq_idx = seq_idx;
+  a.pos = pos;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.n_tok = n_tok;
+  a.num_kv_heads = pool->num_kv_heads;
+  hipError_t e;
+  if (is_local(pool->family))
+    e = gw::launch_append_local(a, pool->kv_dtype == GW_KV_E4M3, rope, (hipStream_t)stream);
+  else
+    e = gw::launch_append_global(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_rows, int32_t num_q_heads,
+                               int32_t head_dim, int32_t max_seq_len, int32_t window, int32_t max_q_len) {
+  (void)num_rows;
+  (void)max_q_len;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+  if (family == GW_FAMILY_LOCAL && window < 1) return 0;
+  if (!is_local(family) && !is_global(family)) return 0;
+  return plan_workspace(family, num_seqs, num_q_heads, head_dim, max_seq_len, window).total;
+}
+
+int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+                         const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
+                         int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                         int32_t max_seq_len, int32_t window, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const char* fn = "gw_decode_attn_local";
+  int rc = check_pool(pool, fn);
+  if (rc != GW_OK) return rc;
+  if (!is_local(pool->family))
+    return fail(GW_ERR_INVALID_ARG, fn, "pool family %d is not GW_FAMILY_LOCAL", pool->family);
+  if (window < 1) return fail(GW_ERR_INVALID_ARG, fn, "window %d (must be >= 1)", window);
+  rc = check_attn_common(fn, q, num_q_heads, q_indptr, seq_lens, page_table, pt_stride, num_seqs,
+                         num_rows, max_q_len, max_seq_len, scale, out);
+  if (rc != GW_OK) return rc;
+  if (num_q_heads % pool->num_kv_heads != 0)
+    return fail(GW_ERR_GEOMETRY, fn, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4)
+    return fail(GW_ERR_UNSUPPORTED, fn, "query group size %d (served: 1, 2, 4)", group);
+  const WsPlan w = plan_workspace(GW_FAMILY_LOCAL, num_seqs, num_q_heads, 256, max_seq_len, window);
+  if (workspace_bytes < w.total)
+    return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+  if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
+  if (w.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
+    return fail(GW_ERR_INVALID_ARG, fn, "workspace is not 256-byte aligned");
+  if (num_seqs == 0 || num_rows == 0) return ok();
+
+  gw::LocalAttnArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.page_bytes = page_bytes_of(pool);
+  a.head_bytes = (int32_t)(a.page_bytes / pool->num_kv_heads);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_indptr = q_indptr;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.window = window;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.part_acc = static_cast<float*>(workspace);
+  a.part_ml = w.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_bytes) : nullptr;
+  a.max_splits = w.max_splits;
+  a.num_seqs = num_seqs;
+  (void)hipGetLastError();   // a stale error from earlier work is not ours to report
+  hipError_t e = gw::launch_local_decode(a, group, pool->kv_dtype == GW_KV_E4M3, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (w.max_splits > 1) {
+    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, 256, w.max_splits, window};
+    e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+                          const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
+                          int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                          int32_t max_seq_len, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const char* fn = "gw_decode_attn_global";
+  int rc = check_pool(pool, fn);
+  if (rc != GW_OK) return rc;
+  if (!is_global(pool->family))
+    return fail(GW_ERR_INVALID_ARG, fn, "pool family %d is not a global family", pool->family);
+  rc = check_attn_common(fn, q, num_q_heads, q_indptr, seq_lens, page_table, pt_stride, num_seqs,
+                         num_rows, max_q_len, max_seq_len, scale, out);
+  if (rc != GW_OK) return rc;
+  if (num_q_heads != 16 && num_q_heads != 32)
+    return fail(GW_ERR_UNSUPPORTED, fn, "num_q_heads %d (served: 16, 32)", num_q_heads);
+  const WsPlan w = plan_workspace(pool->family, num_seqs, num_q_heads, 512, max_seq_len, 0);
+  if (workspace_bytes < w.total)
+    return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+  if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
+  if (w.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
+    return fail(GW_ERR_INVALID_ARG, fn, "workspace is not 256-byte aligned");
+  if (num_seqs == 0 || num_rows == 0) return ok();
+
+  gw::GlobalAttnArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.page_bytes = page_bytes_of(pool);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_indptr = q_indptr;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.num_q_heads = num_q_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.part_acc = static_cast<float*>(workspace);
+  a.part_ml = w.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_bytes) : nullptr;
+  a.max_splits = w.max_splits;
+  a.num_seqs = num_seqs;
+  (void)hipGetLastError();
+  hipError_t e = gw::launch_global_decode(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (w.max_splits > 1) {
+    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, 512, w.max_splits, 0};
+    e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+}  // extern "C"

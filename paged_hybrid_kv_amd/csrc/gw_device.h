@@ -1,0 +1,98 @@
+// Device helpers shared by the gw kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gw {
+
+constexpr int kPage = 16;        // tokens per page, both families
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 1/ln(2): softmax runs in base 2, z = s * scale * log2(e).
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 pair (low half = first element) -> two floats, exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return bits_to_f32(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return bits_to_f32(p & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// Two e4m3 bytes of a dword (word 0: bytes 0,1; word 1: bytes 2,3) -> packed
+// bf16 pair, exactly (every e4m3 value is a bf16 value).
+template <bool kHiWord>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHiWord);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// fp32 (already a bf16 value) -> e4m3 code: nearest even, saturating to
+// +-448, NaN -> 0x7f | sign.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = f32_to_bits(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 24) & 0x80u) | 0x7fu;
+  float c = fminf(fmaxf(x, -448.0f), 448.0f);
+  int packed = __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false);
+  return (uint32_t)packed & 0xffu;
+}
+
+// Round a float to bf16 and back (nearest even), as the stores do.
+__device__ __forceinline__ float round_bf16(float x) {
+  return bf16_lo(pack_bf16(x, 0.0f));
+}
+
+// Cross-lane moves.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_to_bits(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int m) {
+  return bits_to_f32((uint32_t)__shfl_xor((int)f32_to_bits(x), m, kWave));
+}
+__device__ __forceinline__ float shfl_down_f32(float x, int d) {
+  return bits_to_f32((uint32_t)__shfl_down((int)f32_to_bits(x), d, kWave));
+}
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+__device__ __forceinline__ int uniform_i32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Streaming 16-byte load (KV pages are read once per call).
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint4 ld16_cached(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
+__device__ __forceinline__ int split_lo(int n, int k, int i) {
+  return (int)(((long long)n * i) / k);
+}
+
+}  // namespace gw

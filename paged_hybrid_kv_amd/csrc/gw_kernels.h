@@ -1,0 +1,84 @@
+// Internal launch interface between the C ABI (gw_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gw {
+
+struct LocalAttnArgs {
+  const uint8_t* pool;        // page 0 of the layer's local pool
+  int64_t page_bytes;         // bytes per physical page
+  int32_t head_bytes;         // bytes per (page, KV head): K block + V block
+  const uint16_t* q;          // bf16 [rows][Hq][256]
+  const int32_t* q_indptr;    // [S+1] or null (one row per sequence)
+  const int32_t* seq_lens;    // [S]
+  const int32_t* page_table;  // [S][pt_stride]
+  int32_t pt_stride;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t window;
+  float scale_log2;           // softmax scale * log2(e)
+  float* out;                 // fp32 [rows][Hq][256]
+  float* part_acc;            // fp32 [S][Hq][max_splits][256]
+  float* part_ml;             // fp32 [S][Hq][max_splits][2]: (max, sum) in base 2
+  int32_t max_splits;
+  int32_t num_seqs;
+};
+
+struct GlobalAttnArgs {
+  const uint8_t* pool;
+  int64_t page_bytes;         // 20480 compressed, 32768 full
+  const uint16_t* q;          // bf16 [rows][Hq][512]
+  const int32_t* q_indptr;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  int32_t num_q_heads;        // 16 or 32
+  float scale_log2;
+  float* out;                 // fp32 [rows][Hq][512]
+  float* part_acc;            // fp32 [S][Hq][max_splits][512]
+  float* part_ml;             // fp32 [S][Hq][max_splits][2]
+  int32_t max_splits;
+  int32_t num_seqs;
+};
+
+struct ReduceArgs {
+  const int32_t* q_indptr;
+  const int32_t* seq_lens;
+  const float* part_acc;
+  const float* part_ml;
+  float* out;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t max_splits;
+  int32_t window;             // local family; <= 0 for the global family
+};
+
+struct AppendArgs {
+  uint8_t* pool;
+  int64_t page_bytes;
+  int32_t head_bytes;         // local: bytes per (page, KV head)
+  const uint16_t* k_raw;      // bf16 [n][Hkv][D] (local only)
+  const uint16_t* v;          // bf16 [n][Hkv][D]
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  const float* rope_cos;      // [max_pos][rot/2] or null
+  const float* rope_sin;
+  int32_t n_tok;
+  int32_t num_kv_heads;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the
+// hipGetLastError() status of the launch.
+hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream);
+hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream);
+hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream);
+hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStream_t stream);
+hipError_t launch_append_global(const AppendArgs& a, bool compressed, hipStream_t stream);
+hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int rot_dim,
+                             int head_dim, double theta, hipStream_t stream);
+
+}  // namespace gw

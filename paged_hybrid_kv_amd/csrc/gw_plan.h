@@ -1,0 +1,50 @@
+// Split plan shared by host (grid and workspace sizing) and device (what each
+// workgroup does).  A row's plan depends only on the number of pages its own
+// attended range covers, never on the other rows of the call, their order or
+// where pages sit, so every row's result is the same whatever batch it is in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gw {
+
+// Local family: ranges up to the window (65 pages at window 1024) cut into
+// splits of at least 16 pages: 5 splits x 13 pages for a full window.
+constexpr int kLocalMinPagesPerSplit = 16;
+constexpr int kLocalMaxSplits = 16;
+
+// Global family: 2-page tiles (32 tokens); splits of at least 8 tiles
+// (256 tokens), at most 64 per row -- 16..64 splits at 4K..128K tokens.
+constexpr int kGlobalTilePages = 2;
+constexpr int kGlobalMinTilesPerSplit = 8;
+constexpr int kGlobalMaxSplits = 64;
+
+__host__ __device__ inline int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+
+__host__ __device__ inline int local_nsplit(int n_pages) {
+  int k = cdiv_i(n_pages, kLocalMinPagesPerSplit);
+  k = k < 1 ? 1 : k;
+  return k > kLocalMaxSplits ? kLocalMaxSplits : k;
+}
+
+__host__ __device__ inline int global_nsplit(int n_tiles) {
+  int k = cdiv_i(n_tiles, kGlobalMinTilesPerSplit);
+  k = k < 1 ? 1 : k;
+  return k > kGlobalMaxSplits ? kGlobalMaxSplits : k;
+}
+
+// Pages touched by the window of a query at position p: [p_lo/16, p/16].
+__host__ __device__ inline int local_range_pages(int p, int window) {
+  int lo = p - window + 1;
+  lo = lo < 0 ? 0 : lo;
+  return p / 16 - lo / 16 + 1;
+}
+
+// Upper bound on pages of any local decode range for sequences <= max_len.
+inline int local_max_range_pages(int max_len, int window) {
+  int w = window < max_len ? window : max_len;
+  // a w-token range starting mid-page spans at most cdiv(w - 1, 16) + 1 pages
+  return cdiv_i(w - 1, 16) + 1;
+}
+
+}  // namespace gw

@@ -1,0 +1,184 @@
+"""The C-ABI library loads, exports every symbol include/gw.h declares, and
+rejects invalid calls on the host before any HIP call (so these run with no
+GPU).  Error conventions follow pegainfer PR #1012: a width outside the
+enum is unrepresentable, a refused combination carries a fixed message, and
+a failure names the entry point that ran."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_hybrid_kv_amd import gw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gw.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gw.LIB_PATH), reason="libgw.so not built")
+
+FAKE = 0x1000   # non-null stand-in address; never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gw_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(gw.EXPORTS)
+    L = gw.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version():
+    assert "gfx950" in gw.gw_version()
+
+
+def desc(family=gw.GW_FAMILY_LOCAL, dt=gw.GW_KV_BF16, page=16, heads=8, dim=None, rot=None, pages=4,
+         base=FAKE):
+    if dim is None:
+        dim = 256 if family == gw.GW_FAMILY_LOCAL else 512
+    if rot is None:
+        rot = 256 if family == gw.GW_FAMILY_LOCAL else 128
+    if family != gw.GW_FAMILY_LOCAL and heads == 8:
+        heads = 1
+    return gw.gw_pool_desc(family, dt, page, heads, dim, rot, pages, base)
+
+
+def test_page_bytes():
+    assert gw.gw_pool_page_bytes(desc()) == 16 * 2 * 8 * 256 * 2
+    assert gw.gw_pool_page_bytes(desc(dt=gw.GW_KV_E4M3)) == 16 * 2 * 8 * 256
+    comp = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_COMPRESSED))
+    full = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_FULL))
+    assert (comp, full) == (20480, 32768) and comp / full == 0.625
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(family=0), gw.GW_ERR_INVALID_ARG, "unknown family"),
+    (dict(dt=0), gw.GW_ERR_INVALID_ARG, "unknown kv_dtype"),
+    (dict(dt=3), gw.GW_ERR_INVALID_ARG, "unknown kv_dtype"),
+    (dict(page=32), gw.GW_ERR_GEOMETRY, "page_size"),
+    (dict(dim=128), gw.GW_ERR_GEOMETRY, "head_dim"),
+    (dict(rot=64), gw.GW_ERR_GEOMETRY, "rot_dim"),
+    (dict(heads=0), gw.GW_ERR_GEOMETRY, "num_kv_heads"),
+    (dict(family=gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), gw.GW_ERR_UNSUPPORTED,
+     "e4m3 supports only the local family"),
+    (dict(family=gw.GW_FAMILY_GLOBAL_FULL, heads=2), gw.GW_ERR_GEOMETRY, "num_kv_heads"),
+    (dict(family=gw.GW_FAMILY_GLOBAL_FULL, rot=512), gw.GW_ERR_GEOMETRY, "rot_dim"),
+])
+def test_page_bytes_rejects(kw, code, frag):
+    with pytest.raises(gw.GwError) as e:
+        gw.gw_pool_page_bytes(desc(**kw))
+    assert e.value.code == code
+    assert e.value.message.startswith("gw_pool_page_bytes: ")
+    assert frag in e.value.message
+
+
+def append(d, k=FAKE, v=FAKE, n=4, stride=8, cos=FAKE, sin=FAKE):
+    gw.gw_kv_append(d, k, v, FAKE, FAKE, n, FAKE, stride, cos, sin)
+
+
+@pytest.mark.parametrize("call,code,frag", [
+    (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), k=None),
+     gw.GW_ERR_UNSUPPORTED, "gw_kv_append: e4m3 supports only the local family"),
+    (lambda: append(desc(base=None)), gw.GW_ERR_INVALID_ARG, "base is null"),
+    (lambda: append(desc(pages=0)), gw.GW_ERR_INVALID_ARG, "num_pages"),
+    (lambda: append(desc(), n=-1), gw.GW_ERR_INVALID_ARG, "n_tok"),
+    (lambda: append(desc(), cos=None), gw.GW_ERR_INVALID_ARG, "both"),
+    (lambda: append(desc(), cos=None, sin=None), gw.GW_ERR_INVALID_ARG, "needs rotary tables"),
+    (lambda: append(desc(rot=0)), gw.GW_ERR_INVALID_ARG, "takes no rotary tables"),
+    (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_FULL)), gw.GW_ERR_INVALID_ARG, "k_raw must be null"),
+    (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_FULL), k=None, cos=None, sin=None),
+     gw.GW_ERR_INVALID_ARG, "needs rotary tables"),
+    (lambda: append(desc(), k=None), gw.GW_ERR_INVALID_ARG, "k_raw is null"),
+    (lambda: append(desc(), stride=0), gw.GW_ERR_INVALID_ARG, "pt_stride"),
+])
+def test_append_rejects(call, code, frag):
+    with pytest.raises(gw.GwError) as e:
+        call()
+    assert e.value.code == code
+    assert e.value.message.startswith("gw_kv_append: ")
+    assert frag in e.value.message
+
+
+def test_append_zero_tokens_is_noop():
+    append(desc(), n=0)   # returns GW_OK without touching the GPU
+
+
+def local(d=None, q=FAKE, hq=16, indptr=None, lens=FAKE, pt=FAKE, stride=512, S=4, rows=4, mql=1,
+          msl=8192, win=1024, scale=0.0625, out=FAKE, ws=FAKE, wsb=1 << 30):
+    gw.gw_decode_attn_local(d or desc(), q, hq, indptr, lens, pt, stride, S, rows, mql, msl, win, scale,
+                            out, ws, wsb, None)
+
+
+def glob(d=None, q=FAKE, hq=32, indptr=None, lens=FAKE, pt=FAKE, stride=8192, S=4, rows=4, mql=1,
+         msl=131072, scale=0.044, out=FAKE, ws=FAKE, wsb=1 << 30):
+    gw.gw_decode_attn_global(d or desc(gw.GW_FAMILY_GLOBAL_COMPRESSED), q, hq, indptr, lens, pt, stride,
+                             S, rows, mql, msl, scale, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call,code,frag", [
+    (lambda: local(win=0), gw.GW_ERR_INVALID_ARG, "window"),
+    (lambda: local(hq=12), gw.GW_ERR_GEOMETRY, "multiple"),
+    (lambda: local(hq=64), gw.GW_ERR_UNSUPPORTED, "group size 8"),
+    (lambda: local(d=desc(gw.GW_FAMILY_GLOBAL_FULL)), gw.GW_ERR_INVALID_ARG, "not GW_FAMILY_LOCAL"),
+    (lambda: local(rows=5), gw.GW_ERR_INVALID_ARG, "num_rows"),
+    (lambda: local(mql=2), gw.GW_ERR_INVALID_ARG, "max_q_len"),
+    (lambda: local(stride=10), gw.GW_ERR_INVALID_ARG, "pt_stride"),
+    (lambda: local(q=None), gw.GW_ERR_INVALID_ARG, "null"),
+    (lambda: local(out=None), gw.GW_ERR_INVALID_ARG, "null"),
+    (lambda: local(scale=float("nan")), gw.GW_ERR_INVALID_ARG, "scale"),
+    (lambda: local(S=-1), gw.GW_ERR_INVALID_ARG, "num_seqs"),
+    (lambda: local(wsb=16), gw.GW_ERR_WORKSPACE, "workspace"),
+    (lambda: local(ws=None), gw.GW_ERR_INVALID_ARG, "workspace is null"),
+    (lambda: local(ws=FAKE + 8), gw.GW_ERR_INVALID_ARG, "aligned"),
+    (lambda: local(d=desc(dt=gw.GW_KV_BF16, page=8)), gw.GW_ERR_GEOMETRY, "page_size"),
+])
+def test_local_rejects(call, code, frag):
+    with pytest.raises(gw.GwError) as e:
+        call()
+    assert e.value.code == code
+    assert e.value.message.startswith("gw_decode_attn_local: ")
+    assert frag in e.value.message
+
+
+@pytest.mark.parametrize("call,code,frag", [
+    (lambda: glob(hq=8), gw.GW_ERR_UNSUPPORTED, "num_q_heads"),
+    (lambda: glob(d=desc()), gw.GW_ERR_INVALID_ARG, "not a global family"),
+    (lambda: glob(d=desc(gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3)), gw.GW_ERR_UNSUPPORTED,
+     "e4m3 supports only the local family"),
+    (lambda: glob(wsb=0), gw.GW_ERR_WORKSPACE, "workspace"),
+    (lambda: glob(msl=0), gw.GW_ERR_INVALID_ARG, "max_seq_len"),
+])
+def test_global_rejects(call, code, frag):
+    with pytest.raises(gw.GwError) as e:
+        call()
+    assert e.value.code == code
+    assert e.value.message.startswith("gw_decode_attn_global: ")
+    assert frag in e.value.message
+
+
+def test_empty_batches_are_noops():
+    local(S=0, rows=0, ws=None, wsb=0)
+    glob(S=0, rows=0, ws=None, wsb=0)
+
+
+def test_workspace_plan():
+    # one window of 1024 tokens spans at most 65 pages -> 5 splits of >= 13 pages
+    ws = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 16, 16, 16, 256, 8192, 1024, 1)
+    assert ws >= 16 * 16 * 5 * 258 * 4
+    assert gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 1, 1, 2, 256, 64, 32, 1) == 0
+    wg = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_GLOBAL_COMPRESSED, 8, 8, 32, 512, 131072, 0, 1)
+    assert wg >= 8 * 32 * 64 * 514 * 4
+    assert gw.gw_attn_workspace_bytes(gw.GW_FAMILY_GLOBAL_FULL, 1, 1, 32, 512, 256, 0, 1) == 0
+
+
+def test_error_message_is_thread_local_and_cleared():
+    with pytest.raises(gw.GwError):
+        local(win=0)
+    assert gw.gw_last_error().startswith("gw_decode_attn_local")
+    assert gw.gw_pool_page_bytes(desc()) > 0
+    assert gw.gw_last_error() == ""

@@ -1,0 +1,136 @@
+"""Global family on the GPU: append of the compressed and full records and
+paged MQA decode attention (head dim 512, one tied KV head) against the CPU
+oracle, plus the bit-exact gates (compressed == full, page placement, row
+order, dominant-key probes).  Tolerances: max abs 1e-2, mean abs 1e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs as OC
+from oracle import pool as OP
+from oracle import rope as OR
+from paged_hybrid_kv_amd import runtime as RT, synth as SY
+
+from .oracle_side import compare, global_seq, oracle_out
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, compressed=True):
+    dc = RT.upload_global(case, compressed=compressed)
+    out = RT.attend(dc)
+    torch.cuda.synchronize()
+    return dc, out.cpu().numpy()
+
+
+def check(case, out, label, seqs=None):
+    ref = oracle_out(case, seqs)
+    worst = 0.0
+    for s, r in ref.items():
+        mx, _, _ = compare(out[s:s + 1], r, f"{label} seq {s}")
+        worst = max(worst, mx)
+    return worst
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_small_global(rope):
+    lens = [1, 2, 16, 17, 31, 32, 33, 63, 64, 65, 700, 4097]
+    case = SY.global_case("small", 30, lens, num_q_heads=32, rope=rope)
+    _, oc = run(case, True)
+    _, of = run(case, False)
+    assert np.array_equal(oc, of), "compressed and full records differ"
+    mx = check(case, oc, f"small rope={rope}")
+    print(f"global small rope={rope} max abs err {mx:.2e}", flush=True)
+
+
+def test_sixteen_heads():
+    case = SY.global_case("h16", 31, [5, 300, 2000], num_q_heads=16, rope=True)
+    _, out = run(case)
+    check(case, out, "Hq=16")
+
+
+def test_global_full_size():
+    """8 slots x 131072 tokens: every slot compared bit-exactly between the two
+    records; two slots against the oracle."""
+    case = SY.global_tied()
+    dc, oc = run(case, True)
+    del dc
+    torch.cuda.empty_cache()
+    dcf, of = run(case, False)
+    del dcf
+    torch.cuda.empty_cache()
+    assert np.array_equal(oc, of), "compressed and full records differ at 131072 tokens"
+    mx = check(case, oc, "global_tied", seqs=[0, 5])
+    print(f"global_tied (2 of 8 slots) max abs err {mx:.2e}", flush=True)
+
+
+def test_dominant_key_probes():
+    L = 100
+    probes = [0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 95, 96, 98, 99]
+    case = SY.global_case("dominant", 33, [L] * len(probes), num_q_heads=32, rope=False)
+    case.q[:] = case.q[:, :1, :]                      # all heads equal
+    for s, j in enumerate(probes):
+        qd = case.q[s, 0].astype(np.float64)
+        idx = np.nonzero((case.tok_seq == s) & (case.tok_pos == j))[0][0]
+        case.v[idx] = (200.0 * qd / np.linalg.norm(qd)).astype(np.float32)   # K = V (tied)
+    for compressed in (True, False):
+        _, out = run(case, compressed)
+        for s, j in enumerate(probes):
+            _, V = global_seq(case, s)
+            want = V[j, 0].astype(np.float32)
+            for h in range(32):
+                assert np.array_equal(out[s, h], want), f"probe j*={j} head {h}"
+
+
+def test_page_permutation_and_row_order_bitexact():
+    lens = [3000, 129, 4500, 64]
+    a = SY.global_case("perm", 34, lens, rope=True)
+    b = SY.global_case("perm", 34, lens, rope=True, extra_pages=11)
+    assert not np.array_equal(a.seqs.page_table, b.seqs.page_table)
+    b.q, b.v = a.q, a.v
+    _, oa = run(a)
+    _, ob = run(b)
+    assert np.array_equal(oa, ob)
+    # reverse the rows
+    perm = np.arange(len(lens))[::-1]
+    r = SY.global_case("perm", 35, [lens[i] for i in perm], rope=True)
+    r.q = a.q[perm]
+    vs, ts, ps = [], [], []
+    for new_s, old_s in enumerate(perm):
+        sel = a.tok_seq == old_s
+        vs.append(a.v[sel]); ts.append(np.full(sel.sum(), new_s, np.int32)); ps.append(a.tok_pos[sel])
+    r.v, r.tok_seq, r.tok_pos = np.concatenate(vs), np.concatenate(ts), np.concatenate(ps)
+    _, orr = run(r)
+    assert np.array_equal(orr, oa[perm])
+
+
+def test_repeat_determinism():
+    case = SY.global_case("repeat", 36, [20000, 9000], rope=True)
+    dc, o1 = run(case)
+    o2 = RT.attend(dc).cpu().numpy()
+    assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("compressed", [True, False])
+def test_append_global(compressed):
+    case = SY.global_case("append", 37, [40, 17, 300], rope=True, extra_pages=2)
+    dc = RT.upload_global(case, compressed=compressed)
+    torch.cuda.synchronize()
+    pb = dc.pool.buf.cpu().numpy()
+    for s in range(case.seqs.S):
+        L = int(case.seqs.lens[s])
+        A, B = OP.global_codes(pb, case.seqs.page_table[s], L, compressed)
+        sel = case.tok_seq == s
+        v = OC.bf16_round(case.v[sel].astype(np.float64))
+        k_rot = OC.bf16_round(OR.rotate_global(v, case.tok_pos[sel])[:, :128])
+        if compressed:
+            Vg, Kr = OC.bf16_decode(A), OC.bf16_decode(B)
+        else:
+            Kg, Vg = OC.bf16_decode(A), OC.bf16_decode(B)
+            assert np.array_equal(Kg[:, 128:], v[:, 128:])
+            Kr = Kg[:, :128]
+        assert np.array_equal(Vg, v)
+        tol = np.maximum(np.abs(k_rot), 2.0 ** -126) * 2.0 ** -7
+        assert np.all(np.abs(Kr - k_rot) <= tol)
+        assert np.mean(Kr == k_rot) > 0.95

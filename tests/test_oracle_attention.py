@@ -153,3 +153,20 @@ def test_matches_torch_sdpa(L, W, Hq, Hkv, D):
     ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask, scale=scale)
     ref = ref.permute(1, 0, 2).numpy()
     assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_keys_outside_the_window_are_never_read():
+    # NaN in K/V outside every row's [lo, p] must not reach any output
+    rng = np.random.default_rng(10)
+    q, K, V = _rand(rng, 90, 2, 8, 3, 4)
+    pos = np.array([40, 55, 60])
+    ref = A.attend(q, K, V, pos, 0.5, 16)
+    Kn, Vn = K.copy(), V.copy()
+    Kn[:25], Vn[:25] = np.nan, np.nan       # before the first row's window
+    Kn[61:], Vn[61:] = np.inf, np.nan       # after the last row
+    Kn[30:40, 1], Vn[30:40, 1] = np.nan, np.nan   # inside the union, outside row 1/2 windows
+    got = A.attend(q[1:], Kn, Vn, pos[1:], 0.5, 16)
+    assert np.isfinite(got).all() and np.max(np.abs(got - ref[1:])) < 1e-13
+    got0 = A.attend(q[:1], Kn, Vn, pos[:1], 0.5, 16)   # row 0's window 25..40 holds NaN at 30..39
+    assert np.isnan(got0[0, 2:]).all()      # heads of KV head 1 read it: NaN propagates
+    assert np.max(np.abs(got0[0, :2] - ref[0, :2])) < 1e-13
