@@ -170,10 +170,10 @@ int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const v
  * Query rows and sequences (pegainfer "Gemma 4" page, Scheduling: every
  * active request advances one token per step, and a new prompt's rows are
  * computed in the same step):
- *   num_seqs sequences; sequence s has seq_lens[s] tokens in the pool (its
- *   current tokens included) and q_len_s = q_indptr[s+1] - q_indptr[s] query
- *   rows, rows q_indptr[s] .. q_indptr[s+1]-1, the last q_len_s tokens of the
- *   sequence: row r of s is at position seq_lens[s] - q_len_s + r.
+ *   num_seqs sequences; sequence s has seq_lens[s] tokens (its current tokens
+ *   included) and q_len_s = q_indptr[s+1] - q_indptr[s] query rows, rows
+ *   q_indptr[s] .. q_indptr[s+1]-1, the last q_len_s tokens of the sequence:
+ *   row r of s is at position seq_lens[s] - q_len_s + r.
  *   q_indptr NULL means one row per sequence (num_rows == num_seqs).
  *   A row at position p attends keys j with lo <= j <= p, lo = max(0,
  *   p - window + 1) for LOCAL and 0 for GLOBAL; q head h reads KV head
@@ -185,8 +185,16 @@ int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const v
  *
  *   q   : bf16 [num_rows][num_q_heads][head_dim], already rotated.
  *   out : fp32 [num_rows][num_q_heads][head_dim].
- *   workspace : at least gw_attn_workspace_bytes(...) bytes (may be NULL
- *   when that is 0), 256-byte aligned; contents on entry are ignored.
+ *   k_new, v_new, rope_cos, rope_sin : optional append of each row's own
+ *     token before attention, with exactly gw_kv_append's arithmetic and
+ *     placement (the prep step fused into the call): k_new/v_new hold the
+ *     raw K/V of row r's token (position seq_lens[s] - q_len_s + r).  NULL
+ *     k_new/v_new: the pool already holds every row's token.
+ *   workspace : at least gw_attn_workspace_bytes(...) bytes (NULL when that
+ *     is 0), 256-byte aligned, ZERO-FILLED before its first use; every call
+ *     that completes leaves it ready for the next call (it holds split
+ *     counters that the call's last workgroups reset).  Calls that overlap
+ *     in time must not share a workspace.
  *
  * Results are deterministic, and each row's result depends only on that
  * row's query, its sequence's length and K/V, the window and the scale --
@@ -197,21 +205,29 @@ size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_row
                                int32_t window, int32_t max_q_len);
 
 /* Local family (pool->family == GW_FAMILY_LOCAL; bf16 or e4m3).
- * num_q_heads a multiple of num_kv_heads, group size 1, 2 or 4; window >= 1. */
+ * num_q_heads a multiple of num_kv_heads, group size 1, 2 or 4; window >= 1.
+ * k_new / v_new: bf16 [num_rows][num_kv_heads][256]; with rot_dim 256 the
+ * rotary tables (fp32 [max_pos][128]) are required, with rot_dim 0 they must
+ * be NULL. */
 int gw_decode_attn_local(const gw_pool_desc* pool /* host */, const void* q,
-                         int32_t num_q_heads, const int32_t* q_indptr, const int32_t* seq_lens,
-                         const int32_t* page_table, int32_t pt_stride, int32_t num_seqs,
-                         int32_t num_rows, int32_t max_q_len, int32_t max_seq_len,
-                         int32_t window, float scale, float* out, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         int32_t num_q_heads, const void* k_new, const void* v_new,
+                         const float* rope_cos, const float* rope_sin, const int32_t* q_indptr,
+                         const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
+                         int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                         int32_t max_seq_len, int32_t window, float scale, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16).
- * num_q_heads 16 or 32.  The two layouts give bit-identical results. */
+ * num_q_heads 16 or 32.  The two layouts give bit-identical results.
+ * v_new: bf16 [num_rows][512] (K is V before rotation), with the rotary
+ * tables fp32 [max_pos][64]; NULL when the pool already holds the rows. */
 int gw_decode_attn_global(const gw_pool_desc* pool /* host */, const void* q,
-                          int32_t num_q_heads, const int32_t* q_indptr, const int32_t* seq_lens,
-                          const int32_t* page_table, int32_t pt_stride, int32_t num_seqs,
-                          int32_t num_rows, int32_t max_q_len, int32_t max_seq_len, float scale,
-                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+                          int32_t num_q_heads, const void* v_new, const float* rope_cos,
+                          const float* rope_sin, const int32_t* q_indptr,
+                          const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
+                          int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                          int32_t max_seq_len, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -90,20 +90,24 @@ int max_splits_for(int family, int max_seq_len, int window) {
   return gw::global_nsplit(tiles);
 }
 
+// Workspace: [split counters | partial accumulators | partial (max, sum)].
+// The counters must be zero before the first call (the caller zero-fills the
+// workspace once); every call that completes leaves them zero again.
 struct WsPlan {
   int max_splits;
-  size_t acc_bytes, ml_bytes, total;
+  size_t counter_bytes, acc_bytes, ml_bytes, total;
 };
 
-WsPlan plan_workspace(int family, int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
-                      int window) {
+WsPlan plan_workspace(int family, int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
+                      int max_seq_len, int window) {
   WsPlan w{};
   w.max_splits = max_splits_for(family, max_seq_len, window);
   if (w.max_splits <= 1 || num_seqs <= 0) return w;
   const size_t units = (size_t)num_seqs * num_q_heads * w.max_splits;
+  w.counter_bytes = align_up((size_t)num_seqs * num_kv_heads * sizeof(int));
   w.acc_bytes = align_up(units * head_dim * sizeof(float));
   w.ml_bytes = align_up(units * 2 * sizeof(float));
-  w.total = w.acc_bytes + w.ml_bytes;
+  w.total = w.counter_bytes + w.acc_bytes + w.ml_bytes;
   return w;
 }
 
@@ -222,11 +226,13 @@ size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_row
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
   if (family == GW_FAMILY_LOCAL && window < 1) return 0;
   if (!is_local(family) && !is_global(family)) return 0;
-  return plan_workspace(family, num_seqs, num_q_heads, head_dim, max_seq_len, window).total;
+  // one counter per (sequence, q head) bounds the per-(sequence, KV head) need
+  return plan_workspace(family, num_seqs, num_q_heads, num_q_heads, head_dim, max_seq_len, window).total;
 }
 
 int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
-                         const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
+                         const void* k_new, const void* v_new, const float* rope_cos,
+                         const float* rope_sin, const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
                          int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
                          int32_t max_seq_len, int32_t window, float scale, float* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -245,7 +251,16 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   const int group = num_q_heads / pool->num_kv_heads;
   if (group != 1 && group != 2 && group != 4)
     return fail(GW_ERR_UNSUPPORTED, fn, "query group size %d (served: 1, 2, 4)", group);
-  const WsPlan w = plan_workspace(GW_FAMILY_LOCAL, num_seqs, num_q_heads, 256, max_seq_len, window);
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(GW_ERR_INVALID_ARG, fn, "k_new and v_new must both be set or both be null");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
+  if (v_new && pool->rot_dim != 0 && !rope_cos)
+    return fail(GW_ERR_INVALID_ARG, fn, "rot_dim %d needs rotary tables", pool->rot_dim);
+  if (v_new && pool->rot_dim == 0 && rope_cos)
+    return fail(GW_ERR_INVALID_ARG, fn, "rot_dim 0 takes no rotary tables");
+  const WsPlan w = plan_workspace(GW_FAMILY_LOCAL, num_seqs, pool->num_kv_heads, num_q_heads, 256,
+                                  max_seq_len, window);
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
@@ -267,22 +282,24 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
-  a.part_acc = static_cast<float*>(workspace);
-  a.part_ml = w.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = w.total ? reinterpret_cast<int*>(ws) : nullptr;
+  a.part_acc = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes) : nullptr;
+  a.part_ml = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes + w.acc_bytes) : nullptr;
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   (void)hipGetLastError();   // a stale error from earlier work is not ours to report
   hipError_t e = gw::launch_local_decode(a, group, pool->kv_dtype == GW_KV_E4M3, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
-  if (w.max_splits > 1) {
-    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, 256, w.max_splits, window};
-    e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
   return ok();
 }
 
 int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+                          const void* v_new, const float* rope_cos, const float* rope_sin,
                           const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
                           int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
                           int32_t max_seq_len, float scale, float* out, void* workspace,
@@ -297,7 +314,11 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if (rc != GW_OK) return rc;
   if (num_q_heads != 16 && num_q_heads != 32)
     return fail(GW_ERR_UNSUPPORTED, fn, "num_q_heads %d (served: 16, 32)", num_q_heads);
-  const WsPlan w = plan_workspace(pool->family, num_seqs, num_q_heads, 512, max_seq_len, 0);
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
+  if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
+  if (v_new) return fail(GW_ERR_UNSUPPORTED, fn, "appending inside the global call is not served by this build");
+  const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0);
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
@@ -316,10 +337,15 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   a.num_q_heads = num_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
-  a.part_acc = static_cast<float*>(workspace);
-  a.part_ml = w.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = w.total ? reinterpret_cast<int*>(ws) : nullptr;
+  a.part_acc = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes) : nullptr;
+  a.part_ml = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes + w.acc_bytes) : nullptr;
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   (void)hipGetLastError();
   hipError_t e = gw::launch_global_decode(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);

@@ -58,10 +58,7 @@ __global__ __launch_bounds__(64) void append_local_kernel(AppendArgs a) {
       const float4 sn = *reinterpret_cast<const float4*>(a.rope_sin + (int64_t)ps * 128 + 4 * l);
       const float c4[4] = {cs.x, cs.y, cs.z, cs.w}, s4[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ya[j] = xa[j] * c4[j] - xb[j] * s4[j];
-        yb[j] = xb[j] * c4[j] + xa[j] * s4[j];
-      }
+      for (int j = 0; j < 4; ++j) rope_pair(xa[j], xb[j], c4[j], s4[j], ya[j], yb[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) { ya[j] = xa[j]; yb[j] = xb[j]; }
@@ -138,9 +135,11 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
     for (int m = 0; m < 4; ++m) {
       const float a0 = bf16_lo(xa_p[m]), a1 = bf16_hi(xa_p[m]);
       const float b0 = bf16_lo(xb_p[m]), b1 = bf16_hi(xb_p[m]);
-      const float c0 = cp[2 * m], c1 = cp[2 * m + 1], s0 = sp[2 * m], s1 = sp[2 * m + 1];
-      ya[m] = pack_bf16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-      yb[m] = pack_bf16(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+      float y0a, y0b, y1a, y1b;
+      rope_pair(a0, b0, cp[2 * m], sp[2 * m], y0a, y0b);
+      rope_pair(a1, b1, cp[2 * m + 1], sp[2 * m + 1], y1a, y1b);
+      ya[m] = pack_bf16(y0a, y1a);
+      yb[m] = pack_bf16(y0b, y1b);
     }
     *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 8) = uint4{ya[0], ya[1], ya[2], ya[3]};
     *reinterpret_cast<uint4*>(kblock + ((l + 8) * 16 + slot) * 8) = uint4{yb[0], yb[1], yb[2], yb[3]};

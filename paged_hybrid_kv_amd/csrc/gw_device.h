@@ -61,6 +61,14 @@ __device__ __forceinline__ float round_bf16(float x) {
   return bf16_lo(pack_bf16(x, 0.0f));
 }
 
+// One rotate-half RoPE pair in fp32 with the rounding fixed by explicit
+// fused multiply-adds, so every kernel that rotates K gets the same bits:
+//   ya = xa*c - xb*s,  yb = xb*c + xa*s.
+__device__ __forceinline__ void rope_pair(float xa, float xb, float c, float s, float& ya, float& yb) {
+  ya = __builtin_fmaf(xa, c, -(xb * s));
+  yb = __builtin_fmaf(xb, c, xa * s);
+}
+
 // Cross-lane moves.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -68,6 +76,22 @@ __device__ __forceinline__ float dpp_f32(float x) {
 }
 constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;    // row_ror:4  (within 16-lane rows)
+constexpr int kRowRor8 = 0x128;    // row_ror:8
+constexpr int kRowShl4 = 0x104;    // row_shl:4: lane i reads lane i + 4 of its row
+
+// Max over the 64 lanes of a value held identically by the 4 lanes of each
+// quad and differing across quads: two DPP rotations inside each 16-lane
+// row, then the four row results through SGPRs.  Returns a wave-uniform value.
+__device__ __forceinline__ float wave_max_quads(float x) {
+  x = fmaxf(x, bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_to_bits(x), kRowRor4, 0xf, 0xf, false)));
+  x = fmaxf(x, bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_to_bits(x), kRowRor8, 0xf, 0xf, false)));
+  const float r0 = bits_to_f32((uint32_t)__builtin_amdgcn_readlane((int)f32_to_bits(x), 0));
+  const float r1 = bits_to_f32((uint32_t)__builtin_amdgcn_readlane((int)f32_to_bits(x), 16));
+  const float r2 = bits_to_f32((uint32_t)__builtin_amdgcn_readlane((int)f32_to_bits(x), 32));
+  const float r3 = bits_to_f32((uint32_t)__builtin_amdgcn_readlane((int)f32_to_bits(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 
 __device__ __forceinline__ float shfl_xor_f32(float x, int m) {
   return bits_to_f32((uint32_t)__shfl_xor((int)f32_to_bits(x), m, kWave));
@@ -88,6 +112,15 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 }
 __device__ __forceinline__ uint4 ld16_cached(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+
+// Wait until every memory access this wave issued has completed (on gfx9
+// stores are counted in vmcnt): s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched.
+// The signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).

@@ -22,8 +22,13 @@ struct LocalAttnArgs {
   float* out;                 // fp32 [rows][Hq][256]
   float* part_acc;            // fp32 [S][Hq][max_splits][256]
   float* part_ml;             // fp32 [S][Hq][max_splits][2]: (max, sum) in base 2
+  int* counters;              // [S][Hkv] splits finished; zero between calls
   int32_t max_splits;
   int32_t num_seqs;
+  const uint16_t* k_new;      // bf16 [rows][Hkv][256] raw K of each row's own token, or null
+  const uint16_t* v_new;      // bf16 [rows][Hkv][256], or null (no append)
+  const float* rope_cos;      // [max_pos][128] or null (K stored as given)
+  const float* rope_sin;
 };
 
 struct GlobalAttnArgs {
@@ -39,8 +44,12 @@ struct GlobalAttnArgs {
   float* out;                 // fp32 [rows][Hq][512]
   float* part_acc;            // fp32 [S][Hq][max_splits][512]
   float* part_ml;             // fp32 [S][Hq][max_splits][2]
+  int* counters;              // [S] splits finished; zero between calls
   int32_t max_splits;
   int32_t num_seqs;
+  const uint16_t* v_new;      // bf16 [rows][512] raw V (= K before rotation) of each row's token, or null
+  const float* rope_cos;      // [max_pos][64]
+  const float* rope_sin;
 };
 
 struct ReduceArgs {

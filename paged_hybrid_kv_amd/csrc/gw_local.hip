@@ -1,16 +1,22 @@
 // Local-family paged decode attention (sliding window, head dim 256, grouped
-// query heads) and the cross-split reduce shared with the global family.
+// query heads), with the decode rows' own K/V append and the cross-split
+// reduce fused in, plus the standalone cross-split reduce used by the global
+// family.
 //
 // What is computed (pegainfer "Gemma 4" page, intro and Architecture notes;
 // pegainfer PR #1012, Description, for the e4m3 pool): for each decode row of
 // sequence s at position p = seq_len - 1 and each q head h of KV head
 // g = h / G, softmax over the keys j in [max(0, p - W + 1), p] of
 // scale * q_h . K_j, applied to V_j, with K/V read from 16-token pages.
+// When the call carries the rows' new K/V, the token at p is rotated and
+// stored first (the prep step), exactly as gw_kv_append stores it.
 //
 // Work split: one workgroup per (split, KV head, sequence); a split is a
 // balanced run of the pages of the row's window (gw_plan.h).  Four waves per
 // workgroup take every fourth page of the split, each with its own online
 // softmax state (running max m, sum l, accumulator), merged in LDS at the end.
+// The last workgroup of a (sequence, KV head) to finish merges the splits'
+// partials in split order (a counter per pair, reset by that workgroup).
 //
 // Lane roles inside a wave (the page layout puts each lane's 16 bytes next
 // to its neighbours', so every load instruction reads a contiguous 1 KiB):
@@ -48,9 +54,7 @@ struct PageRegs {
 };
 
 template <bool FP8>
-__device__ __forceinline__ void load_page(PageRegs<FP8>& r, const uint8_t* head_base,
-                                          int64_t page_bytes, int phys, int lane) {
-  const uint8_t* b = head_base + (int64_t)phys * page_bytes + lane * 16;
+__device__ __forceinline__ void load_page(PageRegs<FP8>& r, const uint8_t* b) {
 #pragma unroll
   for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) r.k[k] = ld16(b + k * 1024);
 #pragma unroll
@@ -61,8 +65,103 @@ __device__ __forceinline__ void load_page(PageRegs<FP8>& r, const uint8_t* head_
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
+__device__ __forceinline__ void u4_set(uint4& v, int i, uint32_t x) {
+  if (i == 0) v.x = x; else if (i == 1) v.y = x; else if (i == 2) v.z = x; else v.w = x;
+}
 __device__ __forceinline__ void u4_and(uint4& v, uint32_t m) {
   v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+}
+
+// The new token of a decode row (slot p % 16 of the page just loaded into r):
+// rotate and round its K exactly as gw_kv_append does, patch it into the
+// registers and store K and V into the pool page at b (this lane's offsets).
+template <bool FP8>
+__device__ __forceinline__ void patch_new_token(PageRegs<FP8>& r, uint8_t* b, const LocalAttnArgs& a,
+                                               int row, int g, int p, int lane) {
+  const int slot = p & 15, t = lane >> 2, c = lane & 3;
+  const uint16_t* kr = a.k_new + ((int64_t)row * a.num_kv_heads + g) * kLocalD;
+  const uint16_t* vr = a.v_new + ((int64_t)row * a.num_kv_heads + g) * kLocalD;
+  // K: this lane's quarter, dims 64c .. 64c+63; rotation partners 128 apart.
+  // Each 16-byte chunk of the page register takes kPer dims, read with
+  // 16-byte loads (raw K, its partner dims, cos, sin).
+  const int d0 = 64 * c;
+  const int pd0 = (d0 + 128) & 255;
+  const bool lower = c < 2;
+  const bool rope = a.rope_cos != nullptr;
+  const float* cs = a.rope_cos + (int64_t)p * 128 + (d0 & 127);
+  const float* sn = a.rope_sin + (int64_t)p * 128 + (d0 & 127);
+  constexpr int kPer = FP8 ? 16 : 8;   // dims per 16-byte chunk of the page
+#pragma unroll
+  for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) {
+    uint32_t xo[kPer / 2], xp[kPer / 2];
+#pragma unroll
+    for (int q = 0; q < kPer / 8; ++q) {
+      const uint4 o4 = ld16_cached(kr + d0 + k * kPer + 8 * q);
+      const uint4 p4 = ld16_cached(kr + pd0 + k * kPer + 8 * q);
+      xo[4 * q] = o4.x; xo[4 * q + 1] = o4.y; xo[4 * q + 2] = o4.z; xo[4 * q + 3] = o4.w;
+      xp[4 * q] = p4.x; xp[4 * q + 1] = p4.y; xp[4 * q + 2] = p4.z; xp[4 * q + 3] = p4.w;
+    }
+    float cv[kPer], sv[kPer];
+    if (rope) {
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) {
+        const float4 c4 = *reinterpret_cast<const float4*>(cs + k * kPer + 4 * q);
+        const float4 s4 = *reinterpret_cast<const float4*>(sn + k * kPer + 4 * q);
+        cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
+        sv[4 * q] = s4.x; sv[4 * q + 1] = s4.y; sv[4 * q + 2] = s4.z; sv[4 * q + 3] = s4.w;
+      }
+    }
+    float y[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const float x = (e & 1) ? bf16_hi(xo[e >> 1]) : bf16_lo(xo[e >> 1]);
+      const float xq = (e & 1) ? bf16_hi(xp[e >> 1]) : bf16_lo(xp[e >> 1]);
+      float ya, yb;
+      if (lower) rope_pair(x, xq, cv[e], sv[e], ya, yb);
+      else rope_pair(xq, x, cv[e], sv[e], yb, ya);
+      y[e] = rope ? ya : x;
+    }
+    uint4 wv;
+    if constexpr (!FP8) {
+      wv = uint4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    } else {
+      uint32_t q4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        q4[m] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q4[m] |= f32_to_e4m3(round_bf16(y[4 * m + j])) << (8 * j);
+      }
+      wv = uint4{q4[0], q4[1], q4[2], q4[3]};
+    }
+    if (t == slot) {
+      r.k[k] = wv;
+      *reinterpret_cast<uint4*>(b + k * 1024) = wv;
+    }
+  }
+  // V: this lane's dims 4l..4l+3 of the token, into the pair / quad registers;
+  // the whole 16 bytes go back, the other tokens' parts unchanged.  (Register
+  // arrays are indexed with constants only, so they stay in registers.)
+  const uint2 raw = *reinterpret_cast<const uint2*>(vr + 4 * lane);
+  const uint32_t v16[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
+  constexpr int kTokPerReg = FP8 ? 4 : 2;
+  const int u = slot / kTokPerReg;
+  const int sh = (FP8 ? 8 : 16) * (slot % kTokPerReg);
+  const uint32_t field = (FP8 ? 0xffu : 0xffffu) << sh;
+  uint32_t bits[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bits[j] = (FP8 ? f32_to_e4m3(bits_to_f32(v16[j] << 16)) : v16[j]) << sh;
+  uint4 st = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int uu = 0; uu < LocalLayout<FP8>::kLoads; ++uu) {
+    const uint32_t m = (uu == u) ? field : 0u;
+    r.v[uu].x = (r.v[uu].x & ~m) | (bits[0] & m);
+    r.v[uu].y = (r.v[uu].y & ~m) | (bits[1] & m);
+    r.v[uu].z = (r.v[uu].z & ~m) | (bits[2] & m);
+    r.v[uu].w = (r.v[uu].w & ~m) | (bits[3] & m);
+    if (uu == u) st = r.v[uu];
+  }
+  *reinterpret_cast<uint4*>(b + LocalLayout<FP8>::kBlockBytes + u * 1024) = st;
 }
 
 template <int G, bool FP8>
@@ -108,12 +207,7 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
   // ---- online softmax: page max, rescale on a new maximum (wave-uniform)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = z[h];
-    mx = fmaxf(mx, shfl_xor_f32(mx, 4));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 8));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    mx = bits_to_f32((uint32_t)uniform_i32((int)f32_to_bits(mx)));
+    const float mx = wave_max_quads(z[h]);
     const float mnew = fmaxf(m_run[h], mx);
     if (mnew > m_run[h]) {
       const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mnew);
@@ -129,7 +223,7 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float pr = __builtin_amdgcn_exp2f(z[h] - m_run[h]);  // 0 where masked
-    const float nb = shfl_down_f32(pr, 4);                       // token t + 1
+    const float nb = dpp_f32<kRowShl4>(pr);                      // token t + 1
     const uint32_t pair = pack_bf16(pr, nb);
     l_run[h] += bf16_lo(pair);
 #pragma unroll
@@ -190,7 +284,8 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(LocalAttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform_i32(tid >> 6);
 
   int row = s;
   if (a.q_indptr) {
@@ -206,6 +301,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   if (split >= nsplit) return;
   const int my0 = pg0 + split_lo(npg, nsplit, split);
   const int my1 = pg0 + split_lo(npg, nsplit, split + 1);
+  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
 
   // q of the group, this lane's quarter of the dims, as bf16 pairs
   const int c = lane & 3;
@@ -230,29 +326,48 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     for (int j = 0; j < 4; ++j) acc[h][j] = 0.f;
   }
 
+  // this wave's pages: my0 + w + 4k, k < nw; their physical ids, 64 at a
+  // time, sit one per lane and are read back with v_readlane
   const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride;
-  const uint8_t* head_base = a.pool + (int64_t)g * a.head_bytes;
+  const int nw = (my1 - my0 - w + kLocalWaves - 1) / kLocalWaves;
+  uint8_t* head_base = const_cast<uint8_t*>(a.pool) + (int64_t)g * a.head_bytes + lane * 16;
+  int ptv = 0;
+  auto refill = [&](int k0) __attribute__((always_inline)) {
+    const int idx = my0 + w + kLocalWaves * (k0 + lane);
+    ptv = idx < my1 ? pt[idx] : 0;
+  };
+  auto page_ptr = [&](int k) __attribute__((always_inline)) {
+    return head_base + (int64_t)(int)readlane_u32((uint32_t)ptv, k & 63) * a.page_bytes;
+  };
+  auto run_page = [&](PageRegs<FP8>& r, int k) __attribute__((always_inline)) {
+    const int lp = my0 + w + kLocalWaves * k;
+    if (append_here && lp == (p >> 4)) patch_new_token<FP8>(r, page_ptr(k), a, row, g, p, lane);
+    process_page<G, FP8>(r, qr, lp, lo, p, a.scale_log2, lane, m_run, l_run, acc);
+  };
 
-  // software pipeline: the next page of this wave is in flight while the
-  // current one is processed
   PageRegs<FP8> A, B;
-  int i = my0 + w;
-  if (i < my1) load_page<FP8>(A, head_base, a.page_bytes, uniform_i32(pt[i]), lane);
-  while (i < my1) {
-    int n = i + kLocalWaves;
-    if (n < my1) load_page<FP8>(B, head_base, a.page_bytes, uniform_i32(pt[n]), lane);
-    process_page<G, FP8>(A, qr, i, lo, p, a.scale_log2, lane, m_run, l_run, acc);
-    i = n;
-    if (i >= my1) break;
-    n = i + kLocalWaves;
-    if (n < my1) load_page<FP8>(A, head_base, a.page_bytes, uniform_i32(pt[n]), lane);
-    process_page<G, FP8>(B, qr, i, lo, p, a.scale_log2, lane, m_run, l_run, acc);
-    i = n;
+  if (nw > 0) {
+    refill(0);
+    load_page<FP8>(A, page_ptr(0));
+  }
+  for (int k = 0; k < nw; k += 2) {
+    if (k + 1 < nw) {
+      if (((k + 1) & 63) == 0) refill(k + 1);
+      load_page<FP8>(B, page_ptr(k + 1));
+    }
+    run_page(A, k);
+    if (k + 1 >= nw) break;
+    if (k + 2 < nw) {
+      if (((k + 2) & 63) == 0) refill(k + 2);
+      load_page<FP8>(A, page_ptr(k + 2));
+    }
+    run_page(B, k + 1);
   }
 
   // ---- merge the four waves in LDS, in wave order
   __shared__ float sm_acc[kLocalWaves][G][kLocalD];
   __shared__ float sm_m[kLocalWaves][G], sm_l[kLocalWaves][G];
+  __shared__ int sm_last;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float lv = (c == 0) ? l_run[h] : 0.f;   // one lane per token slot
@@ -269,31 +384,69 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   __syncthreads();
 
   const int d = tid;   // 256 threads, one output dim each
+  float o[G], M[G], lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = sm_m[0][h];
+    M[h] = sm_m[0][h];
 #pragma unroll
-    for (int ww = 1; ww < kLocalWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
-    float lsum = 0.f, o = 0.f;
+    for (int ww = 1; ww < kLocalWaves; ++ww) M[h] = fmaxf(M[h], sm_m[ww][h]);
+    lsum[h] = 0.f;
+    o[h] = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kLocalWaves; ++ww) {
       const float mw = sm_m[ww][h];
-      const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lsum += sm_l[ww][h] * sw;
-      o += sm_acc[ww][h][d] * sw;
-    }
-    const int qh = g * G + h;
-    if (nsplit == 1) {
-      a.out[((int64_t)row * a.num_q_heads + qh) * kLocalD + d] = o / lsum;
-    } else {
-      const int64_t pi = ((int64_t)s * a.num_q_heads + qh) * a.max_splits + split;
-      a.part_acc[pi * kLocalD + d] = o;
-      if (d == 0) {
-        a.part_ml[pi * 2 + 0] = M;
-        a.part_ml[pi * 2 + 1] = lsum;
-      }
+      const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M[h]);
+      lsum[h] += sm_l[ww][h] * sw;
+      o[h] += sm_acc[ww][h][d] * sw;
     }
   }
+  if (nsplit == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = o[h] / lsum[h];
+    return;
+  }
+
+  // ---- publish this split's partial; the last split of the pair to finish
+  // reduces all of them in split order.  The partials are written and read
+  // with device-scope accesses (written through to memory, read past the
+  // per-XCD L2), and the stores have completed before the counter moves, so
+  // no whole-cache write-back or invalidate is needed.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int64_t pi = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits + split;
+    __hip_atomic_store(a.part_acc + pi * kLocalD + d, o[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(a.part_ml + pi * 2 + 0, M[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + pi * 2 + 1, lsum[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  wait_stores_done();
+  __syncthreads();
+  int* counter = a.counters + (int64_t)s * a.num_kv_heads + g;
+  if (tid == 0)
+    sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!sm_last) return;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int64_t base = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits;
+    float Mx = -INFINITY;
+    for (int i = 0; i < nsplit; ++i)
+      Mx = fmaxf(Mx, __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float ls = 0.f, ov = 0.f;
+    for (int i = 0; i < nsplit; ++i) {
+      const float mi = __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float li = __hip_atomic_load(a.part_ml + (base + i) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float ai = __hip_atomic_load(a.part_acc + (base + i) * kLocalD + d, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      const float sw = __builtin_amdgcn_exp2f(mi - Mx);
+      ls += li * sw;
+      ov += ai * sw;
+    }
+    a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = ov / ls;
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
 }
 
 // Cross-split reduce, in split order: M = max m_i, l = sum l_i 2^(m_i - M),

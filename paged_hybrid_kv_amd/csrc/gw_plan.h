@@ -9,8 +9,9 @@
 namespace gw {
 
 // Local family: ranges up to the window (65 pages at window 1024) cut into
-// splits of at least 16 pages: 5 splits x 13 pages for a full window.
-constexpr int kLocalMinPagesPerSplit = 16;
+// splits of at least 17 pages: 4 splits of 16-17 pages for a full window,
+// so 16 rows x 8 KV heads fill the GPU with 512 workgroups in one round.
+constexpr int kLocalMinPagesPerSplit = 17;
 constexpr int kLocalMaxSplits = 16;
 
 // Global family: 2-page tiles (32 tokens); splits of at least 8 tiles

@@ -155,7 +155,8 @@ def upload_global(case: GlobalCase, compressed: bool = True, device="cuda",
 
 
 class Workspace:
-    """Grow-only device workspace, 256-byte aligned."""
+    """Grow-only device workspace, 256-byte aligned, zero-filled when
+    (re)allocated; the library leaves it ready for the next call."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -165,15 +166,18 @@ class Workspace:
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes + 256:
-            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
         addr = self.buf.data_ptr()
         aligned = (addr + 255) // 256 * 256
         return aligned, nbytes
 
 
 def attend(dc: DeviceCase, out: torch.Tensor | None = None, ws: Workspace | None = None,
-           stream=None) -> torch.Tensor:
-    """One attention call over an uploaded workload; returns fp32 [rows][Hq][D]."""
+           stream=None, k_new=None, v_new=None, rope=None) -> torch.Tensor:
+    """One attention call over an uploaded workload; returns fp32 [rows][Hq][D].
+
+    k_new/v_new (+ rope = (cos, sin)): append each row's own token in the call.
+    """
     local = dc.pool.family == gw.GW_FAMILY_LOCAL
     D = dc.pool.head_dim
     if out is None:
@@ -182,12 +186,15 @@ def attend(dc: DeviceCase, out: torch.Tensor | None = None, ws: Workspace | None
     need = gw.gw_attn_workspace_bytes(dc.pool.family, dc.num_seqs, dc.num_rows, dc.num_q_heads, D,
                                       dc.max_seq_len, dc.window if local else 0, dc.max_q_len)
     wptr, wbytes = ws.get(need)
+    cos, sin = rope if rope is not None else (None, None)
     if local:
-        gw.gw_decode_attn_local(dc.pool.desc, dc.q, dc.num_q_heads, dc.q_indptr, dc.seq_lens,
+        gw.gw_decode_attn_local(dc.pool.desc, dc.q, dc.num_q_heads, k_new, v_new, cos, sin,
+                                dc.q_indptr, dc.seq_lens,
                                 dc.page_table, dc.pt_stride, dc.num_seqs, dc.num_rows, dc.max_q_len,
                                 dc.max_seq_len, dc.window, dc.scale, out, wptr, wbytes, stream)
     else:
-        gw.gw_decode_attn_global(dc.pool.desc, dc.q, dc.num_q_heads, dc.q_indptr, dc.seq_lens,
+        gw.gw_decode_attn_global(dc.pool.desc, dc.q, dc.num_q_heads, v_new, cos, sin,
+                                 dc.q_indptr, dc.seq_lens,
                                  dc.page_table, dc.pt_stride, dc.num_seqs, dc.num_rows, dc.max_q_len,
                                  dc.max_seq_len, dc.scale, out, wptr, wbytes, stream)
     return out

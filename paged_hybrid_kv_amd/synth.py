@@ -270,3 +270,74 @@ class HybridShape:
         extra = [self.prompt_len] * self.prompts if with_prompts else []
         return np.concatenate([np.ones(self.decode_slots, dtype=np.int64),
                                np.array(extra, dtype=np.int64)])
+
+
+# ----------------------------------------------------------------------------
+# per-layer draws of the hybrid step, made on the device (torch's seeded
+# generator) so that 60 layers of context can be drawn in seconds; the same
+# call on any device returns the same values, so the oracle can re-draw a
+# layer on the host side of a test.
+# ----------------------------------------------------------------------------
+@dataclass
+class LayerDraws:
+    """Raw N(0,1) draws of one layer (bf16, before any rotation).
+
+    q        [rows][Hq][D]          query rows (decode rows, then prompt rows)
+    k_new    [n_new][Hkv][D] | None K of the tokens appended in the step
+    v_new    [n_new][Hkv][D] (local) or [n_new][D] (global)
+    k_prior, v_prior: the same for the context already in the cache
+    """
+    q: object
+    k_new: object
+    v_new: object
+    k_prior: object
+    v_prior: object
+
+
+def step_tokens(shape: HybridShape, with_prompts: bool, local: bool):
+    """(seq, pos) of the tokens appended in the step and of the prior context.
+
+    Decode slot s appends its current token at L_s - 1; prompt i (sequence
+    16 + i) appends positions 0..511.  Prior context: positions from the first
+    allocated page (local: the window's first page; global: 0) to L_s - 2.
+    """
+    lens = shape.lens(with_prompts)
+    new_s, new_p, pri_s, pri_p = [], [], [], []
+    for s in range(shape.decode_slots):
+        L = int(lens[s])
+        new_s.append([s]); new_p.append([L - 1])
+        lo = (max(0, L - shape.window) // PAGE) * PAGE if local else 0
+        pri_s.append(np.full(L - 1 - lo, s)); pri_p.append(np.arange(lo, L - 1))
+    if with_prompts:
+        for i in range(shape.prompts):
+            s = shape.decode_slots + i
+            new_s.append(np.full(shape.prompt_len, s)); new_p.append(np.arange(shape.prompt_len))
+    cat = lambda xs: np.concatenate([np.asarray(x, dtype=np.int32) for x in xs]) if xs else np.zeros(0, np.int32)
+    return cat(new_s), cat(new_p), cat(pri_s), cat(pri_p)
+
+
+def layer_draws(shape: HybridShape, layer: int, with_prompts: bool, device="cuda") -> LayerDraws:
+    """Draw layer ``layer``'s inputs with seed layer_seed_base + layer, in the
+    fixed order q -> K new -> V new -> K prior -> V prior (global: no K)."""
+    import torch
+    local = not shape.is_global(layer)
+    g = torch.Generator(device=device)
+    g.manual_seed(shape.layer_seed_base + layer)
+    new_s, _, pri_s, _ = step_tokens(shape, with_prompts, local)
+    rows = int(shape.q_len(with_prompts).sum())
+    if local:
+        Hq, Hkv, D = shape.local_q_heads, shape.local_kv_heads, shape.local_head_dim
+        kv = (Hkv, D)
+    else:
+        Hq, D = shape.global_q_heads, shape.global_head_dim
+        kv = (D,)
+
+    def draw(*sz):
+        return torch.randn(*sz, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+    q = draw(rows, Hq, D)
+    k_new = draw(len(new_s), *kv) if local else None
+    v_new = draw(len(new_s), *kv)
+    k_prior = draw(len(pri_s), *kv) if local else None
+    v_prior = draw(len(pri_s), *kv)
+    return LayerDraws(q, k_new, v_new, k_prior, v_prior)

@@ -108,16 +108,17 @@ def test_append_zero_tokens_is_noop():
     append(desc(), n=0)   # returns GW_OK without touching the GPU
 
 
-def local(d=None, q=FAKE, hq=16, indptr=None, lens=FAKE, pt=FAKE, stride=512, S=4, rows=4, mql=1,
-          msl=8192, win=1024, scale=0.0625, out=FAKE, ws=FAKE, wsb=1 << 30):
-    gw.gw_decode_attn_local(d or desc(), q, hq, indptr, lens, pt, stride, S, rows, mql, msl, win, scale,
-                            out, ws, wsb, None)
+def local(d=None, q=FAKE, hq=16, kn=None, vn=None, cos=None, sin=None, indptr=None, lens=FAKE, pt=FAKE,
+          stride=512, S=4, rows=4, mql=1, msl=8192, win=1024, scale=0.0625, out=FAKE, ws=FAKE,
+          wsb=1 << 30):
+    gw.gw_decode_attn_local(d or desc(), q, hq, kn, vn, cos, sin, indptr, lens, pt, stride, S, rows, mql,
+                            msl, win, scale, out, ws, wsb, None)
 
 
-def glob(d=None, q=FAKE, hq=32, indptr=None, lens=FAKE, pt=FAKE, stride=8192, S=4, rows=4, mql=1,
-         msl=131072, scale=0.044, out=FAKE, ws=FAKE, wsb=1 << 30):
-    gw.gw_decode_attn_global(d or desc(gw.GW_FAMILY_GLOBAL_COMPRESSED), q, hq, indptr, lens, pt, stride,
-                             S, rows, mql, msl, scale, out, ws, wsb, None)
+def glob(d=None, q=FAKE, hq=32, vn=None, cos=None, sin=None, indptr=None, lens=FAKE, pt=FAKE,
+         stride=8192, S=4, rows=4, mql=1, msl=131072, scale=0.044, out=FAKE, ws=FAKE, wsb=1 << 30):
+    gw.gw_decode_attn_global(d or desc(gw.GW_FAMILY_GLOBAL_COMPRESSED), q, hq, vn, cos, sin, indptr, lens,
+                             pt, stride, S, rows, mql, msl, scale, out, ws, wsb, None)
 
 
 @pytest.mark.parametrize("call,code,frag", [
@@ -136,6 +137,11 @@ def glob(d=None, q=FAKE, hq=32, indptr=None, lens=FAKE, pt=FAKE, stride=8192, S=
     (lambda: local(ws=None), gw.GW_ERR_INVALID_ARG, "workspace is null"),
     (lambda: local(ws=FAKE + 8), gw.GW_ERR_INVALID_ARG, "aligned"),
     (lambda: local(d=desc(dt=gw.GW_KV_BF16, page=8)), gw.GW_ERR_GEOMETRY, "page_size"),
+    (lambda: local(kn=FAKE), gw.GW_ERR_INVALID_ARG, "k_new and v_new"),
+    (lambda: local(kn=FAKE, vn=FAKE), gw.GW_ERR_INVALID_ARG, "needs rotary tables"),
+    (lambda: local(kn=FAKE, vn=FAKE, cos=FAKE), gw.GW_ERR_INVALID_ARG, "both"),
+    (lambda: local(d=desc(rot=0), kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE), gw.GW_ERR_INVALID_ARG,
+     "takes no rotary tables"),
 ])
 def test_local_rejects(call, code, frag):
     with pytest.raises(gw.GwError) as e:
@@ -152,6 +158,7 @@ def test_local_rejects(call, code, frag):
      "e4m3 supports only the local family"),
     (lambda: glob(wsb=0), gw.GW_ERR_WORKSPACE, "workspace"),
     (lambda: glob(msl=0), gw.GW_ERR_INVALID_ARG, "max_seq_len"),
+    (lambda: glob(vn=FAKE), gw.GW_ERR_INVALID_ARG, "rotary tables"),
 ])
 def test_global_rejects(call, code, frag):
     with pytest.raises(gw.GwError) as e:
@@ -167,9 +174,9 @@ def test_empty_batches_are_noops():
 
 
 def test_workspace_plan():
-    # one window of 1024 tokens spans at most 65 pages -> 5 splits of >= 13 pages
+    # one window of 1024 tokens spans at most 65 pages -> 4 splits of 16-17 pages
     ws = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 16, 16, 16, 256, 8192, 1024, 1)
-    assert ws >= 16 * 16 * 5 * 258 * 4
+    assert ws >= 16 * 16 * 4 * 258 * 4
     assert gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 1, 1, 2, 256, 64, 32, 1) == 0
     wg = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_GLOBAL_COMPRESSED, 8, 8, 32, 512, 131072, 0, 1)
     assert wg >= 8 * 32 * 64 * 514 * 4
