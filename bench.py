@@ -71,6 +71,20 @@ def dominant_kernel(step, rounds):
             "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of nbytes, reps times: under a counter
+    run it shows what FETCH_SIZE / WRITE_SIZE read for exactly nbytes moved
+    each way."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"copy calibration: {reps} x {nbytes} B device copy")
+
+
 def cpu_baseline(step):
     """The oracle as it stands, on a bounded sample of the same workload:
     the decode rows of layers 0 and 1 (local) and 5 (global)."""
@@ -135,6 +149,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="replay the step eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-rounds", type=int, default=10)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy three times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -180,6 +197,9 @@ def main():
     except gw.GwError as e:
         mixed = {"served": False, "reason": e.message}
     torch.cuda.empty_cache()
+
+    if args.copy_calib:
+        copy_calibration()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(step)
     if cpu:

@@ -326,42 +326,50 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     for (int j = 0; j < 4; ++j) acc[h][j] = 0.f;
   }
 
-  // this wave's pages: my0 + w + 4k, k < nw; their physical ids, 64 at a
-  // time, sit one per lane and are read back with v_readlane
+  // This wave's pages are my0 + w + 4k, k < nw.  The wave holding the
+  // split's last page (where a decode row's new token sits) takes that page
+  // first and the rest in order; every other wave goes in order.  The order
+  // is the same whether or not the call appends, so results are too.
+  // Physical ids, 64 at a time, sit one per lane and come back by readlane.
   const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride;
   const int nw = (my1 - my0 - w + kLocalWaves - 1) / kLocalWaves;
+  const int w_last = (my1 - 1 - my0) % kLocalWaves;
+  const bool last_first = (w == w_last);
+  const int first_k = last_first ? nw - 1 : 0;
+  const int rest0 = last_first ? 0 : 1;          // k of the 2nd page in order
   uint8_t* head_base = const_cast<uint8_t*>(a.pool) + (int64_t)g * a.head_bytes + lane * 16;
   int ptv = 0;
   auto refill = [&](int k0) __attribute__((always_inline)) {
     const int idx = my0 + w + kLocalWaves * (k0 + lane);
     ptv = idx < my1 ? pt[idx] : 0;
   };
-  auto page_ptr = [&](int k) __attribute__((always_inline)) {
+  auto page_at = [&](int k) __attribute__((always_inline)) {
     return head_base + (int64_t)(int)readlane_u32((uint32_t)ptv, k & 63) * a.page_bytes;
   };
-  auto run_page = [&](PageRegs<FP8>& r, int k) __attribute__((always_inline)) {
-    const int lp = my0 + w + kLocalWaves * k;
-    if (append_here && lp == (p >> 4)) patch_new_token<FP8>(r, page_ptr(k), a, row, g, p, lane);
-    process_page<G, FP8>(r, qr, lp, lo, p, a.scale_log2, lane, m_run, l_run, acc);
-  };
+  auto k_of = [&](int i) __attribute__((always_inline)) { return i == 0 ? first_k : rest0 + i - 1; };
 
   PageRegs<FP8> A, B;
   if (nw > 0) {
+    const int phys_first = uniform_i32(pt[my0 + w + kLocalWaves * first_k]);
+    uint8_t* first_ptr = head_base + (int64_t)phys_first * a.page_bytes;
+    load_page<FP8>(A, first_ptr);
     refill(0);
-    load_page<FP8>(A, page_ptr(0));
+    if (append_here && last_first) patch_new_token<FP8>(A, first_ptr, a, row, g, p, lane);
   }
-  for (int k = 0; k < nw; k += 2) {
-    if (k + 1 < nw) {
-      if (((k + 1) & 63) == 0) refill(k + 1);
-      load_page<FP8>(B, page_ptr(k + 1));
+  for (int i = 0; i < nw; i += 2) {
+    if (i + 1 < nw) {
+      const int k1 = k_of(i + 1);
+      if ((k1 & 63) == 0 && k1 > 0) refill(k1);
+      load_page<FP8>(B, page_at(k1));
     }
-    run_page(A, k);
-    if (k + 1 >= nw) break;
-    if (k + 2 < nw) {
-      if (((k + 2) & 63) == 0) refill(k + 2);
-      load_page<FP8>(A, page_ptr(k + 2));
+    process_page<G, FP8>(A, qr, my0 + w + kLocalWaves * k_of(i), lo, p, a.scale_log2, lane, m_run, l_run, acc);
+    if (i + 1 >= nw) break;
+    if (i + 2 < nw) {
+      const int k2 = k_of(i + 2);
+      if ((k2 & 63) == 0 && k2 > 0) refill(k2);
+      load_page<FP8>(A, page_at(k2));
     }
-    run_page(B, k + 1);
+    process_page<G, FP8>(B, qr, my0 + w + kLocalWaves * k_of(i + 1), lo, p, a.scale_log2, lane, m_run, l_run, acc);
   }
 
   // ---- merge the four waves in LDS, in wave order
