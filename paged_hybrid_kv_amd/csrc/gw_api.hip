@@ -86,8 +86,7 @@ int check_pool(const gw_pool_desc* p, const char* fn) {
 // Largest split count of any decode row of a call.
 int max_splits_for(int family, int max_seq_len, int window) {
   if (family == GW_FAMILY_LOCAL) return gw::local_nsplit(gw::local_max_range_pages(max_seq_len, window));
-  const int tiles = gw::cdiv_i(gw::cdiv_i(max_seq_len, 16), gw::kGlobalTilePages);
-  return gw::global_nsplit(tiles);
+  return gw::global_nsplit(gw::cdiv_i(max_seq_len, 16));
 }
 
 // Workspace: [split counters | partial accumulators | partial (max, sum)].

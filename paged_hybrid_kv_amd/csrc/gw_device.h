@@ -123,6 +123,44 @@ __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the four lanes holding one
+// MFMA 16x16 column): v_permlane32_swap / v_permlane16_swap exchange the
+// halves / the 16-lane rows of a register with itself, so each step pairs a
+// lane with its xor-32 / xor-16 partner without going through LDS.  The
+// result is the same in all four lanes.
+__device__ __forceinline__ float max_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(f32_to_bits(x), f32_to_bits(x), false, false);
+  x = fmaxf(bits_to_f32((uint32_t)a[0]), bits_to_f32((uint32_t)a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(f32_to_bits(x), f32_to_bits(x), false, false);
+  return fmaxf(bits_to_f32((uint32_t)b[0]), bits_to_f32((uint32_t)b[1]));
+}
+__device__ __forceinline__ float sum_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(f32_to_bits(x), f32_to_bits(x), false, false);
+  x = bits_to_f32((uint32_t)a[0]) + bits_to_f32((uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(f32_to_bits(x), f32_to_bits(x), false, false);
+  return bits_to_f32((uint32_t)b[0]) + bits_to_f32((uint32_t)b[1]);
+}
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes at gptr land at LDS byte address lds_base + 16 l, where
+// lds_base (wave-uniform) goes in M0.  Written as inline assembly so that the
+// compiler does not treat every later LDS read as possibly aliasing the
+// transfer (it would wait for all outstanding loads before each one); the
+// caller waits for completion itself (wait_vmcnt) before a barrier.
+__device__ __forceinline__ void dma16_to_lds(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// s_waitcnt vmcnt(N): at most N vector memory operations of this wave left
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
 __device__ __forceinline__ int split_lo(int n, int k, int i) {
   return (int)(((long long)n * i) / k);

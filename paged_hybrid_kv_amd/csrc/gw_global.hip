@@ -9,24 +9,31 @@
 // Both records take the same arithmetic, so their results are bit-identical.
 //
 // With every q head on one KV head the score and value steps are dense
-// contractions (32 heads x 16 tokens x 512 dims per page), so both run on
-// MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   S^T (32 tokens x 32 heads) = K (32 x 512) . Q^T (512 x 32)
-//   O^T (512 dims x 32 heads) += V^T (512 x 32 tokens) . P^T (32 x 32 heads)
-// Work split: one workgroup per (split, sequence); a split is a balanced run
-// of 2-page tiles (gw_plan.h).  The four waves of a workgroup each own 128
-// of the 512 dims: wave w forms the partial S over its dims (wave 0 from the
-// K_rot block, waves 1-3 from V, read once for both products), the partials
-// are summed in LDS in wave order, and every wave then runs the same online
-// softmax and accumulates its 128 output dims.  V reaches the PV operand
-// layout (8 consecutive tokens of one dim per lane) through a wave-private
-// LDS transpose.
+// contractions (heads x 16 tokens x 512 dims per page), so both run on MFMA
+// with fp32 accumulation, in 16 x 16 blocks:
+//   S^T (16 tokens x 16 heads) = K (16 x 512) . Q^T (512 x 16 heads)
+//                                  -- v_mfma_f32_16x16x32_bf16, 16 steps
+//   O^T (16 dims x 16 heads)  += V^T (16 x 16 tokens) . P^T (16 x 16 heads)
+//                                  -- v_mfma_f32_16x16x16_bf16, per dim block
+// The S^T result already sits in the lanes as the P^T operand wants it (lane
+// l: head l % 16, tokens 4(l/16) .. +3), so the softmax of a page stays in
+// the wave: no score exchange between waves.
 //
-// Lane roles: with l32 = lane % 32 and hf = lane / 32, the S output gives
-// lane (l32, hf) head l32 and tokens 8(r/4) + 4hf + r%4 (r < 16); those same
-// registers, rounded to bf16 pairs, are the P operand of the PV product, by
-// ordering its 16-token contraction as slot (8hf + e) of step ks <-> token
-// 16ks + 8(e/4) + 4hf + e%4.  P's rounding is also what the sum l adds.
+// Work split: one workgroup per (sequence, split) item, numbered compactly
+// (workgroup b takes item b); a split is a balanced run of the row's pages
+// (gw_plan.h).  A workgroup is two groups of four waves that take alternate
+// pages of the split, each with its own online-softmax state, merged at the
+// end.  Inside a group, wave w takes head block w % 2 (16 heads; with 16 q
+// heads, the only block) and a slice of the output dims (256 dims per wave
+// with 32 heads, 128 with 16).  Pages stream straight from HBM into a ring
+// of LDS page pairs (global_load_lds_dwordx4, each wave moving a quarter of
+// its group's page), NP - 1 pairs in flight while one is read; after an
+// LDS-only barrier each wave reads K (as stored) and V^T (through the gfx950
+// transposing LDS read ds_read_b64_tr_b16) from its group's page.  On the
+// row's last page, V of tokens past the row's position is zeroed in the
+// operand registers and their scores are masked, so unwritten slots (possibly
+// NaN) never reach the output.  P is rounded to bf16 for PV and the sum l
+// adds exactly those rounded values.
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -36,212 +43,277 @@ namespace gw {
 namespace {
 
 constexpr int kGD = 512;
-constexpr int kGWaves = 4;
-constexpr int kVtStride = 40;    // uint16 per row of the V^T tile (32 used; 80-byte rows)
 
-// token <-> PV contraction slot: swap bits 2 and 3
-__device__ __forceinline__ int slot_of_token(int t) {
-  return (t & ~0xC) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
+// LDS ring depth in page pairs, compressed / full record (3 x 40 KiB and
+// 2 x 64 KiB: one workgroup per CU either way).
+#ifndef GW_GLOBAL_NP_C
+#define GW_GLOBAL_NP_C 3
+#endif
+#ifndef GW_GLOBAL_NP_F
+#define GW_GLOBAL_NP_F 2
+#endif
 
-struct TileRegs {
-  uint4 k[8];
-  uint4 v[8];
-};
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Write a wave's V fragments (token l32, dims 16kc + 8hf + e) transposed into
-// its LDS tile: row = local dim, column = contraction slot of the token.
-__device__ __forceinline__ void stage_vt(uint16_t (*vt)[kVtStride], const uint4 (&src)[8], bool zero,
-                                         int hf, int l32) {
-  const int col = slot_of_token(l32);
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    uint32_t d4[4] = {src[kc].x, src[kc].y, src[kc].z, src[kc].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) d4[j] = zero ? 0u : d4[j];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t wv = d4[e >> 1];
-      vt[16 * kc + 8 * hf + e][col] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffff));
-    }
-  }
+// Barrier that orders LDS accesses only: outstanding global loads stay in
+// flight across it, and the compiler does not move LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <bool COMPRESSED>
-__global__ __launch_bounds__(256, 1) void global_decode_kernel(GlobalAttnArgs a) {
-  const int split = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int hf = lane >> 5, l32 = lane & 31;
-
-  int row = s;
-  if (a.q_indptr) {
-    row = a.q_indptr[s];
-    if (a.q_indptr[s + 1] - row != 1) return;
+struct GlobalPage {
+  static constexpr int kBytes = COMPRESSED ? 20480 : 32768;
+  static constexpr int kLoads = kBytes / 4096;            // 16-byte loads per thread (256 threads)
+  static constexpr int kVOff = COMPRESSED ? 0 : 16384;    // V block inside the page
+  // byte offset of chunk c (8 dims) of token t of K inside the page
+  __device__ static __forceinline__ int k_off(int c, int t) {
+    if constexpr (COMPRESSED) return c < 16 ? 16384 + (c * 16 + t) * 16 : (c * 16 + t) * 16;
+    else return (c * 16 + t) * 16;
   }
+};
+
+// Wait until at most k page pairs' transfers of this wave remain in flight
+// (k = pairs issued after the one about to be read; 0 <= k <= 4).
+template <int kPerPair>
+__device__ __forceinline__ void wait_pairs_after(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kPerPair>(); break;
+    case 2: wait_vmcnt<2 * kPerPair>(); break;
+    case 3: wait_vmcnt<3 * kPerPair>(); break;
+    default: wait_vmcnt<4 * kPerPair>(); break;
+  }
+}
+
+// One workgroup = two groups of four waves.  Group q (0, 1) takes the pages
+// 2j + q of the split: in every step j the two groups work on the two pages
+// of pair j side by side (one wave of each group per SIMD, so the phases of
+// one overlap the other's), each with its own online-softmax state; the two
+// states merge once at the end, group 1 into group 0, in that order.
+// NP: page pairs in the LDS ring (NP - 1 pairs in flight while one is read).
+template <bool COMPRESSED, int HB, int NP>
+__global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a) {
+  using PG = GlobalPage<COMPRESSED>;
+  constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
+  constexpr int kPerWave = kUnits / 4;        // units per wave per pair
+  constexpr int kBlocks = 8 * HB;             // 16-dim output blocks per wave
+  static_assert(NP >= 2 && kPerWave * (NP - 2) < 64 && NP - 2 <= 4, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NP][2][PG::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform_i32(tid >> 6);
+  const int grp = wv >> 2, w = wv & 3;
+  const int hb = HB == 2 ? (w & 1) : 0;
+  const int d_lo = HB == 2 ? 256 * (w >> 1) : 128 * w;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // ---- work item of this workgroup: the call's (sequence, split) items are
+  // numbered sequence by sequence, and workgroup b takes item b, so the
+  // active workgroups are 0 .. items-1 and spread evenly over the XCDs
+  int s = -1, split = 0, nsplit = 1;
+  {
+    const int b = blockIdx.x;
+    int base = 0;
+    for (int c = 0; c < a.num_seqs; c += 64) {
+      const int sl = c + lane;
+      int cnt = 0;
+      if (sl < a.num_seqs && (!a.q_indptr || a.q_indptr[sl + 1] - a.q_indptr[sl] == 1))
+        cnt = global_nsplit(((a.seq_lens[sl] - 1) >> 4) + 1);
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int up = __shfl_up(incl, d, 64);
+        incl += lane >= d ? up : 0;
+      }
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (b < base + total) {
+        const uint64_t hit = __ballot(base + incl > b);
+        const int ls = __builtin_ctzll(hit);
+        s = c + ls;
+        nsplit = __builtin_amdgcn_readlane(cnt, ls);
+        split = b - (base + __builtin_amdgcn_readlane(incl, ls) - nsplit);
+        break;
+      }
+      base += total;
+    }
+  }
+  if (s < 0) return;
+  s = uniform_i32(s);
+  split = uniform_i32(split);
+  nsplit = uniform_i32(nsplit);
+  const int row = a.q_indptr ? a.q_indptr[s] : s;
   const int L = a.seq_lens[s];
   const int p = L - 1;
   const int n_pages = (p >> 4) + 1;
-  const int n_tiles = cdiv_i(n_pages, kGlobalTilePages);
-  const int nsplit = global_nsplit(n_tiles);
-  if (split >= nsplit) return;
-  const int t0 = split_lo(n_tiles, nsplit, split);
-  const int t1 = split_lo(n_tiles, nsplit, split + 1);
+  const int pg0 = split_lo(n_pages, nsplit, split);
+  const int n = split_lo(n_pages, nsplit, split + 1) - pg0;
+  const int n_pairs = (n + 1) >> 1;
+  const int head = 16 * hb + l16;
 
-  __shared__ __attribute__((aligned(16))) float sbuf[2][kGWaves][64][16];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kGWaves][128][kVtStride];
-
-  // ---- Q fragments (B operand of S^T): head l32, dims 128w + 16kc + 8hf + e
-  bf16x8 qf[8];
-  {
-    const bool head_ok = l32 < a.num_q_heads;
-    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + (head_ok ? l32 : 0)) * kGD + 128 * w + 8 * hf;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      uint4 v = ld16_cached(qp + 16 * kc);
-      if (!head_ok) v = uint4{0u, 0u, 0u, 0u};
-      qf[kc] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  // ---- where this lane's 16-byte pieces sit inside a page (kc = 0; +512 B per kc)
-  const int slot = l32 & 15;
-  const int chunk0 = 16 * w + hf;                  // 8-dim chunk of dims 128w + 8hf
-  int k_off, v_off;
-  if constexpr (COMPRESSED) {
-    k_off = (w == 0) ? 16 * 512 * 2 + ((hf * 16) + slot) * 16 : (chunk0 * 16 + slot) * 16;
-    v_off = (chunk0 * 16 + slot) * 16;
-  } else {
-    k_off = (chunk0 * 16 + slot) * 16;
-    v_off = 16 * 512 * 2 + k_off;
-  }
-  const bool sep_v = !COMPRESSED || w == 0;       // V needs its own registers
-  const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride;
-
-  auto load_tile = [&](TileRegs& r, int tile) {
-    const int lp0 = tile * 2;
-    const int ph0 = uniform_i32(pt[lp0]);
-    const int ph1 = (lp0 + 1 < n_pages) ? uniform_i32(pt[lp0 + 1]) : ph0;
-    const uint8_t* base = a.pool + (int64_t)((l32 < 16) ? ph0 : ph1) * a.page_bytes;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) r.k[kc] = ld16(base + k_off + 512 * kc);
-    if (sep_v) {
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) r.v[kc] = ld16(base + v_off + 512 * kc);
-    }
+  // ---- physical page ids of the split, one per lane and register (a split
+  // has at most 256 pages); read back with readlane, so the page loop issues
+  // no vector memory operation the compiler would wait on
+  const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride + pg0;
+  auto pt_at = [&](int idx) __attribute__((always_inline)) { return idx < n ? pt[idx] : 0; };
+  const int ptv0 = pt_at(lane);
+  const int ptv1 = n > 64 ? pt_at(64 + lane) : 0;
+  const int ptv2 = n > 128 ? pt_at(128 + lane) : 0;
+  const int ptv3 = n > 192 ? pt_at(192 + lane) : 0;
+  auto phys = [&](int i) __attribute__((always_inline)) {
+    const int l = i & 63;
+    return i < 64 ? __builtin_amdgcn_readlane(ptv0, l)
+         : i < 128 ? __builtin_amdgcn_readlane(ptv1, l)
+         : i < 192 ? __builtin_amdgcn_readlane(ptv2, l)
+                   : __builtin_amdgcn_readlane(ptv3, l);
   };
 
+  // ---- transfers: group q moves page 2j + q of pair j, wave w of the group
+  // the units [kPerWave w, kPerWave (w + 1)) of the page (1 KiB each), so
+  // the LDS copy has the pool's layout.  An odd split's last pair repeats
+  // its last page as the second one; that copy is never computed on.
+  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) +
+                             (uint32_t)(grp * PG::kBytes + 1024 * kPerWave * w);
+  auto issue_pair = [&](int j) __attribute__((always_inline)) {
+    const int i = min(2 * j + grp, n - 1);
+    const uint8_t* src = a.pool + (int64_t)phys(i) * a.page_bytes + 1024 * kPerWave * w + 16 * lane;
+    const uint32_t dst = ring_base + (uint32_t)((j % NP) * 2 * PG::kBytes);
+#pragma unroll
+    for (int u = 0; u < kPerWave; ++u) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+  };
+#pragma unroll
+  for (int j = 0; j < NP - 1; ++j)
+    if (j < n_pairs) issue_pair(j);
+
+  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7.  The empty asm
+  // consumes the registers here, so the compiler waits for these loads once,
+  // before the page loop, instead of at every use inside it (it does not see
+  // the page transfers, and its wait would hold for them too).
+  bf16x8 qf[16];
+  {
+    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + head) * kGD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+
+  f32x4 acc[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 acc[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
-  int cur = 0;
+  // transposing-read lane roles: lane (g, e, q) names token 4g + e, dims
+  // d0 + 4q .. +3 and receives dim d0 + l16 of tokens 4g .. 4g+3
+  const int t_rd = 4 * g + (l16 >> 2);
+  const int q4 = 4 * (l16 & 3);
+  const int v_lane_off = PG::kVOff + (((d_lo + q4) >> 3) * 16 + t_rd) * 16 + ((d_lo + q4) & 7) * 2;
 
-  auto process_tile = [&](TileRegs& r, int tile) {
-    // S^T partial over this wave's 128 dims
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r.k[kc]), qf[kc], sacc, 0, 0, 0);
+  for (int j = 0; j < n_pairs; ++j) {
+    wait_pairs_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
+    lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
+    if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
+    const int i = 2 * j + grp;
+    if (i >= n) continue;
+    const uint8_t* pg = ring[j % NP][grp];
 
-    // V of tokens past p (unwritten slots, or the stand-in second page) -> 0,
-    // then V^T into this wave's LDS tile (row = local dim, column = slot)
-    const int tok0 = tile * 32;
-    const bool zero_v = tok0 + l32 > p;
-    if (sep_v) stage_vt(vt[w], r.v, zero_v, hf, l32);
-    else stage_vt(vt[w], r.k, zero_v, hf, l32);
-    // exchange score partials; every wave sums them in wave order
-    *reinterpret_cast<f32x4*>(&sbuf[cur][w][lane][0]) = f32x4{sacc[0], sacc[1], sacc[2], sacc[3]};
-    *reinterpret_cast<f32x4*>(&sbuf[cur][w][lane][4]) = f32x4{sacc[4], sacc[5], sacc[6], sacc[7]};
-    *reinterpret_cast<f32x4*>(&sbuf[cur][w][lane][8]) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
-    *reinterpret_cast<f32x4*>(&sbuf[cur][w][lane][12]) = f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
-    __syncthreads();
-    float z[16];
+    // ---- S^T = K . Q^T: all 16 K fragments are read first (their LDS
+    // latencies overlap), then two accumulation chains; lane holds head l16,
+    // tokens 4g .. 4g+3
+    bf16x8 kf[16];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[cur][0][lane][4 * q4]);
+    for (int ks = 0; ks < 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * ks + g, l16));
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-      for (int ww = 1; ww < kGWaves; ++ww) v += *reinterpret_cast<const f32x4*>(&sbuf[cur][ww][lane][4 * q4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[4 * q4 + j] = v[j];
+    for (int ks = 0; ks < 16; ks += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
     }
-    cur ^= 1;
+    const f32x4 sacc = s0 + s1;
 
-    // online softmax for head l32 over this lane's 16 tokens (+ partner half)
-    float mx = -INFINITY;
+    // ---- online softmax for head l16 over the page's 16 tokens
+    const int tok0 = (pg0 + i) * 16 + 4 * g;
+    float z[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = tok0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      z[r] = (tok <= p) ? z[r] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, z[r]);
-    }
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * a.scale_log2 : -INFINITY;
+    const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     const float mnew = fmaxf(m_run, mx);
     if (__any(mnew > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
+      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
       l_run *= alpha;
     }
     m_run = mnew;
-    uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(z[2 * i] - m_run);
-      const float p1 = __builtin_amdgcn_exp2f(z[2 * i + 1] - m_run);
-      pk[i] = pack_bf16(p0, p1);
-      l_run += bf16_lo(pk[i]);
-      l_run += bf16_hi(pk[i]);
-    }
+    const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
+    const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
+    l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+    const s16x4 pb = __builtin_bit_cast(s16x4, uint2{p01, p23});
 
-    // O^T += V^T . P^T over the two 16-token contraction steps
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const uint4 av = *reinterpret_cast<const uint4*>(&vt[w][32 * mb + l32][16 * ks + 8 * hf]);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, acc[mb], 0, 0, 0);
-      }
+    // ---- O^T += V^T . P^T.  On the row's last page, V of tokens past p
+    // (unwritten slots, possibly NaN) is zeroed in the operand registers.
+    uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
+    if ((pg0 + i) * 16 + 15 > p) {
+      vm0 = (tok0 + 0 <= p ? 0x0000ffffu : 0u) | (tok0 + 1 <= p ? 0xffff0000u : 0u);
+      vm1 = (tok0 + 2 <= p ? 0x0000ffffu : 0u) | (tok0 + 3 <= p ? 0xffff0000u : 0u);
     }
-  };
-
-  TileRegs A, B;
-  int tile = t0;
-  if (tile < t1) load_tile(A, tile);
-  while (tile < t1) {
-    int n = tile + 1;
-    if (n < t1) load_tile(B, n);
-    process_tile(A, tile);
-    tile = n;
-    if (tile >= t1) break;
-    n = tile + 1;
-    if (n < t1) load_tile(A, n);
-    process_tile(B, tile);
-    tile = n;
+    lds_u8* vrow = (lds_u8*)pg + v_lane_off;
+    uint2 vf[kBlocks];
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b)
+      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+      uint2 vv = vf[b];
+      vv.x &= vm0;
+      vv.y &= vm1;
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+    }
   }
 
-  // ---- write: lane holds head l32, dims 128w + 32mb + 8g + 4hf + j
-  const float l_tot = l_run + shfl_xor_f32(l_run, 32);
-  if (l32 >= a.num_q_heads) return;
+  // ---- merge group 1 into group 0 through LDS (the ring is free now):
+  // M = max(m0, m1), acc = acc0 2^(m0 - M) + acc1 2^(m1 - M), same for l
+  lds_barrier();
+  float* xa = reinterpret_cast<float*>(&ring[0][0][0]) + (w * kBlocks * 64 + lane) * 4;
+  float* xm = reinterpret_cast<float*>(&ring[0][0][0]) + 4 * kBlocks * 64 * 4 + (w * 64 + lane) * 2;
+  if (grp == 1) {
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(xa + b * 256) = acc[b];
+    xm[0] = m_run;
+    xm[1] = l_run;
+  }
+  lds_barrier();
+  if (grp == 1) return;
+  {
+    const float m1 = xm[0], l1 = xm[1];
+    const float M = fmaxf(m_run, m1);
+    const float s0 = __builtin_amdgcn_exp2f(m_run - M);
+    const float s1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) acc[b] = acc[b] * s0 + *reinterpret_cast<const f32x4*>(xa + b * 256) * s1;
+    l_run = l_run * s0 + l1 * s1;
+    m_run = M;
+  }
+
+  // ---- write: lane holds head 16hb + l16, dims d_lo + 16b + 4g .. +3
+  const float l_tot = sum_lanes_xor16_32(l_run);
   if (nsplit == 1) {
-    float* op = a.out + ((int64_t)row * a.num_q_heads + l32) * kGD + 128 * w + 4 * hf;
+    float* op = a.out + ((int64_t)row * a.num_q_heads + head) * kGD + d_lo + 4 * g;
+    const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(op + 32 * mb + 8 * g) =
-            f32x4{acc[mb][4 * g] / l_tot, acc[mb][4 * g + 1] / l_tot, acc[mb][4 * g + 2] / l_tot,
-                  acc[mb][4 * g + 3] / l_tot};
+    for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
   } else {
-    const int64_t pi = ((int64_t)s * a.num_q_heads + l32) * a.max_splits + split;
-    float* op = a.part_acc + pi * kGD + 128 * w + 4 * hf;
+    const int64_t pi = ((int64_t)s * a.num_q_heads + head) * a.max_splits + split;
+    float* op = a.part_acc + pi * kGD + d_lo + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(op + 32 * mb + 8 * g) =
-            f32x4{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
-    if (w == 0 && hf == 0) {
+    for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b];
+    if (d_lo == 0 && g == 0) {
       a.part_ml[pi * 2 + 0] = m_run;
       a.part_ml[pi * 2 + 1] = l_tot;
     }
@@ -251,9 +323,16 @@ __global__ __launch_bounds__(256, 1) void global_decode_kernel(GlobalAttnArgs a)
 }  // namespace
 
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream) {
-  dim3 grid(a.max_splits, a.num_seqs), block(256);
-  if (compressed) hipLaunchKernelGGL((global_decode_kernel<true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((global_decode_kernel<false>), grid, block, 0, stream, a);
+  dim3 grid(a.max_splits * a.num_seqs), block(512);
+  const bool h32 = a.num_q_heads == 32;
+  constexpr int kNc = GW_GLOBAL_NP_C, kNf = GW_GLOBAL_NP_F;
+  if (compressed) {
+    if (h32) hipLaunchKernelGGL((global_decode_kernel<true, 2, kNc>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_decode_kernel<true, 1, kNc>), grid, block, 0, stream, a);
+  } else {
+    if (h32) hipLaunchKernelGGL((global_decode_kernel<false, 2, kNf>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_decode_kernel<false, 1, kNf>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -457,10 +457,14 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
 }
 
-// Cross-split reduce, in split order: M = max m_i, l = sum l_i 2^(m_i - M),
-// out = sum acc_i 2^(m_i - M) / l.  One workgroup per (sequence, q head),
-// four output dims per thread.
-__global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs a) {
+// Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
+// out = sum_i acc_i 2^(m_i - M) / l.  One workgroup per (sequence, q head):
+// thread t takes four output dims (t % (D/4)) and the splits i = t / (D/4)
+// (mod 4), in split order; the four groups' sums are added in group order
+// 0, 1, 2, 3 through LDS, so the result is fixed for a given split count.
+__global__ __launch_bounds__(512) void split_reduce_kernel(ReduceArgs a) {
+  __shared__ __attribute__((aligned(16))) float part[3][128][4];
+  __shared__ float lpart[3];
   const int s = blockIdx.x, h = blockIdx.y;
   int row = s;
   if (a.q_indptr) {
@@ -472,20 +476,48 @@ __global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs a) {
   if (a.window > 0) {
     nsplit = local_nsplit(local_range_pages(L - 1, a.window));
   } else {
-    nsplit = global_nsplit(cdiv_i(cdiv_i(L, kPage), kGlobalTilePages));
+    nsplit = global_nsplit(cdiv_i(L, kPage));
   }
   if (nsplit <= 1) return;
+  const int nd4 = a.head_dim / 4;                 // threads per split group
+  const int grp = threadIdx.x / nd4, d4 = (threadIdx.x % nd4) * 4;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_splits;
+  const float* ml = a.part_ml + base * 2;
   float M = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, a.part_ml[(base + i) * 2]);
+  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+  const float* pa = a.part_acc + base * a.head_dim + d4;
   float lsum = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  const int d4 = threadIdx.x * 4;
-  for (int i = 0; i < nsplit; ++i) {
-    const float sw = __builtin_amdgcn_exp2f(a.part_ml[(base + i) * 2] - M);
-    lsum += a.part_ml[(base + i) * 2 + 1] * sw;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_acc + (base + i) * a.head_dim + d4);
-    o += v * sw;
+  if (grp < 4) {
+    int i = grp;
+    for (; i + 12 < nsplit; i += 16) {            // four of this group's splits at a time
+      f32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(pa + (int64_t)(i + 4 * k) * a.head_dim);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float sw = __builtin_amdgcn_exp2f(ml[2 * (i + 4 * k)] - M);
+        lsum += ml[2 * (i + 4 * k) + 1] * sw;
+        o += v[k] * sw;
+      }
+    }
+    for (; i < nsplit; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(pa + (int64_t)i * a.head_dim);
+      const float sw = __builtin_amdgcn_exp2f(ml[2 * i] - M);
+      lsum += ml[2 * i + 1] * sw;
+      o += v * sw;
+    }
+    if (grp > 0) {
+      *reinterpret_cast<f32x4*>(&part[grp - 1][d4 / 4][0]) = o;
+      if (d4 == 0) lpart[grp - 1] = lsum;
+    }
+  }
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    o += *reinterpret_cast<const f32x4*>(&part[k][d4 / 4][0]);
+    lsum += lpart[k];
   }
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + h) * a.head_dim + d4) = o / lsum;
 }
@@ -503,7 +535,7 @@ hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipS
 }
 
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs, a.num_q_heads), block(a.head_dim / 4);
+  dim3 grid(num_seqs, a.num_q_heads), block(a.head_dim);
   hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }

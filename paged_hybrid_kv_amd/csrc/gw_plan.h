@@ -14,11 +14,13 @@ namespace gw {
 constexpr int kLocalMinPagesPerSplit = 17;
 constexpr int kLocalMaxSplits = 16;
 
-// Global family: 2-page tiles (32 tokens); splits of at least 8 tiles
-// (256 tokens), at most 64 per row -- 16..64 splits at 4K..128K tokens.
-constexpr int kGlobalTilePages = 2;
-constexpr int kGlobalMinTilesPerSplit = 8;
+// Global family: splits of at least 20 pages (320 tokens), at most 64 per
+// row unless that would put more than 256 pages in one split: 16 rows of
+// 2K..8K tokens make about 250 workgroups, one per CU in a single round; a
+// row takes 64 splits from 20K tokens on, and more from 256K tokens on.
+constexpr int kGlobalMinPagesPerSplit = 20;
 constexpr int kGlobalMaxSplits = 64;
+constexpr int kGlobalMaxPagesPerSplit = 256;
 
 __host__ __device__ inline int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 
@@ -28,10 +30,12 @@ __host__ __device__ inline int local_nsplit(int n_pages) {
   return k > kLocalMaxSplits ? kLocalMaxSplits : k;
 }
 
-__host__ __device__ inline int global_nsplit(int n_tiles) {
-  int k = cdiv_i(n_tiles, kGlobalMinTilesPerSplit);
+__host__ __device__ inline int global_nsplit(int n_pages) {
+  int k = cdiv_i(n_pages, kGlobalMinPagesPerSplit);
   k = k < 1 ? 1 : k;
-  return k > kGlobalMaxSplits ? kGlobalMaxSplits : k;
+  k = k > kGlobalMaxSplits ? kGlobalMaxSplits : k;
+  const int k_min = cdiv_i(n_pages, kGlobalMaxPagesPerSplit);
+  return k < k_min ? k_min : k;
 }
 
 // Pages touched by the window of a query at position p: [p_lo/16, p/16].
