@@ -127,8 +127,6 @@ int check_attn_common(const char* fn, const void* q, int num_q_heads, const int3
     return fail(GW_ERR_INVALID_ARG, fn, "q_indptr is null but num_rows %d != num_seqs %d", num_rows, num_seqs);
   if (!q_indptr && max_q_len != 1)
     return fail(GW_ERR_INVALID_ARG, fn, "q_indptr is null but max_q_len %d != 1", max_q_len);
-  if (max_q_len > 1)
-    return fail(GW_ERR_UNSUPPORTED, fn, "query rows with q_len > 1 are not served by this build");
   if (pt_stride < gw::cdiv_i(max_seq_len, 16))
     return fail(GW_ERR_INVALID_ARG, fn, "pt_stride %d < pages of max_seq_len %d", pt_stride, max_seq_len);
   if (num_seqs == 0 || num_rows == 0) return GW_OK;
@@ -292,8 +290,35 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
   (void)hipGetLastError();   // a stale error from earlier work is not ours to report
-  hipError_t e = gw::launch_local_decode(a, group, pool->kv_dtype == GW_KV_E4M3, (hipStream_t)stream);
+  const bool fp8 = pool->kv_dtype == GW_KV_E4M3;
+  hipError_t e;
+  if (max_q_len > 1 && v_new) {
+    // the prompt rows' own tokens go in first; the decode kernel appends its rows itself
+    gw::AppendArgs ap{};
+    ap.pool = const_cast<uint8_t*>(a.pool);
+    ap.page_bytes = a.page_bytes;
+    ap.head_bytes = a.head_bytes;
+    ap.k_raw = a.k_new;
+    ap.v = a.v_new;
+    ap.page_table = page_table;
+    ap.pt_stride = pt_stride;
+    ap.rope_cos = rope_cos;
+    ap.rope_sin = rope_sin;
+    ap.n_tok = num_rows;
+    ap.num_kv_heads = pool->num_kv_heads;
+    ap.q_indptr = q_indptr;
+    ap.seq_lens = seq_lens;
+    ap.num_seqs = num_seqs;
+    ap.skip_single = 1;
+    e = gw::launch_append_local(ap, fp8, rope_cos != nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  e = gw::launch_local_decode(a, group, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
+  if (max_q_len > 1) {
+    e = gw::launch_local_prefill(a, group, fp8, max_q_len, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
   return ok();
 }
 
@@ -316,7 +341,6 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
-  if (v_new) return fail(GW_ERR_UNSUPPORTED, fn, "appending inside the global call is not served by this build");
   const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0);
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
@@ -346,11 +370,36 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
   (void)hipGetLastError();
-  hipError_t e = gw::launch_global_decode(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, (hipStream_t)stream);
+  const bool compressed = pool->family == GW_FAMILY_GLOBAL_COMPRESSED;
+  hipError_t e;
+  if (v_new) {
+    // every row's own token goes in first (K is V before rotation)
+    gw::AppendArgs ap{};
+    ap.pool = const_cast<uint8_t*>(a.pool);
+    ap.page_bytes = a.page_bytes;
+    ap.head_bytes = (int32_t)a.page_bytes;
+    ap.v = a.v_new;
+    ap.page_table = page_table;
+    ap.pt_stride = pt_stride;
+    ap.rope_cos = rope_cos;
+    ap.rope_sin = rope_sin;
+    ap.n_tok = num_rows;
+    ap.num_kv_heads = 1;
+    ap.q_indptr = q_indptr;
+    ap.seq_lens = seq_lens;
+    ap.num_seqs = num_seqs;
+    e = gw::launch_append_global(ap, compressed, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  e = gw::launch_global_decode(a, compressed, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (w.max_splits > 1) {
     gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, 512, w.max_splits, 0};
     e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  if (max_q_len > 1) {
+    e = gw::launch_global_prefill(a, compressed, max_q_len, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ok();

@@ -30,6 +30,32 @@ __global__ void rope_table_kernel(float* cos_out, float* sin_out, int max_pos, i
   sin_out[idx] = (float)sin(ang);
 }
 
+// Sequence and position of appended token tok (see AppendArgs); false if
+// the token is left to another kernel.  Uniform over the workgroup.
+__device__ __forceinline__ bool append_target(const AppendArgs& a, int tok, int& s, int& ps) {
+  if (!a.seq_lens) {
+    s = a.seq_idx[tok];
+    ps = a.pos[tok];
+    return true;
+  }
+  if (!a.q_indptr) {                    // one row per sequence: its last token
+    s = tok;
+    ps = a.seq_lens[tok] - 1;
+    return !a.skip_single;
+  }
+  int lo = 0, hi = a.num_seqs;          // largest s with q_indptr[s] <= tok
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.q_indptr[mid] <= tok) lo = mid;
+    else hi = mid;
+  }
+  s = lo;
+  const int ql = a.q_indptr[s + 1] - a.q_indptr[s];
+  if (a.skip_single && ql == 1) return false;
+  ps = a.seq_lens[s] - ql + (tok - a.q_indptr[s]);
+  return true;
+}
+
 __device__ __forceinline__ void load4_bf16(const uint16_t* p, float (&x)[4]) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
   x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
@@ -42,7 +68,8 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float (&x)[4]) {
 template <bool FP8, bool ROPE>
 __global__ __launch_bounds__(64) void append_local_kernel(AppendArgs a) {
   const int tok = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
-  const int s = a.seq_idx[tok], ps = a.pos[tok];
+  int s, ps;
+  if (!append_target(a, tok, s, ps)) return;
   const int page = a.page_table[(int64_t)s * a.pt_stride + (ps >> 4)];
   const int slot = ps & 15;
   uint8_t* hb = a.pool + (int64_t)page * a.page_bytes + (int64_t)h * a.head_bytes;
@@ -113,7 +140,8 @@ __global__ __launch_bounds__(64) void append_local_kernel(AppendArgs a) {
 template <bool COMPRESSED>
 __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   const int tok = blockIdx.x, l = threadIdx.x;
-  const int s = a.seq_idx[tok], ps = a.pos[tok];
+  int s, ps;
+  if (!append_target(a, tok, s, ps)) return;
   const int page = a.page_table[(int64_t)s * a.pt_stride + (ps >> 4)];
   const int slot = ps & 15;
   uint16_t* pb = reinterpret_cast<uint16_t*>(a.pool + (int64_t)page * a.page_bytes);

@@ -161,6 +161,63 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Barrier that orders LDS accesses only: outstanding global loads stay in
+// flight across it, and the compiler does not move LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait until at most k groups of this wave's transfers remain in flight, a
+// group being kPer transfers (k = groups issued after the one about to be
+// read; 0 <= k <= 4).
+template <int kPer>
+__device__ __forceinline__ void wait_groups_after(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kPer>(); break;
+    case 2: wait_vmcnt<2 * kPer>(); break;
+    case 3: wait_vmcnt<3 * kPer>(); break;
+    default: wait_vmcnt<4 * kPer>(); break;
+  }
+}
+
+// Physical page ids of a run of n logical pages (pt[0 .. n)), held 64 per
+// register, 256 at a time, and read back with readlane, so a page loop that
+// streams pages by direct-to-LDS transfers issues no vector memory operation
+// the compiler would wait on.  Asking for page i >= base + 256 reloads the
+// next 256 (the loads are waited for at once, inside that rare branch, so
+// the compiler's wait stays there).  get() must be called with uniform,
+// non-decreasing i.
+struct PageIds {
+  const int32_t* pt;
+  int n, base, lane;
+  int v0, v1, v2, v3;
+  __device__ __forceinline__ void load(int b) {
+    base = b;
+    v0 = b + lane < n ? pt[b + lane] : 0;
+    v1 = b + 64 < n && b + 64 + lane < n ? pt[b + 64 + lane] : 0;
+    v2 = b + 128 < n && b + 128 + lane < n ? pt[b + 128 + lane] : 0;
+    v3 = b + 192 < n && b + 192 + lane < n ? pt[b + 192 + lane] : 0;
+    asm volatile("" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3));
+  }
+  __device__ __forceinline__ void init(const int32_t* pt_, int n_, int lane_) {
+    pt = pt_;
+    n = n_;
+    lane = lane_;
+    load(0);
+  }
+  __device__ __forceinline__ int get(int i) {
+    if (i >= base + 256) load(i & ~255);
+    const int k = i - base, l = k & 63;
+    return k < 64 ? __builtin_amdgcn_readlane(v0, l)
+         : k < 128 ? __builtin_amdgcn_readlane(v1, l)
+         : k < 192 ? __builtin_amdgcn_readlane(v2, l)
+                   : __builtin_amdgcn_readlane(v3, l);
+  }
+};
+
 // Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
 __device__ __forceinline__ int split_lo(int n, int k, int i) {
   return (int)(((long long)n * i) / k);

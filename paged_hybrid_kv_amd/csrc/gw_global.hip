@@ -58,14 +58,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Barrier that orders LDS accesses only: outstanding global loads stay in
-// flight across it, and the compiler does not move LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <bool COMPRESSED>
 struct GlobalPage {
   static constexpr int kBytes = COMPRESSED ? 20480 : 32768;
@@ -78,17 +70,82 @@ struct GlobalPage {
   }
 };
 
-// Wait until at most k page pairs' transfers of this wave remain in flight
-// (k = pairs issued after the one about to be read; 0 <= k <= 4).
-template <int kPerPair>
-__device__ __forceinline__ void wait_pairs_after(int k) {
-  switch (k) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<kPerPair>(); break;
-    case 2: wait_vmcnt<2 * kPerPair>(); break;
-    case 3: wait_vmcnt<3 * kPerPair>(); break;
-    default: wait_vmcnt<4 * kPerPair>(); break;
+// One page of one wave: scores of the wave's 16 heads against the page's 16
+// tokens over all 512 dims, the online-softmax update, and the PV product
+// into the wave's output-dim slice.  pg: the page in LDS; tok_page0: the
+// position of the page's first token; p: the row's position (tokens past it
+// are masked, and their V zeroed, so unwritten slots never reach the output).
+template <bool COMPRESSED, int HB>
+__device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
+                                                 const uint8_t* pg, const bf16x8 (&qf)[16],
+                                                 int tok_page0, int p, int g, int l16, int v_lane_off,
+                                                 float scale_log2) {
+  using PG = GlobalPage<COMPRESSED>;
+  constexpr int kBlocks = 8 * HB;
+  // ---- S^T = K . Q^T: all 16 K fragments are read first (their LDS
+  // latencies overlap), then two accumulation chains; lane holds head l16,
+  // tokens 4g .. 4g+3
+  bf16x8 kf[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * ks + g, l16));
+  __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+  for (int ks = 0; ks < 16; ks += 2) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
   }
+  const f32x4 sacc = s0 + s1;
+
+  // ---- online softmax for head l16 over the page's 16 tokens
+  const int tok0 = tok_page0 + 4 * g;
+  float z[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * scale_log2 : -INFINITY;
+  const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  const float mnew = fmaxf(m_run, mx);
+  if (__any(mnew > m_run)) {
+    const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
+    l_run *= alpha;
+  }
+  m_run = mnew;
+  const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
+  const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
+  l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+  const s16x4 pb = __builtin_bit_cast(s16x4, uint2{p01, p23});
+
+  // ---- O^T += V^T . P^T.  On the row's last page, V of tokens past p
+  // (unwritten slots, possibly NaN) is zeroed in the operand registers.
+  uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
+  if (tok_page0 + 15 > p) {
+    vm0 = (tok0 + 0 <= p ? 0x0000ffffu : 0u) | (tok0 + 1 <= p ? 0xffff0000u : 0u);
+    vm1 = (tok0 + 2 <= p ? 0x0000ffffu : 0u) | (tok0 + 3 <= p ? 0xffff0000u : 0u);
+  }
+  lds_u8* vrow = (lds_u8*)pg + v_lane_off;
+  uint2 vf[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b)
+    vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {
+    uint2 vv = vf[b];
+    vv.x &= vm0;
+    vv.y &= vm1;
+    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+  }
+}
+
+// Byte offset, inside a page, of what lane (g, l16) names in the transposing
+// read of V for dims d_lo .. (lane (g, e, q) names token 4g + e, dims
+// d_lo + 4q .. +3, and receives dim d_lo + l16 of tokens 4g .. 4g+3).
+template <bool COMPRESSED>
+__device__ __forceinline__ int global_v_lane_off(int d_lo, int g, int l16) {
+  const int t_rd = 4 * g + (l16 >> 2);
+  const int dd = d_lo + 4 * (l16 & 3);
+  return GlobalPage<COMPRESSED>::kVOff + ((dd >> 3) * 16 + t_rd) * 16 + (dd & 7) * 2;
 }
 
 // One workgroup = two groups of four waves.  Group q (0, 1) takes the pages
@@ -207,74 +264,18 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  // transposing-read lane roles: lane (g, e, q) names token 4g + e, dims
-  // d0 + 4q .. +3 and receives dim d0 + l16 of tokens 4g .. 4g+3
-  const int t_rd = 4 * g + (l16 >> 2);
-  const int q4 = 4 * (l16 & 3);
-  const int v_lane_off = PG::kVOff + (((d_lo + q4) >> 3) * 16 + t_rd) * 16 + ((d_lo + q4) & 7) * 2;
+  const int v_lane_off = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
 
   for (int j = 0; j < n_pairs; ++j) {
-    wait_pairs_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
+    wait_groups_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
     lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
     if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
     const int i = 2 * j + grp;
     if (i >= n) continue;
     const uint8_t* pg = ring[j % NP][grp];
 
-    // ---- S^T = K . Q^T: all 16 K fragments are read first (their LDS
-    // latencies overlap), then two accumulation chains; lane holds head l16,
-    // tokens 4g .. 4g+3
-    bf16x8 kf[16];
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * ks + g, l16));
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-    for (int ks = 0; ks < 16; ks += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
-    }
-    const f32x4 sacc = s0 + s1;
-
-    // ---- online softmax for head l16 over the page's 16 tokens
-    const int tok0 = (pg0 + i) * 16 + 4 * g;
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * a.scale_log2 : -INFINITY;
-    const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-    const float mnew = fmaxf(m_run, mx);
-    if (__any(mnew > m_run)) {
-      const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-#pragma unroll
-      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
-      l_run *= alpha;
-    }
-    m_run = mnew;
-    const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
-    const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
-    l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-    const s16x4 pb = __builtin_bit_cast(s16x4, uint2{p01, p23});
-
-    // ---- O^T += V^T . P^T.  On the row's last page, V of tokens past p
-    // (unwritten slots, possibly NaN) is zeroed in the operand registers.
-    uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
-    if ((pg0 + i) * 16 + 15 > p) {
-      vm0 = (tok0 + 0 <= p ? 0x0000ffffu : 0u) | (tok0 + 1 <= p ? 0xffff0000u : 0u);
-      vm1 = (tok0 + 2 <= p ? 0x0000ffffu : 0u) | (tok0 + 3 <= p ? 0xffff0000u : 0u);
-    }
-    lds_u8* vrow = (lds_u8*)pg + v_lane_off;
-    uint2 vf[kBlocks];
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
-      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) {
-      uint2 vv = vf[b];
-      vv.x &= vm0;
-      vv.y &= vm1;
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
-    }
+    global_page_step<COMPRESSED, HB>(acc, m_run, l_run, ring[j % NP][grp], qf, (pg0 + i) * 16, p, g, l16,
+                                     v_lane_off, a.scale_log2);
   }
 
   // ---- merge group 1 into group 0 through LDS (the ring is free now):
@@ -320,6 +321,92 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   }
 }
 
+// Prompt rows (sequences with more than one query row: a new prompt's
+// rows, computed in the same step as the decode rows -- pegainfer "Gemma 4"
+// page, Scheduling).  Row r of sequence s sits at position
+// p_r = seq_len - q_len + r and attends keys 0 .. p_r.  A workgroup takes two
+// consecutive rows: group q (four waves, as in the decode kernel) row 2m + q,
+// and both groups read the same stream of pages, pages 0 .. p_last / 16 of
+// the pair, through an LDS ring of NS pages moved by group 0.  No split: a
+// row's whole range is one pass, and the output is written directly.  The
+// pairs with the most pages are dispatched first.
+template <bool COMPRESSED, int HB, int NS>
+__global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a) {
+  using PG = GlobalPage<COMPRESSED>;
+  constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
+  constexpr int kPerWave = kUnits / 4;        // units per wave of group 0 per page
+  constexpr int kBlocks = 8 * HB;
+  static_assert(NS >= 2 && NS - 2 <= 4 && kPerWave * (NS - 2) < 64, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
+
+  const int s = blockIdx.x;
+  const int row0 = a.q_indptr[s];
+  const int q_len = a.q_indptr[s + 1] - row0;
+  if (q_len < 2) return;
+  const int mp = ((q_len + 1) >> 1) - 1 - (int)blockIdx.y;   // row pair, longest first
+  if (mp < 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform_i32(tid >> 6);
+  const int grp = wv >> 2, w = wv & 3;
+  const int hb = HB == 2 ? (w & 1) : 0;
+  const int d_lo = HB == 2 ? 256 * (w >> 1) : 128 * w;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int head = 16 * hb + l16;
+
+  const int L = a.seq_lens[s];
+  const int r = 2 * mp + grp;
+  const bool row_ok = r < q_len;                 // uniform in the group
+  const int r_last = min(2 * mp + 1, q_len - 1);
+  const int p = L - q_len + (row_ok ? r : r_last);
+  const int p_last = L - q_len + r_last;
+  const int n = (p_last >> 4) + 1;
+
+  PageIds ids;
+  ids.init(a.page_table + (int64_t)s * a.pt_stride, n, lane);
+  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0])) + (uint32_t)(1024 * kPerWave * w);
+  auto issue_page = [&](int i) __attribute__((always_inline)) {
+    if (grp != 0) return;
+    const uint8_t* src = a.pool + (int64_t)ids.get(i) * a.page_bytes + 1024 * kPerWave * w + 16 * lane;
+    const uint32_t dst = ring_base + (uint32_t)((i % NS) * PG::kBytes);
+#pragma unroll
+    for (int u = 0; u < kPerWave; ++u) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+  };
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < n) issue_page(i);
+
+  bf16x8 qf[16];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(row0 + (row_ok ? r : r_last)) * a.num_q_heads + head) * kGD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+
+  f32x4 acc[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int v_lane_off = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
+
+  for (int i = 0; i < n; ++i) {
+    wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
+    lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
+    if (i + NS - 1 < n) issue_page(i + NS - 1);
+    if (row_ok && i * 16 <= p)
+      global_page_step<COMPRESSED, HB>(acc, m_run, l_run, ring[i % NS], qf, i * 16, p, g, l16, v_lane_off,
+                                       a.scale_log2);
+  }
+  if (!row_ok) return;
+  const float l_tot = sum_lanes_xor16_32(l_run);
+  float* op = a.out + ((int64_t)(row0 + r) * a.num_q_heads + head) * kGD + d_lo + 4 * g;
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
+}
+
 }  // namespace
 
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream) {
@@ -332,6 +419,19 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStr
   } else {
     if (h32) hipLaunchKernelGGL((global_decode_kernel<false, 2, kNf>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((global_decode_kernel<false, 1, kNf>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
+  dim3 grid(a.num_seqs, (max_q_len + 1) / 2), block(512);
+  const bool h32 = a.num_q_heads == 32;
+  if (compressed) {
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 4>), grid, block, 0, stream, a);
+  } else {
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 3>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 3>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

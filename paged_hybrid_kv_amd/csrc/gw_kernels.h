@@ -78,12 +78,24 @@ struct AppendArgs {
   const float* rope_sin;
   int32_t n_tok;
   int32_t num_kv_heads;
+  // Rows mode (seq_lens non-null): token i is query row i of an attention
+  // call -- its sequence found in q_indptr (or i itself when q_indptr is
+  // null: one row per sequence), its position seq_lens[s] - q_len +
+  // (i - q_indptr[s]); seq_idx / pos are unused.  skip_single: leave out the
+  // rows of one-row sequences (their decode kernel appends them).
+  const int32_t* q_indptr;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t skip_single;
 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the
 // hipGetLastError() status of the launch.
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream);
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream);
+hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int max_q_len,
+                                hipStream_t stream);
+hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream);
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStream_t stream);
 hipError_t launch_append_global(const AppendArgs& a, bool compressed, hipStream_t stream);

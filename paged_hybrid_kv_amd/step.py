@@ -105,13 +105,11 @@ class HybridStep:
         gw.gw_kv_append(L["pool"].desc, L["k_new"], L["v_new"], si, pos, n, L["pt"], L["stride"],
                         L["cos"], L["sin"])
 
-    def fused_append(self, L) -> bool:
-        """Whether this layer's attention call appends the rows' tokens itself
-        (decode rows of the local family: one token per row)."""
-        return L["local"] and self.max_q_len == 1
-
     def attend(self, L, out=None, append=False):
+        """One layer's attention call; with append=True the call also stores
+        every row's own token first (the prep step inside the call)."""
         sh = self.shape
+        fam = "local" if L["local"] else "global"
         if L["local"]:
             kn, vn, cs, sn = (L["k_new"], L["v_new"], L["cos"], L["sin"]) if append else (None,) * 4
             gw.gw_decode_attn_local(L["pool"].desc, L["q"], sh.local_q_heads, kn, vn, cs, sn,
@@ -119,23 +117,20 @@ class HybridStep:
                                     L["pt"], L["stride"], self.S, self.rows, self.max_q_len, self.max_len,
                                     sh.window, 1.0 / np.sqrt(sh.local_head_dim),
                                     self.out_local if out is None else out,
-                                    self.ws_ptr["local"], self.ws_bytes["local"])
+                                    self.ws_ptr[fam], self.ws_bytes[fam])
         else:
-            gw.gw_decode_attn_global(L["pool"].desc, L["q"], sh.global_q_heads, None, None, None,
-                                     self.q_indptr, self.seq_lens, L["pt"], L["stride"], self.S, self.rows, self.max_q_len,
-                                     self.max_len, 1.0 / np.sqrt(sh.global_head_dim),
+            vn, cs, sn = (L["v_new"], L["cos"], L["sin"]) if append else (None,) * 3
+            gw.gw_decode_attn_global(L["pool"].desc, L["q"], sh.global_q_heads, vn, cs, sn,
+                                     self.q_indptr, self.seq_lens, L["pt"], L["stride"], self.S, self.rows,
+                                     self.max_q_len, self.max_len, 1.0 / np.sqrt(sh.global_head_dim),
                                      self.out_global if out is None else out,
-                                     self.ws_ptr["global"], self.ws_bytes["global"])
+                                     self.ws_ptr[fam], self.ws_bytes[fam])
 
     def run(self):
-        """One step, eagerly: append then attend, layer by layer (the local
-        decode layers append inside their attention call)."""
+        """One step, eagerly: every layer's attention call appends the step's
+        new tokens (decode and prompt rows) and attends, layer by layer."""
         for L in self.layers:
-            if self.fused_append(L):
-                self.attend(L, append=True)
-            else:
-                self.append(L)
-                self.attend(L)
+            self.attend(L, append=True)
 
     def capture(self):
         """Capture the step as one HIP graph (after one eager run)."""

@@ -31,7 +31,7 @@ def resource_usage(src):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["gw_local.hip", "gw_global.hip", "gw_append.hip"])
+@pytest.mark.parametrize("src", ["gw_local.hip", "gw_global.hip", "gw_append.hip", "gw_prefill.hip"])
 def test_no_scratch(src):
     ks = resource_usage(src)
     assert ks, "no kernels compiled"
