@@ -372,8 +372,9 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   (void)hipGetLastError();
   const bool compressed = pool->family == GW_FAMILY_GLOBAL_COMPRESSED;
   hipError_t e;
-  if (v_new) {
-    // every row's own token goes in first (K is V before rotation)
+  if (v_new && max_q_len > 1) {
+    // the prompt rows' own tokens go in first (K is V before rotation); the
+    // decode kernel appends its rows itself
     gw::AppendArgs ap{};
     ap.pool = const_cast<uint8_t*>(a.pool);
     ap.page_bytes = a.page_bytes;
@@ -388,6 +389,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     ap.q_indptr = q_indptr;
     ap.seq_lens = seq_lens;
     ap.num_seqs = num_seqs;
+    ap.skip_single = 1;
     e = gw::launch_append_global(ap, compressed, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }

@@ -143,37 +143,8 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   int s, ps;
   if (!append_target(a, tok, s, ps)) return;
   const int page = a.page_table[(int64_t)s * a.pt_stride + (ps >> 4)];
-  const int slot = ps & 15;
-  uint16_t* pb = reinterpret_cast<uint16_t*>(a.pool + (int64_t)page * a.page_bytes);
-  const uint16_t* vsrc = a.v + (int64_t)tok * 512;
-
-  const uint4 vraw = *reinterpret_cast<const uint4*>(vsrc + 8 * l);
-  uint16_t* vblock = COMPRESSED ? pb : pb + 16 * 512;
-  *reinterpret_cast<uint4*>(vblock + (l * 16 + slot) * 8) = vraw;
-
-  uint16_t* kblock = COMPRESSED ? pb + 16 * 512 : pb;   // K_rot [16][128] or K [16][512]
-  if (l < 8) {
-    const uint4 praw = *reinterpret_cast<const uint4*>(vsrc + 64 + 8 * l);
-    const uint32_t xa_p[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
-    const uint32_t xb_p[4] = {praw.x, praw.y, praw.z, praw.w};
-    const float* cp = a.rope_cos + (int64_t)ps * 64 + 8 * l;
-    const float* sp = a.rope_sin + (int64_t)ps * 64 + 8 * l;
-    uint32_t ya[4], yb[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float a0 = bf16_lo(xa_p[m]), a1 = bf16_hi(xa_p[m]);
-      const float b0 = bf16_lo(xb_p[m]), b1 = bf16_hi(xb_p[m]);
-      float y0a, y0b, y1a, y1b;
-      rope_pair(a0, b0, cp[2 * m], sp[2 * m], y0a, y0b);
-      rope_pair(a1, b1, cp[2 * m + 1], sp[2 * m + 1], y1a, y1b);
-      ya[m] = pack_bf16(y0a, y1a);
-      yb[m] = pack_bf16(y0b, y1b);
-    }
-    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 8) = uint4{ya[0], ya[1], ya[2], ya[3]};
-    *reinterpret_cast<uint4*>(kblock + ((l + 8) * 16 + slot) * 8) = uint4{yb[0], yb[1], yb[2], yb[3]};
-  } else if (!COMPRESSED && l >= 16) {
-    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 8) = vraw;   // K dims >= 128 are V's
-  }
+  const GlobalRecordLane r = global_record_lane(a.v + (int64_t)tok * 512, a.rope_cos, a.rope_sin, ps, l);
+  put_global_record<COMPRESSED>(a.pool + (int64_t)page * a.page_bytes, r, ps & 15, l);
 }
 
 }  // namespace

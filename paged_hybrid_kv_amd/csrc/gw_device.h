@@ -218,6 +218,60 @@ struct PageIds {
   }
 };
 
+// One token's global-family record, computed by one wave (Gewell post,
+// "the Why": K and V are tied and only K's first 128 dims rotate, so the
+// record is V plus the rotated quarter of K).  Lane l holds V chunk l (dims
+// 8l .. 8l+7, bf16 as given); lanes 0..7 also hold K chunks l and l + 8
+// (dims 8l .. and 64 + 8l ..), rotated as rotate-half pairs (i, i + 64) by
+// position pos from the fp32 tables [pos][64], rounded to bf16.
+struct GlobalRecordLane {
+  uint4 v, ka, kb;
+};
+__device__ __forceinline__ GlobalRecordLane global_record_lane(const uint16_t* vsrc, const float* rope_cos,
+                                                               const float* rope_sin, int pos, int l) {
+  GlobalRecordLane r;
+  r.v = *reinterpret_cast<const uint4*>(vsrc + 8 * l);
+  r.ka = r.kb = uint4{0u, 0u, 0u, 0u};
+  if (l < 8) {
+    const uint4 praw = *reinterpret_cast<const uint4*>(vsrc + 64 + 8 * l);
+    const uint32_t xa_p[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+    const uint32_t xb_p[4] = {praw.x, praw.y, praw.z, praw.w};
+    const float* cp = rope_cos + (int64_t)pos * 64 + 8 * l;
+    const float* sp = rope_sin + (int64_t)pos * 64 + 8 * l;
+    uint32_t ya[4], yb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float a0 = bf16_lo(xa_p[m]), a1 = bf16_hi(xa_p[m]);
+      const float b0 = bf16_lo(xb_p[m]), b1 = bf16_hi(xb_p[m]);
+      float y0a, y0b, y1a, y1b;
+      rope_pair(a0, b0, cp[2 * m], sp[2 * m], y0a, y0b);
+      rope_pair(a1, b1, cp[2 * m + 1], sp[2 * m + 1], y1a, y1b);
+      ya[m] = pack_bf16(y0a, y1a);
+      yb[m] = pack_bf16(y0b, y1b);
+    }
+    r.ka = uint4{ya[0], ya[1], ya[2], ya[3]};
+    r.kb = uint4{yb[0], yb[1], yb[2], yb[3]};
+  }
+  return r;
+}
+
+// Store a token's record (global_record_lane of lane l) at slot `slot` of a
+// global page at pb (pool or LDS copy): compressed page = V[16][512] |
+// K_rot[16][128], full page = K[16][512] | V[16][512], blocks chunk-major
+// ((c*16 + t)*8 + e).
+template <bool COMPRESSED>
+__device__ __forceinline__ void put_global_record(uint8_t* pb, const GlobalRecordLane& r, int slot, int l) {
+  uint8_t* vblock = COMPRESSED ? pb : pb + 16384;
+  uint8_t* kblock = COMPRESSED ? pb + 16384 : pb;
+  *reinterpret_cast<uint4*>(vblock + (l * 16 + slot) * 16) = r.v;
+  if (l < 8) {
+    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 16) = r.ka;
+    *reinterpret_cast<uint4*>(kblock + ((l + 8) * 16 + slot) * 16) = r.kb;
+  } else if (!COMPRESSED && l >= 16) {
+    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 16) = r.v;   // K dims >= 128 are V's
+  }
+}
+
 // Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
 __device__ __forceinline__ int split_lo(int n, int k, int i) {
   return (int)(((long long)n * i) / k);

@@ -260,6 +260,20 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
     for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
+  // ---- a decode row's own token, when the call carries it: the workgroup
+  // of the row's last split rotates and stores it (as gw_kv_append does)
+  // and puts it into its LDS copy of that page once the page has landed.
+  // Its loads and stores are waited for here, before the page loop, so the
+  // loop's transfer counts stay exact.
+  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
+  GlobalRecordLane rec{};
+  if (append_here && wv == 0) {
+    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+    put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
+                                  p & 15, lane);
+    wait_vmcnt<0>();
+  }
+
   f32x4 acc[kBlocks];
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -270,6 +284,10 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
     wait_groups_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
     lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
     if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
+    if (append_here && j == ((n - 1) >> 1)) {
+      if (wv == 0) put_global_record<COMPRESSED>(&ring[j % NP][(n - 1) & 1][0], rec, p & 15, lane);
+      lds_barrier();
+    }
     const int i = 2 * j + grp;
     if (i >= n) continue;
     const uint8_t* pg = ring[j % NP][grp];

@@ -436,21 +436,31 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   __syncthreads();
   if (!sm_last) return;
+  // Every split's (max, sum, acc) is loaded at once -- indices past the last
+  // split repeat it and are not used -- so the merge costs one round trip;
+  // the sums then run in split order.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int64_t base = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits;
+    float mi[kLocalMaxSplits], li[kLocalMaxSplits], ai[kLocalMaxSplits];
+#pragma unroll
+    for (int i = 0; i < kLocalMaxSplits; ++i) {
+      const int64_t ic = base + min(i, nsplit - 1);
+      mi[i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      li[i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ai[i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     float Mx = -INFINITY;
-    for (int i = 0; i < nsplit; ++i)
-      Mx = fmaxf(Mx, __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int i = 0; i < kLocalMaxSplits; ++i) Mx = fmaxf(Mx, mi[i]);
     float ls = 0.f, ov = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
-      const float mi = __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float li = __hip_atomic_load(a.part_ml + (base + i) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float ai = __hip_atomic_load(a.part_acc + (base + i) * kLocalD + d, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      const float sw = __builtin_amdgcn_exp2f(mi - Mx);
-      ls += li * sw;
-      ov += ai * sw;
+#pragma unroll
+    for (int i = 0; i < kLocalMaxSplits; ++i) {
+      if (i < nsplit) {
+        const float sw = __builtin_amdgcn_exp2f(mi[i] - Mx);
+        ls += li[i] * sw;
+        ov += ai[i] * sw;
+      }
     }
     a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = ov / ls;
   }
