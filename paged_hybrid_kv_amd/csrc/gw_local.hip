@@ -72,96 +72,118 @@ __device__ __forceinline__ void u4_and(uint4& v, uint32_t m) {
   v.x &= m; v.y &= m; v.z &= m; v.w &= m;
 }
 
-// The new token of a decode row (slot p % 16 of the page just loaded into r):
-// rotate and round its K exactly as gw_kv_append does, patch it into the
-// registers and store K and V into the pool page at b (this lane's offsets).
-template <bool FP8>
-__device__ __forceinline__ void patch_new_token(PageRegs<FP8>& r, uint8_t* b, const LocalAttnArgs& a,
-                                               int row, int g, int p, int lane) {
-  const int slot = p & 15, t = lane >> 2, c = lane & 3;
-  const uint16_t* kr = a.k_new + ((int64_t)row * a.num_kv_heads + g) * kLocalD;
-  const uint16_t* vr = a.v_new + ((int64_t)row * a.num_kv_heads + g) * kLocalD;
-  // K: this lane's quarter, dims 64c .. 64c+63; rotation partners 128 apart.
-  // Each 16-byte chunk of the page register takes kPer dims, read with
-  // 16-byte loads (raw K, its partner dims, cos, sin).
-  const int d0 = 64 * c;
-  const int pd0 = (d0 + 128) & 255;
-  const bool lower = c < 2;
-  const bool rope = a.rope_cos != nullptr;
-  const float* cs = a.rope_cos + (int64_t)p * 128 + (d0 & 127);
-  const float* sn = a.rope_sin + (int64_t)p * 128 + (d0 & 127);
-  constexpr int kPer = FP8 ? 16 : 8;   // dims per 16-byte chunk of the page
-#pragma unroll
-  for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) {
-    uint32_t xo[kPer / 2], xp[kPer / 2];
-#pragma unroll
-    for (int q = 0; q < kPer / 8; ++q) {
-      const uint4 o4 = ld16_cached(kr + d0 + k * kPer + 8 * q);
-      const uint4 p4 = ld16_cached(kr + pd0 + k * kPer + 8 * q);
-      xo[4 * q] = o4.x; xo[4 * q + 1] = o4.y; xo[4 * q + 2] = o4.z; xo[4 * q + 3] = o4.w;
-      xp[4 * q] = p4.x; xp[4 * q + 1] = p4.y; xp[4 * q + 2] = p4.z; xp[4 * q + 3] = p4.w;
-    }
-    float cv[kPer], sv[kPer];
-    if (rope) {
-#pragma unroll
-      for (int q = 0; q < kPer / 4; ++q) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cs + k * kPer + 4 * q);
-        const float4 s4 = *reinterpret_cast<const float4*>(sn + k * kPer + 4 * q);
-        cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
-        sv[4 * q] = s4.x; sv[4 * q + 1] = s4.y; sv[4 * q + 2] = s4.z; sv[4 * q + 3] = s4.w;
-      }
-    }
-    float y[kPer];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const float x = (e & 1) ? bf16_hi(xo[e >> 1]) : bf16_lo(xo[e >> 1]);
-      const float xq = (e & 1) ? bf16_hi(xp[e >> 1]) : bf16_lo(xp[e >> 1]);
-      float ya, yb;
-      if (lower) rope_pair(x, xq, cv[e], sv[e], ya, yb);
-      else rope_pair(xq, x, cv[e], sv[e], yb, ya);
-      y[e] = rope ? ya : x;
-    }
-    uint4 wv;
-    if constexpr (!FP8) {
-      wv = uint4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-    } else {
-      uint32_t q4[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        q4[m] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) q4[m] |= f32_to_e4m3(round_bf16(y[4 * m + j])) << (8 * j);
-      }
-      wv = uint4{q4[0], q4[1], q4[2], q4[3]};
-    }
-    if (t == slot) {
-      r.k[k] = wv;
-      *reinterpret_cast<uint4*>(b + k * 1024) = wv;
+// The new token of a decode row: lane l loads K dims 4l..4l+3 with their
+// rotation partners 128 + 4l.. and the rotary factors (lanes < 32), and V
+// dims 4l..4l+3 (every lane), before the page itself, so the two overlap.
+struct NewTokenLoads {
+  uint2 kr, kp, v;
+  float4 cs, sn;
+};
+
+__device__ __forceinline__ NewTokenLoads load_new_token(const LocalAttnArgs& a, int row, int g, int p, int lane) {
+  NewTokenLoads t{};
+  const int64_t src = ((int64_t)row * a.num_kv_heads + g) * kLocalD;
+  if (lane < 32) {
+    t.kr = *reinterpret_cast<const uint2*>(a.k_new + src + 4 * lane);
+    t.kp = *reinterpret_cast<const uint2*>(a.k_new + src + 128 + 4 * lane);
+    if (a.rope_cos) {
+      t.cs = *reinterpret_cast<const float4*>(a.rope_cos + (int64_t)p * 128 + 4 * lane);
+      t.sn = *reinterpret_cast<const float4*>(a.rope_sin + (int64_t)p * 128 + 4 * lane);
     }
   }
-  // V: this lane's dims 4l..4l+3 of the token, into the pair / quad registers;
-  // the whole 16 bytes go back, the other tokens' parts unchanged.  (Register
-  // arrays are indexed with constants only, so they stay in registers.)
-  const uint2 raw = *reinterpret_cast<const uint2*>(vr + 4 * lane);
-  const uint32_t v16[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
+  t.v = *reinterpret_cast<const uint2*>(a.v_new + src + 4 * lane);
+  return t;
+}
+
+// Rotate and round the new token's K and store K and V into the pool (b:
+// the (page, KV head) record) element by element, exactly as gw_kv_append
+// does; then put the token into this wave's registers of that page: K
+// through the wave's own 1 KiB of LDS (sm_tok), V straight from the lane's
+// own dims.
+template <bool FP8>
+__device__ __forceinline__ void put_new_token(PageRegs<FP8>& r, uint8_t* b, const NewTokenLoads& t, bool rope,
+                                              int p, int lane, uint32_t* sm_tok) {
+  const int slot = p & 15;
+  if (lane < 32) {
+    float xa[4] = {bf16_lo(t.kr.x), bf16_hi(t.kr.x), bf16_lo(t.kr.y), bf16_hi(t.kr.y)};
+    float xb[4] = {bf16_lo(t.kp.x), bf16_hi(t.kp.x), bf16_lo(t.kp.y), bf16_hi(t.kp.y)};
+    float ya[4], yb[4];
+    const float c4[4] = {t.cs.x, t.cs.y, t.cs.z, t.cs.w}, s4[4] = {t.sn.x, t.sn.y, t.sn.z, t.sn.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (rope) rope_pair(xa[j], xb[j], c4[j], s4[j], ya[j], yb[j]);
+      else { ya[j] = xa[j]; yb[j] = xb[j]; }
+    }
+    // dims d = 4l..4l+3 (quarter c = l/16) and d + 128 (quarter c + 2)
+    const int c = lane >> 4;
+    if constexpr (!FP8) {
+      const int k = (lane & 15) >> 1, e0 = 4 * (lane & 1);
+      uint16_t* kb = reinterpret_cast<uint16_t*>(b);
+      const uint2 va = {pack_bf16(ya[0], ya[1]), pack_bf16(ya[2], ya[3])};
+      const uint2 vb = {pack_bf16(yb[0], yb[1]), pack_bf16(yb[2], yb[3])};
+      *reinterpret_cast<uint2*>(kb + ((k * 16 + slot) * 4 + c) * 8 + e0) = va;
+      *reinterpret_cast<uint2*>(kb + ((k * 16 + slot) * 4 + c + 2) * 8 + e0) = vb;
+      sm_tok[2 * lane] = va.x;
+      sm_tok[2 * lane + 1] = va.y;
+      sm_tok[64 + 2 * lane] = vb.x;
+      sm_tok[64 + 2 * lane + 1] = vb.y;
+    } else {
+      const int k = (lane & 15) >> 2, e0 = 4 * (lane & 3);
+      uint32_t wa = 0, wb = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wa |= f32_to_e4m3(round_bf16(ya[j])) << (8 * j);
+        wb |= f32_to_e4m3(round_bf16(yb[j])) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(b + ((k * 16 + slot) * 4 + c) * 16 + e0) = wa;
+      *reinterpret_cast<uint32_t*>(b + ((k * 16 + slot) * 4 + c + 2) * 16 + e0) = wb;
+      sm_tok[lane] = wa;
+      sm_tok[32 + lane] = wb;
+    }
+  }
+  // V: dims 4l + j of token slot -> interleaved pairs (bf16) or quads (e4m3)
+  const uint32_t v16[4] = {t.v.x & 0xffffu, t.v.x >> 16, t.v.y & 0xffffu, t.v.y >> 16};
+  uint32_t bits[4];
+  if constexpr (!FP8) {
+    uint16_t* vb = reinterpret_cast<uint16_t*>(b + LocalLayout<FP8>::kBlockBytes);
+    const int u = slot >> 1, i = slot & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vb[((u * 64 + lane) * 4 + j) * 2 + i] = (uint16_t)v16[j];
+      bits[j] = v16[j];
+    }
+  } else {
+    uint8_t* vb = b + LocalLayout<FP8>::kBlockBytes;
+    const int u = slot >> 2, i = slot & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bits[j] = f32_to_e4m3(bits_to_f32(v16[j] << 16));
+      vb[((u * 64 + lane) * 4 + j) * 4 + i] = (uint8_t)bits[j];
+    }
+  }
+  // registers: V of the token's slot in this lane's pair / quad registers
   constexpr int kTokPerReg = FP8 ? 4 : 2;
   const int u = slot / kTokPerReg;
   const int sh = (FP8 ? 8 : 16) * (slot % kTokPerReg);
   const uint32_t field = (FP8 ? 0xffu : 0xffffu) << sh;
-  uint32_t bits[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) bits[j] = (FP8 ? f32_to_e4m3(bits_to_f32(v16[j] << 16)) : v16[j]) << sh;
-  uint4 st = uint4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int uu = 0; uu < LocalLayout<FP8>::kLoads; ++uu) {
     const uint32_t m = (uu == u) ? field : 0u;
-    r.v[uu].x = (r.v[uu].x & ~m) | (bits[0] & m);
-    r.v[uu].y = (r.v[uu].y & ~m) | (bits[1] & m);
-    r.v[uu].z = (r.v[uu].z & ~m) | (bits[2] & m);
-    r.v[uu].w = (r.v[uu].w & ~m) | (bits[3] & m);
-    if (uu == u) st = r.v[uu];
+    r.v[uu].x = (r.v[uu].x & ~m) | ((bits[0] << sh) & m);
+    r.v[uu].y = (r.v[uu].y & ~m) | ((bits[1] << sh) & m);
+    r.v[uu].z = (r.v[uu].z & ~m) | ((bits[2] << sh) & m);
+    r.v[uu].w = (r.v[uu].w & ~m) | ((bits[3] << sh) & m);
   }
-  *reinterpret_cast<uint4*>(b + LocalLayout<FP8>::kBlockBytes + u * 1024) = st;
+  // K of the token's slot: lane (t = slot, c) holds dims 64c + kPer k .. of
+  // register k (kPer = 8 bf16 / 16 e4m3 per 16 bytes)
+  if ((lane >> 2) == slot) {
+    const int c = lane & 3;
+#pragma unroll
+    for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) {
+      const int w0 = FP8 ? 16 * c + 4 * k : 32 * c + 4 * k;   // first 32-bit word of the chunk
+      r.k[k] = uint4{sm_tok[w0], sm_tok[w0 + 1], sm_tok[w0 + 2], sm_tok[w0 + 3]};
+    }
+  }
 }
 
 template <int G, bool FP8>
@@ -348,13 +370,18 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   };
   auto k_of = [&](int i) __attribute__((always_inline)) { return i == 0 ? first_k : rest0 + i - 1; };
 
+  __shared__ uint32_t sm_tok[kLocalWaves][128];   // a patching wave's rotated token K
   PageRegs<FP8> A, B;
   if (nw > 0) {
+    const bool patch = append_here && last_first;
+    NewTokenLoads tok{};
+    if (patch) tok = load_new_token(a, row, g, p, lane);
     const int phys_first = uniform_i32(pt[my0 + w + kLocalWaves * first_k]);
     uint8_t* first_ptr = head_base + (int64_t)phys_first * a.page_bytes;
     load_page<FP8>(A, first_ptr);
     refill(0);
-    if (append_here && last_first) patch_new_token<FP8>(A, first_ptr, a, row, g, p, lane);
+    if (patch)
+      put_new_token<FP8>(A, first_ptr - lane * 16, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
   }
   for (int i = 0; i < nw; i += 2) {
     if (i + 1 < nw) {
