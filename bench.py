@@ -51,22 +51,52 @@ def time_events(fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
+COUNTER_FILE = os.path.join(ROOT, "profiles", "local_decode_hbm_counters.json")
+LOCAL_KERNEL_SOURCES = ["gw_local.hip", "gw_device.h", "gw_plan.h", "gw_kernels.h"]
+
+
+def local_kernel_hash():
+    """sha256 over the sources the local decode kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in LOCAL_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_hybrid_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the local decode kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or
+    None when the kernel's sources changed since the counters were taken."""
+    try:
+        with open(COUNTER_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != local_kernel_hash():
+        return None
+    return int(c["fetch_bytes_per_launch"] + c["write_bytes_per_launch"])
+
+
 def dominant_kernel(step, rounds):
-    """Local decode attention (50 of 60 layers, most of the KV bytes): average
+    """Local decode attention (50 of 60 layers, most of the KV bytes), called
+    as the step calls it (the row's own token appended in the call): average
     duration of one call, timed over all local layers so that consecutive
-    calls read different pools (no reuse through the 256 MB last-level cache)."""
+    calls read different pools (no reuse through the 256 MB last-level cache).
+    Re-appending a token writes the same bytes to the same slot."""
     local_layers = [L for L in step.layers if L["local"]]
 
     def sweep():
         for L in local_layers:
-            step.attend(L)
+            step.attend(L, append=True)
 
     sweep()
     ms = time_events(sweep, rounds) / len(local_layers)
     nbytes = step.local_decode_kv_bytes_per_layer()
     achieved = nbytes / (ms * 1e-3)
     return {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": measured_traffic(),
             "kernel": "local_decode_kernel<2,false> (gw_decode_attn_local)",
             "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
 
@@ -149,6 +179,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="replay the step eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-rounds", type=int, default=10)
+    ap.add_argument("--no-mixed", action="store_true", help="skip the step with prompt rows")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -185,14 +216,20 @@ def main():
 
     mixed = None
     try:
+        if args.no_mixed:
+            raise gw.GwError(0, "skipped (--no-mixed)")
         ms_step = HybridStep(with_prompts=True)
         if not args.no_graph:
             ms_step.capture()
         for _ in range(args.warmup):
             ms_step.replay()
         mms = time_events(ms_step.replay, args.steps)
+        mb = ms_step.mixed_step_bytes()
         mixed = {"ms_per_step": round(mms, 4), "decode_tok_s": round(16 / (mms * 1e-3), 1),
-                 "rows_per_s": round(ms_step.rows / (mms * 1e-3), 1), "rows": ms_step.rows}
+                 "rows_per_s": round(ms_step.rows / (mms * 1e-3), 1), "rows": ms_step.rows,
+                 "algorithmic_bytes": mb,
+                 "GB_per_s": round(mb["total"] / (mms * 1e-3) / 1e9, 1),
+                 "pct_of_peak": round(mb["total"] / (mms * 1e-3) / PEAK_HBM * 100, 2)}
         del ms_step
     except gw.GwError as e:
         mixed = {"served": False, "reason": e.message}

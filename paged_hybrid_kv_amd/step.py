@@ -158,6 +158,25 @@ class HybridStep:
         n_glob = sum(1 for l in range(sh.num_layers) if sh.is_global(l))
         return (sh.num_layers - n_glob) * local + n_glob * glob
 
+    def mixed_step_bytes(self) -> dict:
+        """Algorithmic bytes of one step with its prompt rows: every token's
+        K/V read once per layer by the rows that attend it (decode rows: the
+        window / whole context; prompt rows: the prompt once), the appended
+        tokens (raw K/V read, record written), and q read / out written."""
+        sh = self.shape
+        n_glob = sum(1 for l in range(sh.num_layers) if sh.is_global(l))
+        n_loc = sh.num_layers - n_glob
+        loc_tok = sh.local_kv_heads * 256 * 2 * 2            # K + V bf16, all KV heads
+        glob_tok = (512 + 128) * 2                          # compressed record
+        prompts = [int(x) for x in self.q_len[sh.decode_slots:]]
+        pre_tok = sum(prompts)
+        new_tok = sh.decode_slots + pre_tok
+        kv = self.decode_kv_bytes() + n_loc * pre_tok * loc_tok + n_glob * pre_tok * glob_tok
+        app = (n_loc * new_tok * (loc_tok + loc_tok) + n_glob * new_tok * (512 * 2 + glob_tok))
+        rows = self.rows
+        qo = (n_loc * rows * sh.local_q_heads * 256 * (2 + 4) + n_glob * rows * sh.global_q_heads * 512 * (2 + 4))
+        return {"kv_read": kv, "append": app, "q_out": qo, "total": kv + app + qo}
+
     def local_decode_kv_bytes_per_layer(self) -> int:
         sh = self.shape
         return sum(min(int(L), sh.window) for L in sh.decode_lens) * sh.local_kv_heads * 256 * 2 * 2
