@@ -12,7 +12,9 @@
 // stored first (the prep step), exactly as gw_kv_append stores it.
 //
 // Work split: one workgroup per (split, KV head, sequence); a split is a
-// balanced run of the pages of the row's window (gw_plan.h).  Four waves per
+// balanced run of the row's range in virtual pages (gw_plan.h: the two
+// partial pages at the ends of a full window are walked as one, so a
+// 1024-token window is 64 pages of work, 16 per split).  Four waves per
 // workgroup take every fourth page of the split, each with its own online
 // softmax state (running max m, sum l, accumulator), merged in LDS at the end.
 // The last workgroup of a (sequence, KV head) to finish merges the splits'
@@ -51,16 +53,39 @@ template <bool FP8>
 struct PageRegs {
   uint4 k[LocalLayout<FP8>::kLoads];
   uint4 v[LocalLayout<FP8>::kLoads];
+  uint4 vx;   // merged page: the V unit that straddles the two pages, from the first page
 };
 
+// Load one virtual page: slots t >= b from the (page, KV head) record r0,
+// slots t < b from r1 (r1 == r0 and b == 0 for an ordinary page).  K lane
+// 4t + c takes token t, so the choice is per lane; a V load u holds the
+// tokens of one pair (bf16) or quad (e4m3), so it is per instruction, and
+// the unit holding slots on both sides of b is loaded from both records.
 template <bool FP8>
-__device__ __forceinline__ void load_page(PageRegs<FP8>& r, const uint8_t* b) {
+__device__ __forceinline__ void load_vpage(PageRegs<FP8>& r, const uint8_t* r0, const uint8_t* r1, int b,
+                                           int lane) {
+  constexpr int kTok = FP8 ? 4 : 2;   // tokens per V unit
+  const uint8_t* kb = ((lane >> 2) >= b ? r0 : r1) + lane * 16;
 #pragma unroll
-  for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) r.k[k] = ld16(b + k * 1024);
+  for (int k = 0; k < LocalLayout<FP8>::kLoads; ++k) r.k[k] = ld16(kb + k * 1024);
 #pragma unroll
   for (int u = 0; u < LocalLayout<FP8>::kLoads; ++u)
-    r.v[u] = ld16(b + LocalLayout<FP8>::kBlockBytes + u * 1024);
+    r.v[u] = ld16((kTok * u >= b ? r0 : r1) + LocalLayout<FP8>::kBlockBytes + u * 1024 + lane * 16);
+  if (b % kTok != 0)
+    r.vx = ld16(r0 + LocalLayout<FP8>::kBlockBytes + (b / kTok) * 1024 + lane * 16);
 }
+
+// A page table (or other int32 array) read-only for the whole call, read
+// through the constant address space so uniform reads become scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* CI32P;
+
+// One virtual page of a wave's walk (load_vpage / process_page arguments).
+struct VPage {
+  const uint8_t* r0;
+  const uint8_t* r1;
+  int b;
+  uint32_t mask;
+};
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -186,12 +211,28 @@ __device__ __forceinline__ void put_new_token(PageRegs<FP8>& r, uint8_t* b, cons
   }
 }
 
+// One virtual page: b as in load_vpage, mask = its slots inside the row's
+// range (bit t for slot t; 0xffff for every page but the range's edges).
 template <int G, bool FP8>
 __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&qr)[G][32],
-                                             int lp, int lo, int p, float scale_log2, int lane,
+                                             uint32_t mask, int b, float scale_log2, int lane,
                                              float (&m_run)[G], float (&l_run)[G],
                                              float (&acc)[G][4]) {
   const int t = lane >> 2;
+  constexpr int kTok = FP8 ? 4 : 2;
+  if (b % kTok != 0) {
+    // the V unit holding slots b - 1 and b: slots >= b come from the first page
+    const uint32_t keep = FP8 ? (1u << (8 * (b % 4))) - 1u : 0x0000ffffu;
+#pragma unroll
+    for (int u = 0; u < LocalLayout<FP8>::kLoads; ++u) {
+      if (u == b / kTok) {
+        r.v[u].x = (r.v[u].x & keep) | (r.vx.x & ~keep);
+        r.v[u].y = (r.v[u].y & keep) | (r.vx.y & ~keep);
+        r.v[u].z = (r.v[u].z & keep) | (r.vx.z & ~keep);
+        r.v[u].w = (r.v[u].w & keep) | (r.vx.w & ~keep);
+      }
+    }
+  }
   // ---- scores: lane (t, c) dots its quarter of K_t with q, then quad sum
   float z[G];
 #pragma unroll
@@ -221,8 +262,7 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
     s += dpp_f32<kQuadSwap2>(s);
     z[h] = s;
   }
-  const int tok = lp * kPage + t;
-  const bool valid = tok >= lo && tok <= p;
+  const bool valid = (mask >> t) & 1u;
 #pragma unroll
   for (int h = 0; h < G; ++h) z[h] = valid ? z[h] * scale_log2 : -INFINITY;
 
@@ -252,16 +292,14 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
     for (int u = 0; u < 8; ++u) P[h][u] = readlane_u32(pair, 8 * u);
   }
 
-  // ---- V of masked tokens at the window's edge pages is zeroed, so that
+  // ---- V of masked slots (the range's edge pages only) is zeroed, so that
   // unwritten or stale slots (possibly NaN) contribute exactly 0.
-  const int base_tok = lp * kPage;
-  if (base_tok < lo || base_tok + kPage - 1 > p) {
+  if (mask != 0xffffu) {
     if constexpr (!FP8) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int t0 = base_tok + 2 * u;
-        const uint32_t m = ((t0 >= lo && t0 <= p) ? 0x0000ffffu : 0u) |
-                           ((t0 + 1 >= lo && t0 + 1 <= p) ? 0xffff0000u : 0u);
+        const uint32_t m = (((mask >> (2 * u)) & 1u) ? 0x0000ffffu : 0u) |
+                           (((mask >> (2 * u + 1)) & 1u) ? 0xffff0000u : 0u);
         u4_and(r.v[u], m);
       }
     } else {
@@ -269,10 +307,8 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
       for (int u = 0; u < 4; ++u) {
         uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ti = base_tok + 4 * u + i;
-          if (ti >= lo && ti <= p) m |= 0xffu << (8 * i);
-        }
+        for (int i = 0; i < 4; ++i)
+          if ((mask >> (4 * u + i)) & 1u) m |= 0xffu << (8 * i);
         u4_and(r.v[u], m);
       }
     }
@@ -311,19 +347,20 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
 
   int row = s;
   if (a.q_indptr) {
-    row = a.q_indptr[s];
-    if (a.q_indptr[s + 1] - row != 1) return;   // rows of prompts go elsewhere
+    row = ((CI32P)a.q_indptr)[s];
+    if (((CI32P)a.q_indptr)[s + 1] - row != 1) return;   // rows of prompts go elsewhere
   }
-  const int L = a.seq_lens[s];
+  const int L = ((CI32P)a.seq_lens)[s];
   const int p = L - 1;
-  const int lo = max(0, p - a.window + 1);
-  const int pg0 = lo >> 4;
-  const int npg = (p >> 4) - pg0 + 1;
-  const int nsplit = local_nsplit(npg);
+  const LocalWindow win = local_window(p, a.window);
+  const int nsplit = local_nsplit(win.nv);
   if (split >= nsplit) return;
-  const int my0 = pg0 + split_lo(npg, nsplit, split);
-  const int my1 = pg0 + split_lo(npg, nsplit, split + 1);
-  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
+  const int v0 = split_lo(win.nv, nsplit, split);
+  const int v1 = split_lo(win.nv, nsplit, split + 1);
+  // the virtual page holding position p, where a decode row's new token goes
+  const int vt = win.wrap ? 0 : win.nv - 1;
+  const bool token_here = vt >= v0 && vt < v1;
+  const bool append_here = a.v_new != nullptr && token_here;
 
   // q of the group, this lane's quarter of the dims, as bf16 pairs
   const int c = lane & 3;
@@ -348,55 +385,67 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     for (int j = 0; j < 4; ++j) acc[h][j] = 0.f;
   }
 
-  // This wave's pages are my0 + w + 4k, k < nw.  The wave holding the
-  // split's last page (where a decode row's new token sits) takes that page
-  // first and the rest in order; every other wave goes in order.  The order
-  // is the same whether or not the call appends, so results are too.
-  // Physical ids, 64 at a time, sit one per lane and come back by readlane.
-  const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride;
-  const int nw = (my1 - my0 - w + kLocalWaves - 1) / kLocalWaves;
-  const int w_last = (my1 - 1 - my0) % kLocalWaves;
-  const bool last_first = (w == w_last);
-  const int first_k = last_first ? nw - 1 : 0;
-  const int rest0 = last_first ? 0 : 1;          // k of the 2nd page in order
-  uint8_t* head_base = const_cast<uint8_t*>(a.pool) + (int64_t)g * a.head_bytes + lane * 16;
-  int ptv = 0;
-  auto refill = [&](int k0) __attribute__((always_inline)) {
-    const int idx = my0 + w + kLocalWaves * (k0 + lane);
-    ptv = idx < my1 ? pt[idx] : 0;
+  // This wave's pages are virtual pages v0 + w + 4k, k < nw.  The wave
+  // holding the token's page takes it first and the rest in order; every
+  // other wave goes in order.  The order is the same whether or not the call
+  // appends, so results are too.  Page ids come from scalar loads (the page
+  // table is read-only during the call), issued a page ahead of their use.
+  const int nw = (v1 - v0 - w + kLocalWaves - 1) / kLocalWaves;
+  const bool tok_wave = token_here && w == (vt - v0) % kLocalWaves;
+  const int k_tok = tok_wave ? (vt - v0) / kLocalWaves : 0;
+  auto k_of = [&](int i) __attribute__((always_inline)) {
+    return !tok_wave ? i : i == 0 ? k_tok : (i <= k_tok ? i - 1 : i);
   };
-  auto page_at = [&](int k) __attribute__((always_inline)) {
-    return head_base + (int64_t)(int)readlane_u32((uint32_t)ptv, k & 63) * a.page_bytes;
+  const CI32P pt = (CI32P)(a.page_table + (int64_t)s * a.pt_stride);
+  const uint8_t* head_base = a.pool + (int64_t)g * a.head_bytes;
+  const int mlo = win.lo & 15, mhi = p & 15;
+  auto vpage = [&](int k) __attribute__((always_inline)) {
+    const int v = v0 + w + kLocalWaves * k;
+    const bool merged = win.wrap && v == 0;
+    const int id0 = pt[win.pg0 + v];
+    const int id1 = merged ? pt[win.pgl] : id0;
+    VPage d;
+    d.r0 = head_base + (int64_t)id0 * a.page_bytes;
+    d.r1 = head_base + (int64_t)id1 * a.page_bytes;
+    d.b = merged ? win.b : 0;
+    uint32_t m = 0xffffu;
+    if (merged) {
+      m = (0xffffu << mlo) | ((2u << mhi) - 1u);
+    } else if (!win.wrap) {
+      if (v == 0) m &= 0xffffu << mlo;
+      if (v == win.nv - 1) m &= (2u << mhi) - 1u;
+    }
+    d.mask = m & 0xffffu;
+    return d;
   };
-  auto k_of = [&](int i) __attribute__((always_inline)) { return i == 0 ? first_k : rest0 + i - 1; };
 
   __shared__ uint32_t sm_tok[kLocalWaves][128];   // a patching wave's rotated token K
   PageRegs<FP8> A, B;
+  VPage dA{}, dB{};
   if (nw > 0) {
-    const bool patch = append_here && last_first;
+    const bool patch = append_here && tok_wave;
     NewTokenLoads tok{};
     if (patch) tok = load_new_token(a, row, g, p, lane);
-    const int phys_first = uniform_i32(pt[my0 + w + kLocalWaves * first_k]);
-    uint8_t* first_ptr = head_base + (int64_t)phys_first * a.page_bytes;
-    load_page<FP8>(A, first_ptr);
-    refill(0);
-    if (patch)
-      put_new_token<FP8>(A, first_ptr - lane * 16, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
+    dA = vpage(k_of(0));
+    load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
+    if (nw > 1) dB = vpage(k_of(1));
+    if (patch) {
+      uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)pt[win.pgl] * a.page_bytes;
+      put_new_token<FP8>(A, rec, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
+    }
   }
   for (int i = 0; i < nw; i += 2) {
-    if (i + 1 < nw) {
-      const int k1 = k_of(i + 1);
-      if ((k1 & 63) == 0 && k1 > 0) refill(k1);
-      load_page<FP8>(B, page_at(k1));
-    }
-    process_page<G, FP8>(A, qr, my0 + w + kLocalWaves * k_of(i), lo, p, a.scale_log2, lane, m_run, l_run, acc);
+    if (i + 1 < nw) load_vpage<FP8>(B, dB.r0, dB.r1, dB.b, lane);
+    const VPage dA2 = i + 2 < nw ? vpage(k_of(i + 2)) : dA;
+    process_page<G, FP8>(A, qr, dA.mask, dA.b, a.scale_log2, lane, m_run, l_run, acc);
     if (i + 1 >= nw) break;
     if (i + 2 < nw) {
-      const int k2 = k_of(i + 2);
-      if ((k2 & 63) == 0 && k2 > 0) refill(k2);
-      load_page<FP8>(A, page_at(k2));
+      dA = dA2;
+      load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
     }
-    process_page<G, FP8>(B, qr, my0 + w + kLocalWaves * k_of(i + 1), lo, p, a.scale_log2, lane, m_run, l_run, acc);
+    const VPage dB2 = i + 3 < nw ? vpage(k_of(i + 3)) : dB;
+    process_page<G, FP8>(B, qr, dB.mask, dB.b, a.scale_log2, lane, m_run, l_run, acc);
+    dB = dB2;
   }
 
   // ---- merge the four waves in LDS, in wave order
@@ -511,7 +560,7 @@ __global__ __launch_bounds__(512) void split_reduce_kernel(ReduceArgs a) {
   const int L = a.seq_lens[s];
   int nsplit;
   if (a.window > 0) {
-    nsplit = local_nsplit(local_range_pages(L - 1, a.window));
+    nsplit = local_nsplit(local_window(L - 1, a.window).nv);
   } else {
     nsplit = global_nsplit(cdiv_i(L, kPage));
   }

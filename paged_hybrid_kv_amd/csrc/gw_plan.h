@@ -45,7 +45,36 @@ __host__ __device__ inline int local_range_pages(int p, int window) {
   return p / 16 - lo / 16 + 1;
 }
 
-// Upper bound on pages of any local decode range for sequences <= max_len.
+// The local range [lo, p] of a decode row at position p, walked as
+// "virtual pages".  The range touches pages pg0 = lo/16 .. pgl = p/16; when
+// the first page's slots in use [lo%16, 15] and the last page's [0, p%16]
+// are disjoint (a full window that does not start on a page boundary), the
+// two are walked as one page, slot t taken from the first page when
+// t >= lo%16 and from the last page otherwise.  A full 1024-token window is
+// then 64 pages of work rather than 65 (the same bytes: the two edge pages
+// together hold exactly 16 slots of the window).  Virtual page 0 is that
+// merged page (wrap) or page pg0; virtual page v >= 1 is page pg0 + v.
+struct LocalWindow {
+  int lo, pg0, pgl;
+  int nv;       // virtual pages
+  int b;        // wrap: first slot read from page pg0 (the rest from pgl); else 0
+  bool wrap;
+};
+
+__host__ __device__ inline LocalWindow local_window(int p, int window) {
+  LocalWindow r;
+  r.lo = p - window + 1 < 0 ? 0 : p - window + 1;
+  r.pg0 = r.lo / 16;
+  r.pgl = p / 16;
+  const int npg = r.pgl - r.pg0 + 1;
+  r.wrap = npg >= 2 && (p % 16) < (r.lo % 16);
+  r.nv = r.wrap ? npg - 1 : npg;
+  r.b = r.wrap ? r.lo % 16 : 0;
+  return r;
+}
+
+// Upper bound on pages of any local decode range for sequences <= max_len
+// (it also bounds the virtual page count).
 inline int local_max_range_pages(int max_len, int window) {
   int w = window < max_len ? window : max_len;
   // a w-token range starting mid-page spans at most cdiv(w - 1, 16) + 1 pages
