@@ -89,12 +89,15 @@ int max_splits_for(int family, int max_seq_len, int window) {
   return gw::global_nsplit(gw::cdiv_i(max_seq_len, 16));
 }
 
-// Workspace: [split counters | partial accumulators | partial (max, sum)].
-// The counters must be zero before the first call (the caller zero-fills the
-// workspace once); every call that completes leaves them zero again.
+// Workspace: [split counters | call epochs (local) | partial accumulators |
+// partial (max, sum)].  The counters must be zero before the first call (the
+// caller zero-fills the workspace once); every call that completes leaves
+// them zero again.  The local family's partials are (value, tag) pairs of 8
+// bytes, tagged with the call's epoch (gw_local.hip); the global family's
+// are plain fp32, reduced by a kernel of their own.
 struct WsPlan {
   int max_splits;
-  size_t counter_bytes, acc_bytes, ml_bytes, total;
+  size_t counter_bytes, epoch_bytes, acc_bytes, ml_bytes, total;
 };
 
 WsPlan plan_workspace(int family, int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
@@ -102,11 +105,14 @@ WsPlan plan_workspace(int family, int num_seqs, int num_kv_heads, int num_q_head
   WsPlan w{};
   w.max_splits = max_splits_for(family, max_seq_len, window);
   if (w.max_splits <= 1 || num_seqs <= 0) return w;
+  const bool local = family == GW_FAMILY_LOCAL;
   const size_t units = (size_t)num_seqs * num_q_heads * w.max_splits;
+  const size_t elem = local ? sizeof(uint64_t) : sizeof(float);
   w.counter_bytes = align_up((size_t)num_seqs * num_kv_heads * sizeof(int));
-  w.acc_bytes = align_up(units * head_dim * sizeof(float));
-  w.ml_bytes = align_up(units * 2 * sizeof(float));
-  w.total = w.counter_bytes + w.acc_bytes + w.ml_bytes;
+  w.epoch_bytes = local ? align_up((size_t)num_seqs * num_kv_heads * sizeof(uint32_t)) : 0;
+  w.acc_bytes = align_up(units * head_dim * elem);
+  w.ml_bytes = align_up(units * 2 * elem);
+  w.total = w.counter_bytes + w.epoch_bytes + w.acc_bytes + w.ml_bytes;
   return w;
 }
 
@@ -281,8 +287,9 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   a.out = out;
   char* ws = static_cast<char*>(workspace);
   a.counters = w.total ? reinterpret_cast<int*>(ws) : nullptr;
-  a.part_acc = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes) : nullptr;
-  a.part_ml = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes + w.acc_bytes) : nullptr;
+  a.epochs = w.total ? reinterpret_cast<uint32_t*>(ws + w.counter_bytes) : nullptr;
+  a.part_acc = w.total ? reinterpret_cast<uint64_t*>(ws + w.counter_bytes + w.epoch_bytes) : nullptr;
+  a.part_ml = w.total ? reinterpret_cast<uint64_t*>(ws + w.counter_bytes + w.epoch_bytes + w.acc_bytes) : nullptr;
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
   a.k_new = static_cast<const uint16_t*>(k_new);

@@ -173,15 +173,18 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   // ---- work item of this workgroup: the call's (sequence, split) items are
   // numbered sequence by sequence, and workgroup b takes item b, so the
   // active workgroups are 0 .. items-1 and spread evenly over the XCDs
-  int s = -1, split = 0, nsplit = 1;
+  int s = -1, split = 0, nsplit = 1, L = 1, row = 0;
   {
     const int b = blockIdx.x;
     int base = 0;
     for (int c = 0; c < a.num_seqs; c += 64) {
       const int sl = c + lane;
-      int cnt = 0;
-      if (sl < a.num_seqs && (!a.q_indptr || a.q_indptr[sl + 1] - a.q_indptr[sl] == 1))
-        cnt = global_nsplit(((a.seq_lens[sl] - 1) >> 4) + 1);
+      int cnt = 0, len = 1, r0 = sl;
+      if (sl < a.num_seqs) {
+        len = a.seq_lens[sl];
+        if (a.q_indptr) r0 = a.q_indptr[sl];
+        if (!a.q_indptr || a.q_indptr[sl + 1] - r0 == 1) cnt = global_nsplit(((len - 1) >> 4) + 1);
+      }
       int incl = cnt;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -194,6 +197,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
         const int ls = __builtin_ctzll(hit);
         s = c + ls;
         nsplit = __builtin_amdgcn_readlane(cnt, ls);
+        L = __builtin_amdgcn_readlane(len, ls);
+        row = __builtin_amdgcn_readlane(r0, ls);
         split = b - (base + __builtin_amdgcn_readlane(incl, ls) - nsplit);
         break;
       }
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   s = uniform_i32(s);
   split = uniform_i32(split);
   nsplit = uniform_i32(nsplit);
-  const int row = a.q_indptr ? a.q_indptr[s] : s;
-  const int L = a.seq_lens[s];
+  L = uniform_i32(L);
+  row = uniform_i32(row);
   const int p = L - 1;
   const int n_pages = (p >> 4) + 1;
   const int pg0 = split_lo(n_pages, nsplit, split);
@@ -213,9 +218,19 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   const int n_pairs = (n + 1) >> 1;
   const int head = 16 * hb + l16;
 
-  // ---- physical page ids of the split, one per lane and register (a split
-  // has at most 256 pages); read back with readlane, so the page loop issues
-  // no vector memory operation the compiler would wait on
+  // ---- everything the page loop needs besides the pages goes out first, in
+  // one round trip: the Q^T operand (head 16hb + l16, dims 32ks + 8g .. +7),
+  // the split's physical page ids (one per lane and register, read back with
+  // readlane; a split has at most 256 pages) and, on the wave that appends a
+  // decode row's own token, that token's inputs.  They are waited for before
+  // the first page transfer is issued: the compiler does not see the
+  // transfers, and a wait of its own placed later would hold for them too.
+  bf16x8 qf[16];
+  {
+    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + head) * kGD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+  }
   const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride + pg0;
   auto pt_at = [&](int idx) __attribute__((always_inline)) { return idx < n ? pt[idx] : 0; };
   const int ptv0 = pt_at(lane);
@@ -229,11 +244,26 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
          : i < 192 ? __builtin_amdgcn_readlane(ptv2, l)
                    : __builtin_amdgcn_readlane(ptv3, l);
   };
+  // a decode row's own token, when the call carries it: the workgroup of the
+  // row's last split rotates it and stores it into the pool (as
+  // gw_kv_append does) before any transfer, and into its LDS copy of that
+  // page once the page has landed
+  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
+  GlobalRecordLane rec{};
+  if (append_here && wv == 0) rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
+  if (append_here && wv == 0)
+    put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
+                                  p & 15, lane);
 
   // ---- transfers: group q moves page 2j + q of pair j, wave w of the group
   // the units [kPerWave w, kPerWave (w + 1)) of the page (1 KiB each), so
   // the LDS copy has the pool's layout.  An odd split's last pair repeats
-  // its last page as the second one; that copy is never computed on.
+  // its last page as the second one; that copy is never computed on.  The
+  // loop's waits count transfers only; the appending wave's pool stores are
+  // older than all of them, so they are covered too.
   const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) +
                              (uint32_t)(grp * PG::kBytes + 1024 * kPerWave * w);
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
@@ -246,33 +276,6 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
-
-  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7.  The empty asm
-  // consumes the registers here, so the compiler waits for these loads once,
-  // before the page loop, instead of at every use inside it (it does not see
-  // the page transfers, and its wait would hold for them too).
-  bf16x8 qf[16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + head) * kGD + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-
-  // ---- a decode row's own token, when the call carries it: the workgroup
-  // of the row's last split rotates and stores it (as gw_kv_append does)
-  // and puts it into its LDS copy of that page once the page has landed.
-  // Its loads and stores are waited for here, before the page loop, so the
-  // loop's transfer counts stay exact.
-  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
-  GlobalRecordLane rec{};
-  if (append_here && wv == 0) {
-    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
-    put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
-                                  p & 15, lane);
-    wait_vmcnt<0>();
-  }
 
   f32x4 acc[kBlocks];
 #pragma unroll

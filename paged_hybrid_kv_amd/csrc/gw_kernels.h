@@ -20,9 +20,11 @@ struct LocalAttnArgs {
   int32_t window;
   float scale_log2;           // softmax scale * log2(e)
   float* out;                 // fp32 [rows][Hq][256]
-  float* part_acc;            // fp32 [S][Hq][max_splits][256]
-  float* part_ml;             // fp32 [S][Hq][max_splits][2]: (max, sum) in base 2
+  // split partials as (fp32 value | tag << 32) pairs, tag = the call's epoch + 1
+  uint64_t* part_acc;         // [S][Hq][max_splits][256]
+  uint64_t* part_ml;          // [S][Hq][max_splits][2]: (max, sum) in base 2
   int* counters;              // [S][Hkv] splits finished; zero between calls
+  uint32_t* epochs;           // [S][Hkv] calls with split partials so far
   int32_t max_splits;
   int32_t num_seqs;
   const uint16_t* k_new;      // bf16 [rows][Hkv][256] raw K of each row's own token, or null

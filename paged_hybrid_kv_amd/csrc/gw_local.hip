@@ -33,6 +33,8 @@
 // e4m3 pages hold the same roles at one byte per element; two codes convert
 // to a bf16 pair exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1).
 
+#include <type_traits>
+
 #include "gw_device.h"
 #include "gw_kernels.h"
 #include "gw_plan.h"
@@ -42,6 +44,8 @@ namespace {
 
 constexpr int kLocalD = 256;
 constexpr int kLocalWaves = 4;
+// Re-reads of one partial before the reducing workgroup gives up on it.
+constexpr int kLocalMaxReReads = 1 << 20;
 
 template <bool FP8>
 struct LocalLayout {
@@ -339,9 +343,85 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
   }
 }
 
+// The reducing workgroup's merge of q heads h0 .. h0 + GH - 1, output dim d:
+// every split's (max, sum, acc) is loaded at once (pairs whose tag is not
+// yet this call's are read again until it is), then M = max_i m_i,
+// l = sum_i l_i 2^(m_i - M), out = sum_i acc_i 2^(m_i - M) / l, both sums
+// in split order.  NS bounds nsplit.  Returns false, after writing NaN, if a
+// pair never arrived.
+template <int GH, int NS>
+__device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int h0, int row, int d, int nsplit,
+                                             uint64_t tag) {
+  uint64_t mi[GH][NS], li[GH][NS], ai[GH][NS];
+  // first read: through this XCD's L2 (workgroup scope), where the splits
+  // placed on this XCD left their partials; a pair found stale there is
+  // read again at device scope
+  auto fetch = [&](int h, int i, auto scope) __attribute__((always_inline)) {
+    constexpr int kScope = decltype(scope)::value;
+    const int64_t ic = ((int64_t)s * a.num_q_heads + h0 + h) * a.max_splits + i;
+    mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, kScope);
+    li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, kScope);
+    ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, kScope);
+  };
+  using WgScope = std::integral_constant<int, __HIP_MEMORY_SCOPE_WORKGROUP>;
+  using DevScope = std::integral_constant<int, __HIP_MEMORY_SCOPE_AGENT>;
+  auto landed = [&](int h, int i) __attribute__((always_inline)) {
+    return i >= nsplit || (((mi[h][i] >> 32) == (tag >> 32)) & ((li[h][i] >> 32) == (tag >> 32)) &
+                           ((ai[h][i] >> 32) == (tag >> 32)));
+  };
+#pragma unroll
+  for (int h = 0; h < GH; ++h)
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      mi[h][i] = li[h][i] = ai[h][i] = 0;
+      if (i < nsplit) fetch(h, i, WgScope{});
+    }
+  bool ok = true;
+  for (int spin = 0;; ++spin) {
+    bool all = true;
+#pragma unroll
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) all &= landed(h, i);
+    if (all) break;
+    if (spin == kLocalMaxReReads) { ok = false; break; }
+#pragma unroll
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        if (!landed(h, i)) fetch(h, i, DevScope{});
+  }
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (i < nsplit) Mx = fmaxf(Mx, bits_to_f32((uint32_t)mi[h][i]));
+    float ls = 0.f, ov = 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i < nsplit) {
+        const float sw = __builtin_amdgcn_exp2f(bits_to_f32((uint32_t)mi[h][i]) - Mx);
+        ls += bits_to_f32((uint32_t)li[h][i]) * sw;
+        ov += bits_to_f32((uint32_t)ai[h][i]) * sw;
+      }
+    }
+    a.out[((int64_t)row * a.num_q_heads + h0 + h) * kLocalD + d] = ok ? ov / ls : __builtin_nanf("");
+  }
+  return ok;
+}
+
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(LocalAttnArgs a) {
-  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // Workgroup -> (sequence, KV head, split): workgroups go to the 8 XCDs in
+  // turn (id % 8), so the splits of one (sequence, KV head) pair are given
+  // ids 8 apart and share an XCD -- and its L2, where the reducing
+  // workgroup then finds the other splits' partials.  Results do not depend
+  // on this placement (the partials' tags decide what is read from where).
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int pair = (j / a.max_splits) * 8 + xcd, split = j % a.max_splits;
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int s = pair / a.num_kv_heads, g = pair % a.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
 
@@ -361,6 +441,12 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   const int vt = win.wrap ? 0 : win.nv - 1;
   const bool token_here = vt >= v0 && vt < v1;
   const bool append_here = a.v_new != nullptr && token_here;
+  // this (sequence, KV head)'s call count, the tag of this call's partials;
+  // read now, first used after the page loop (the empty asm there keeps the
+  // compiler from waiting for it before the pages are requested)
+  uint32_t epoch = nsplit > 1 ? __hip_atomic_load(a.epochs + (int64_t)s * a.num_kv_heads + g, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0u;
 
   // q of the group, this lane's quarter of the dims, as bf16 pairs
   const int c = lane & 3;
@@ -448,6 +534,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     dB = dB2;
   }
 
+  asm volatile("" : "+v"(epoch));
   // ---- merge the four waves in LDS, in wave order
   __shared__ float sm_acc[kLocalWaves][G][kLocalD];
   __shared__ float sm_m[kLocalWaves][G], sm_l[kLocalWaves][G];
@@ -491,56 +578,50 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     return;
   }
 
-  // ---- publish this split's partial; the last split of the pair to finish
-  // reduces all of them in split order.  The partials are written and read
-  // with device-scope accesses (written through to memory, read past the
-  // per-XCD L2), and the stores have completed before the counter moves, so
-  // no whole-cache write-back or invalidate is needed.
+  // ---- publish this split's partial; the last workgroup of the (sequence,
+  // KV head) to arrive reduces all of them in split order.  Every value goes
+  // out as one 64-bit (value, tag) pair, tag = this call's epoch, with
+  // device-scope atomic stores, and the arrival counter moves right after
+  // the stores are issued, without waiting for them: the last workgroup
+  // reads each pair with a device-scope atomic load and reads again, until
+  // its tag is this call's, the few pairs whose stores are still on their
+  // way.  Every pair it waits for was stored before its writer's arrival,
+  // so each wait ends; a bound on the re-reads turns a broken invariant
+  // into NaN output instead of a hang.
+  const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int64_t pi = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits + split;
-    __hip_atomic_store(a.part_acc + pi * kLocalD + d, o[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.part_acc + pi * kLocalD + d, tag | f32_to_bits(o[h]), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      __hip_atomic_store(a.part_ml + pi * 2 + 0, M[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.part_ml + pi * 2 + 1, lsum[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + pi * 2 + 0, tag | f32_to_bits(M[h]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + pi * 2 + 1, tag | f32_to_bits(lsum[h]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  wait_stores_done();
-  __syncthreads();
+  __syncthreads();   // every store of the workgroup is issued
   int* counter = a.counters + (int64_t)s * a.num_kv_heads + g;
   if (tid == 0)
     sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   __syncthreads();
   if (!sm_last) return;
-  // Every split's (max, sum, acc) is loaded at once -- indices past the last
-  // split repeat it and are not used -- so the merge costs one round trip;
-  // the sums then run in split order.
+  // The heads of the group are merged together, so their loads share one
+  // round trip; a row's range of up to 68 pages has at most 4 splits.
+  bool ok;
+  if (nsplit <= 4) {
+    ok = merge_splits<G, 4>(a, s, g * G, row, d, nsplit, tag);
+  } else {
+    ok = true;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int64_t base = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits;
-    float mi[kLocalMaxSplits], li[kLocalMaxSplits], ai[kLocalMaxSplits];
-#pragma unroll
-    for (int i = 0; i < kLocalMaxSplits; ++i) {
-      const int64_t ic = base + min(i, nsplit - 1);
-      mi[i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      li[i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ai[i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kLocalMaxSplits; ++i) Mx = fmaxf(Mx, mi[i]);
-    float ls = 0.f, ov = 0.f;
-#pragma unroll
-    for (int i = 0; i < kLocalMaxSplits; ++i) {
-      if (i < nsplit) {
-        const float sw = __builtin_amdgcn_exp2f(mi[i] - Mx);
-        ls += li[i] * sw;
-        ov += ai[i] * sw;
-      }
-    }
-    a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = ov / ls;
+    for (int h = 0; h < G; ++h) ok &= merge_splits<1, kLocalMaxSplits>(a, s, g * G + h, row, d, nsplit, tag);
   }
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+  (void)ok;
+  if (tid == 0) {   // ready for the next call
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.epochs + (int64_t)s * a.num_kv_heads + g, epoch + 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
@@ -611,7 +692,8 @@ __global__ __launch_bounds__(512) void split_reduce_kernel(ReduceArgs a) {
 }  // namespace
 
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
-  dim3 grid(a.max_splits, a.num_kv_heads, a.num_seqs), block(256);
+  const int pairs = a.num_seqs * a.num_kv_heads;
+  dim3 grid(((pairs + 7) / 8) * 8 * a.max_splits), block(256);
 #define GW_LOCAL_CASE(G_, F_) \
   if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, block, 0, stream, a); return hipGetLastError(); }
   GW_LOCAL_CASE(1, false) GW_LOCAL_CASE(2, false) GW_LOCAL_CASE(4, false)

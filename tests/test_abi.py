@@ -174,9 +174,10 @@ def test_empty_batches_are_noops():
 
 
 def test_workspace_plan():
-    # one window of 1024 tokens spans at most 65 pages -> 4 splits of 16-17 pages
+    # one window of 1024 tokens is 64 pages of work -> 4 splits of 16 pages;
+    # local partials are 8-byte (value, tag) pairs
     ws = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 16, 16, 16, 256, 8192, 1024, 1)
-    assert ws >= 16 * 16 * 4 * 258 * 4
+    assert ws >= 16 * 16 * 4 * 258 * 8
     assert gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 1, 1, 2, 256, 64, 32, 1) == 0
     wg = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_GLOBAL_COMPRESSED, 8, 8, 32, 512, 131072, 0, 1)
     assert wg >= 8 * 32 * 64 * 514 * 4

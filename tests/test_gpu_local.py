@@ -187,6 +187,11 @@ def test_repeat_determinism():
     o2 = RT.attend(dc).cpu().numpy()
     o3 = RT.attend(dc).cpu().numpy()
     assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
+    # one workspace over many calls: the split counters and the partials'
+    # call tags carry over from call to call
+    ws = RT.Workspace()
+    for _ in range(6):
+        assert np.array_equal(o1, RT.attend(dc, ws=ws).cpu().numpy())
 
 
 # ------------------------------------------------------------- append ------
