@@ -403,7 +403,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   e = gw::launch_global_decode(a, compressed, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (w.max_splits > 1) {
-    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, 512, w.max_splits, 0};
+    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, w.max_splits};
     e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }

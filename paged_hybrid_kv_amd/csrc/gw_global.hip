@@ -428,7 +428,71 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
 }
 
+// Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
+// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  One
+// workgroup per (sequence, q head), 128 threads: thread t owns output dims
+// 4t .. 4t+3.  Every load of a chunk of 32 splits (each thread's acc
+// quarter-rows, and (m, l) of split t by thread t) goes out at once, so a
+// chunk costs one round trip; M and the weights are shared through LDS.
+constexpr int kReduceChunk = 32;
+
+__global__ __launch_bounds__(128) void global_split_reduce_kernel(ReduceArgs a) {
+  __shared__ float sm_m[kReduceChunk], sm_l[kReduceChunk];
+  const int s = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  int row = s;
+  if (a.q_indptr) {
+    row = a.q_indptr[s];
+    if (a.q_indptr[s + 1] - row != 1) return;
+  }
+  const int nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
+  if (nsplit <= 1) return;
+  const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_splits;
+  const float* pa = a.part_acc + base * kGD + 4 * t;
+  const float* ml = a.part_ml + base * 2;
+  float M = -INFINITY, lsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk) {
+    const int nc = min(kReduceChunk, nsplit - c0);
+    f32x4 v[kReduceChunk];
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i)
+      v[i] = i < nc ? *reinterpret_cast<const f32x4*>(pa + (int64_t)(c0 + i) * kGD) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < nc) {
+      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * (c0 + t));
+      sm_m[t] = x.x;
+      sm_l[t] = x.y;
+    }
+    __syncthreads();
+    // the running max over the splits so far; earlier chunks rescale once
+    float mc = -INFINITY;
+    for (int i = 0; i < nc; ++i) mc = fmaxf(mc, sm_m[i]);
+    const float mnew = fmaxf(M, mc);
+    if (mnew > M) {
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      o *= r;
+      lsum *= r;
+      M = mnew;
+    }
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i) {
+      if (i < nc) {
+        const float w = __builtin_amdgcn_exp2f(sm_m[i] - M);
+        lsum += sm_l[i] * w;
+        o += v[i] * w;
+      }
+    }
+    __syncthreads();   // sm_m / sm_l are rewritten by the next chunk
+  }
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + h) * kGD + 4 * t) = o / lsum;
+}
+
 }  // namespace
+
+hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
+  dim3 grid(num_seqs, a.num_q_heads), block(128);
+  hipLaunchKernelGGL(global_split_reduce_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream) {
   dim3 grid(a.max_splits * a.num_seqs), block(512);

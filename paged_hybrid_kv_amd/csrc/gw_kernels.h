@@ -54,16 +54,15 @@ struct GlobalAttnArgs {
   const float* rope_sin;
 };
 
+// Global family's cross-split reduce (gw_global.hip).
 struct ReduceArgs {
   const int32_t* q_indptr;
   const int32_t* seq_lens;
-  const float* part_acc;
-  const float* part_ml;
-  float* out;
+  const float* part_acc;      // fp32 [S][Hq][max_splits][512]
+  const float* part_ml;       // fp32 [S][Hq][max_splits][2]
+  float* out;                 // fp32 [rows][Hq][512]
   int32_t num_q_heads;
-  int32_t head_dim;
   int32_t max_splits;
-  int32_t window;             // local family; <= 0 for the global family
 };
 
 struct AppendArgs {

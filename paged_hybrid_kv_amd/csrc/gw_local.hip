@@ -1,7 +1,6 @@
 // Local-family paged decode attention (sliding window, head dim 256, grouped
 // query heads), with the decode rows' own K/V append and the cross-split
-// reduce fused in, plus the standalone cross-split reduce used by the global
-// family.
+// reduce fused in.
 //
 // What is computed (pegainfer "Gemma 4" page, intro and Architecture notes;
 // pegainfer PR #1012, Description, for the e4m3 pool): for each decode row of
@@ -32,8 +31,6 @@
 // values, so the normalisation matches the weights used.
 // e4m3 pages hold the same roles at one byte per element; two codes convert
 // to a bf16 pair exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1).
-
-#include <type_traits>
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -344,8 +341,8 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
 }
 
 // The reducing workgroup's merge of q heads h0 .. h0 + GH - 1, output dim d:
-// every split's (max, sum, acc) is loaded at once (pairs whose tag is not
-// yet this call's are read again until it is), then M = max_i m_i,
+// every split's (max, sum, acc) is loaded at once (all of them again while
+// any pair's tag is not yet this call's), then M = max_i m_i,
 // l = sum_i l_i 2^(m_i - M), out = sum_i acc_i 2^(m_i - M) / l, both sums
 // in split order.  NS bounds nsplit.  Returns false, after writing NaN, if a
 // pair never arrived.
@@ -353,43 +350,30 @@ template <int GH, int NS>
 __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int h0, int row, int d, int nsplit,
                                              uint64_t tag) {
   uint64_t mi[GH][NS], li[GH][NS], ai[GH][NS];
-  // first read: through this XCD's L2 (workgroup scope), where the splits
-  // placed on this XCD left their partials; a pair found stale there is
-  // read again at device scope
-  auto fetch = [&](int h, int i, auto scope) __attribute__((always_inline)) {
-    constexpr int kScope = decltype(scope)::value;
-    const int64_t ic = ((int64_t)s * a.num_q_heads + h0 + h) * a.max_splits + i;
-    mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, kScope);
-    li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, kScope);
-    ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, kScope);
-  };
-  using WgScope = std::integral_constant<int, __HIP_MEMORY_SCOPE_WORKGROUP>;
-  using DevScope = std::integral_constant<int, __HIP_MEMORY_SCOPE_AGENT>;
-  auto landed = [&](int h, int i) __attribute__((always_inline)) {
-    return i >= nsplit || (((mi[h][i] >> 32) == (tag >> 32)) & ((li[h][i] >> 32) == (tag >> 32)) &
-                           ((ai[h][i] >> 32) == (tag >> 32)));
-  };
-#pragma unroll
-  for (int h = 0; h < GH; ++h)
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      mi[h][i] = li[h][i] = ai[h][i] = 0;
-      if (i < nsplit) fetch(h, i, WgScope{});
-    }
+  // one copy of the load code (the kernel's tail runs from a cold
+  // instruction cache): read everything, and again while any pair is stale
   bool ok = true;
   for (int spin = 0;; ++spin) {
     bool all = true;
 #pragma unroll
     for (int h = 0; h < GH; ++h)
 #pragma unroll
-      for (int i = 0; i < NS; ++i) all &= landed(h, i);
-    if (all) break;
-    if (spin == kLocalMaxReReads) { ok = false; break; }
+      for (int i = 0; i < NS; ++i) {
+        mi[h][i] = li[h][i] = ai[h][i] = tag;
+        if (i < nsplit) {
+          const int64_t ic = ((int64_t)s * a.num_q_heads + h0 + h) * a.max_splits + i;
+          mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
 #pragma unroll
     for (int h = 0; h < GH; ++h)
 #pragma unroll
       for (int i = 0; i < NS; ++i)
-        if (!landed(h, i)) fetch(h, i, DevScope{});
+        all &= ((mi[h][i] >> 32) == (tag >> 32)) & ((li[h][i] >> 32) == (tag >> 32)) & ((ai[h][i] >> 32) == (tag >> 32));
+    if (all) break;
+    if (spin == kLocalMaxReReads) { ok = false; break; }
   }
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
@@ -413,15 +397,7 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
 
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(LocalAttnArgs a) {
-  // Workgroup -> (sequence, KV head, split): workgroups go to the 8 XCDs in
-  // turn (id % 8), so the splits of one (sequence, KV head) pair are given
-  // ids 8 apart and share an XCD -- and its L2, where the reducing
-  // workgroup then finds the other splits' partials.  Results do not depend
-  // on this placement (the partials' tags decide what is read from where).
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int pair = (j / a.max_splits) * 8 + xcd, split = j % a.max_splits;
-  if (pair >= a.num_seqs * a.num_kv_heads) return;
-  const int s = pair / a.num_kv_heads, g = pair % a.num_kv_heads;
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
 
@@ -624,88 +600,16 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   }
 }
 
-// Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
-// out = sum_i acc_i 2^(m_i - M) / l.  One workgroup per (sequence, q head):
-// thread t takes four output dims (t % (D/4)) and the splits i = t / (D/4)
-// (mod 4), in split order; the four groups' sums are added in group order
-// 0, 1, 2, 3 through LDS, so the result is fixed for a given split count.
-__global__ __launch_bounds__(512) void split_reduce_kernel(ReduceArgs a) {
-  __shared__ __attribute__((aligned(16))) float part[3][128][4];
-  __shared__ float lpart[3];
-  const int s = blockIdx.x, h = blockIdx.y;
-  int row = s;
-  if (a.q_indptr) {
-    row = a.q_indptr[s];
-    if (a.q_indptr[s + 1] - row != 1) return;
-  }
-  const int L = a.seq_lens[s];
-  int nsplit;
-  if (a.window > 0) {
-    nsplit = local_nsplit(local_window(L - 1, a.window).nv);
-  } else {
-    nsplit = global_nsplit(cdiv_i(L, kPage));
-  }
-  if (nsplit <= 1) return;
-  const int nd4 = a.head_dim / 4;                 // threads per split group
-  const int grp = threadIdx.x / nd4, d4 = (threadIdx.x % nd4) * 4;
-  const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_splits;
-  const float* ml = a.part_ml + base * 2;
-  float M = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
-  const float* pa = a.part_acc + base * a.head_dim + d4;
-  float lsum = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  if (grp < 4) {
-    int i = grp;
-    for (; i + 12 < nsplit; i += 16) {            // four of this group's splits at a time
-      f32x4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(pa + (int64_t)(i + 4 * k) * a.head_dim);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float sw = __builtin_amdgcn_exp2f(ml[2 * (i + 4 * k)] - M);
-        lsum += ml[2 * (i + 4 * k) + 1] * sw;
-        o += v[k] * sw;
-      }
-    }
-    for (; i < nsplit; i += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(pa + (int64_t)i * a.head_dim);
-      const float sw = __builtin_amdgcn_exp2f(ml[2 * i] - M);
-      lsum += ml[2 * i + 1] * sw;
-      o += v * sw;
-    }
-    if (grp > 0) {
-      *reinterpret_cast<f32x4*>(&part[grp - 1][d4 / 4][0]) = o;
-      if (d4 == 0) lpart[grp - 1] = lsum;
-    }
-  }
-  __syncthreads();
-  if (grp != 0) return;
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    o += *reinterpret_cast<const f32x4*>(&part[k][d4 / 4][0]);
-    lsum += lpart[k];
-  }
-  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + h) * a.head_dim + d4) = o / lsum;
-}
-
 }  // namespace
 
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
-  const int pairs = a.num_seqs * a.num_kv_heads;
-  dim3 grid(((pairs + 7) / 8) * 8 * a.max_splits), block(256);
+  dim3 grid(a.max_splits, a.num_kv_heads, a.num_seqs), block(256);
 #define GW_LOCAL_CASE(G_, F_) \
   if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, block, 0, stream, a); return hipGetLastError(); }
   GW_LOCAL_CASE(1, false) GW_LOCAL_CASE(2, false) GW_LOCAL_CASE(4, false)
   GW_LOCAL_CASE(1, true) GW_LOCAL_CASE(2, true) GW_LOCAL_CASE(4, true)
 #undef GW_LOCAL_CASE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs, a.num_q_heads), block(a.head_dim);
-  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace gw
