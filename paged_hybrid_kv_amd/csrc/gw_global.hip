@@ -219,17 +219,20 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   const int head = 16 * hb + l16;
 
   // ---- everything the page loop needs besides the pages goes out first, in
-  // one round trip: the Q^T operand (head 16hb + l16, dims 32ks + 8g .. +7),
-  // the split's physical page ids (one per lane and register, read back with
-  // readlane; a split has at most 256 pages) and, on the wave that appends a
-  // decode row's own token, that token's inputs.  They are waited for before
-  // the first page transfer is issued: the compiler does not see the
-  // transfers, and a wait of its own placed later would hold for them too.
-  bf16x8 qf[16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + head) * kGD + 8 * g;
+  // one round trip: the row's q (64 bytes per thread: head tid / 16, 16-byte
+  // chunks 4 (tid % 16) .. +3), the split's physical page ids (one per lane
+  // and register, read back with readlane; a split has at most 256 pages)
+  // and, on the wave that appends a decode row's own token, that token's
+  // inputs.  They are waited for before the first page transfer is issued:
+  // the compiler does not see the transfers, and a wait of its own placed
+  // later would hold for them too.
+  const int qh = tid >> 4, qc0 = 4 * (tid & 15);
+  const bool q_mine = qh < a.num_q_heads;
+  u32x4 qraw[4] = {};
+  if (q_mine) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * a.num_q_heads + qh) * kGD) + qc0;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
   }
   const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride + pg0;
   auto pt_at = [&](int idx) __attribute__((always_inline)) { return idx < n ? pt[idx] : 0; };
@@ -252,11 +255,19 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   GlobalRecordLane rec{};
   if (append_here && wv == 0) rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qraw[c]));
   asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
   if (append_here && wv == 0)
     put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
                                   p & 15, lane);
+  // q into LDS, in ring slot NP - 1 (free until the loop's first transfer),
+  // 1 KiB per head with 16-byte chunk c of head h at chunk c ^ (h % 8), so
+  // that the Q^T operand reads below hit distinct banks
+  uint8_t* qs = &ring[NP - 1][0][0];
+  if (q_mine) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(qs + qh * 1024 + (((qc0 + c) ^ (qh & 7)) * 16)) = qraw[c];
+  }
 
   // ---- transfers: group q moves page 2j + q of pair j, wave w of the group
   // the units [kPerWave w, kPerWave (w + 1)) of the page (1 KiB each), so
@@ -276,6 +287,13 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
+
+  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7 (16-byte chunk 4ks + g)
+  lds_barrier();
+  bf16x8 qf[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + (((4 * ks + g) ^ (head & 7)) * 16));
 
   f32x4 acc[kBlocks];
 #pragma unroll
