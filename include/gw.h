@@ -181,7 +181,8 @@ int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const v
  *   out[row][h][:] = sum_j softmax_j(scale * q[row][h] . K[j]) V[j], fp32.
  * Host sizing arguments (upper bounds used to size grids; a device value
  * beyond them is a contract violation): num_rows = q_indptr[num_seqs];
- * max_q_len >= every q_len_s; max_seq_len >= every seq_lens[s].
+ * max_q_len >= every q_len_s; max_seq_len >= every seq_lens[s];
+ * max_seq_len <= 2^24 (16,777,216 tokens).
  *
  *   q   : bf16 [num_rows][num_q_heads][head_dim], already rotated.
  *   out : fp32 [num_rows][num_q_heads][head_dim].

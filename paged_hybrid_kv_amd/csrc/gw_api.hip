@@ -30,6 +30,9 @@ int ok() {
 }
 
 constexpr size_t kAlign = 256;
+// Longest sequence served (tokens): keeps every page count and split bound
+// of the plans well inside 32-bit arithmetic.
+constexpr int kMaxSeqLen = 1 << 24;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool is_local(int f) { return f == GW_FAMILY_LOCAL; }
@@ -125,7 +128,8 @@ int check_attn_common(const char* fn, const void* q, int num_q_heads, const int3
   if (num_rows < 0) return fail(GW_ERR_INVALID_ARG, fn, "num_rows %d", num_rows);
   if (num_q_heads < 1) return fail(GW_ERR_INVALID_ARG, fn, "num_q_heads %d", num_q_heads);
   if (max_q_len < 1) return fail(GW_ERR_INVALID_ARG, fn, "max_q_len %d", max_q_len);
-  if (max_seq_len < 1) return fail(GW_ERR_INVALID_ARG, fn, "max_seq_len %d", max_seq_len);
+  if (max_seq_len < 1 || max_seq_len > kMaxSeqLen)
+    return fail(GW_ERR_INVALID_ARG, fn, "max_seq_len %d (served: 1 .. %d)", max_seq_len, kMaxSeqLen);
   if (max_q_len > max_seq_len)
     return fail(GW_ERR_INVALID_ARG, fn, "max_q_len %d exceeds max_seq_len %d", max_q_len, max_seq_len);
   if (!isfinite(scale)) return fail(GW_ERR_INVALID_ARG, fn, "scale is not finite");

@@ -41,6 +41,8 @@ namespace {
 
 constexpr int kLocalD = 256;
 constexpr int kLocalWaves = 4;
+// Page-table rows up to this many entries are read whole into LDS.
+constexpr int kLocalPtLds = 2048;
 // Re-reads of one partial before the reducing workgroup gives up on it.
 constexpr int kLocalMaxReReads = 1 << 20;
 
@@ -407,6 +409,21 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     if (((CI32P)a.q_indptr)[s + 1] - row != 1) return;   // rows of prompts go elsewhere
   }
   const int L = ((CI32P)a.seq_lens)[s];
+  // The page-table row (when it has at most kLocalPtLds entries) and the
+  // group's q are read in the same round trip as the length -- before it is
+  // known which pages the window covers -- and go to LDS.
+  const bool pt_lds = a.pt_stride <= kLocalPtLds;
+  int ptv[kLocalPtLds / 256] = {};
+  if (pt_lds) {
+    const int32_t* prow = a.page_table + (int64_t)s * a.pt_stride;
+#pragma unroll
+    for (int i = 0; i < kLocalPtLds / 256; ++i)
+      if (tid + 256 * i < a.pt_stride) ptv[i] = prow[tid + 256 * i];
+  }
+  u32x4 qv = {0u, 0u, 0u, 0u};
+  if (tid < 32 * G)   // 16-byte chunk tid % 32 of head tid / 32
+    qv = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * a.num_q_heads + g * G + tid / 32) * kLocalD +
+                                          8 * (tid % 32));
   const int p = L - 1;
   const LocalWindow win = local_window(p, a.window);
   const int nsplit = local_nsplit(win.nv);
@@ -417,24 +434,33 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   const int vt = win.wrap ? 0 : win.nv - 1;
   const bool token_here = vt >= v0 && vt < v1;
   const bool append_here = a.v_new != nullptr && token_here;
-  // this (sequence, KV head)'s call count, the tag of this call's partials;
-  // read now, first used after the page loop (the empty asm there keeps the
-  // compiler from waiting for it before the pages are requested)
-  uint32_t epoch = nsplit > 1 ? __hip_atomic_load(a.epochs + (int64_t)s * a.num_kv_heads + g, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                              : 0u;
+
+  // q chunk j of a head sits at chunk j ^ ((j / 8) % 8) in LDS, so that the
+  // four quarters read below (chunks 8c + k, c = 0..3) hit distinct banks
+  __shared__ int sm_pt[kLocalPtLds];
+  __shared__ __attribute__((aligned(16))) uint32_t sm_q[G][128];
+  if (pt_lds) {
+#pragma unroll
+    for (int i = 0; i < kLocalPtLds / 256; ++i)
+      if (tid + 256 * i < a.pt_stride) sm_pt[tid + 256 * i] = ptv[i];
+  }
+  if (tid < 32 * G) {
+    const int j = tid % 32;
+    *reinterpret_cast<u32x4*>(&sm_q[tid / 32][4 * (j ^ ((j >> 3) & 7))]) = qv;
+  }
+  __syncthreads();
 
   // q of the group, this lane's quarter of the dims, as bf16 pairs
   const int c = lane & 3;
   uint32_t qr[G][32];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint16_t* qp = a.q + ((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + 64 * c;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint4 v = ld16_cached(qp + 8 * k);
-      qr[h][4 * k + 0] = v.x; qr[h][4 * k + 1] = v.y;
-      qr[h][4 * k + 2] = v.z; qr[h][4 * k + 3] = v.w;
+      const int j = 8 * c + k;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&sm_q[h][4 * (j ^ ((j >> 3) & 7))]);
+      qr[h][4 * k + 0] = v[0]; qr[h][4 * k + 1] = v[1];
+      qr[h][4 * k + 2] = v[2]; qr[h][4 * k + 3] = v[3];
     }
   }
 
@@ -450,8 +476,9 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   // This wave's pages are virtual pages v0 + w + 4k, k < nw.  The wave
   // holding the token's page takes it first and the rest in order; every
   // other wave goes in order.  The order is the same whether or not the call
-  // appends, so results are too.  Page ids come from scalar loads (the page
-  // table is read-only during the call), issued a page ahead of their use.
+  // appends, so results are too.  Page ids come from the LDS copy of the
+  // row, or, for longer rows, from scalar loads (the page table is read-only
+  // during the call) issued a page ahead of their use.
   const int nw = (v1 - v0 - w + kLocalWaves - 1) / kLocalWaves;
   const bool tok_wave = token_here && w == (vt - v0) % kLocalWaves;
   const int k_tok = tok_wave ? (vt - v0) / kLocalWaves : 0;
@@ -464,8 +491,8 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   auto vpage = [&](int k) __attribute__((always_inline)) {
     const int v = v0 + w + kLocalWaves * k;
     const bool merged = win.wrap && v == 0;
-    const int id0 = pt[win.pg0 + v];
-    const int id1 = merged ? pt[win.pgl] : id0;
+    const int id0 = pt_lds ? uniform_i32(sm_pt[win.pg0 + v]) : pt[win.pg0 + v];
+    const int id1 = merged ? (pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl]) : id0;
     VPage d;
     d.r0 = head_base + (int64_t)id0 * a.page_bytes;
     d.r1 = head_base + (int64_t)id1 * a.page_bytes;
@@ -481,6 +508,16 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     return d;
   };
 
+  // this (sequence, KV head)'s call count, the tag of this call's partials:
+  // read behind the first page's loads (a device-scope load goes to memory,
+  // and any wait for it would hold the page requests back), first used after
+  // the page loop (the empty asm there keeps the compiler from waiting for
+  // it earlier)
+  uint32_t epoch = 0u;
+  auto load_epoch = [&]() __attribute__((always_inline)) {
+    return __hip_atomic_load(a.epochs + (int64_t)s * a.num_kv_heads + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   __shared__ uint32_t sm_tok[kLocalWaves][128];   // a patching wave's rotated token K
   PageRegs<FP8> A, B;
   VPage dA{}, dB{};
@@ -492,10 +529,12 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
     if (nw > 1) dB = vpage(k_of(1));
     if (patch) {
-      uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)pt[win.pgl] * a.page_bytes;
+      const int id_tok = pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl];
+      uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)id_tok * a.page_bytes;
       put_new_token<FP8>(A, rec, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
     }
   }
+  if (nsplit > 1) epoch = load_epoch();
   for (int i = 0; i < nw; i += 2) {
     if (i + 1 < nw) load_vpage<FP8>(B, dB.r0, dB.r1, dB.b, lane);
     const VPage dA2 = i + 2 < nw ? vpage(k_of(i + 2)) : dA;
