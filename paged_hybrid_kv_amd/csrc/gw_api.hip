@@ -296,6 +296,7 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   a.part_ml = w.total ? reinterpret_cast<uint64_t*>(ws + w.counter_bytes + w.epoch_bytes + w.acc_bytes) : nullptr;
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
+  a.num_rows = num_rows;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.rope_cos = rope_cos;

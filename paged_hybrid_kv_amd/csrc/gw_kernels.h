@@ -27,6 +27,7 @@ struct LocalAttnArgs {
   uint32_t* epochs;           // [S][Hkv] calls with split partials so far
   int32_t max_splits;
   int32_t num_seqs;
+  int32_t num_rows;
   const uint16_t* k_new;      // bf16 [rows][Hkv][256] raw K of each row's own token, or null
   const uint16_t* v_new;      // bf16 [rows][Hkv][256], or null (no append)
   const float* rope_cos;      // [max_pos][128] or null (K stored as given)

@@ -403,15 +403,23 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
 
+  // The page-table row (when it has at most kLocalPtLds entries) and the
+  // group's q are read in the same round trip as the sequence's length and
+  // row -- before it is known which pages the window covers -- and go to LDS.
+  // q is read from row s, which is the row whenever the decode sequences
+  // come first (or one row per sequence); it is read again otherwise.
+  const auto q_chunk = [&](int r) __attribute__((always_inline)) {   // chunk tid % 32 of head tid / 32
+    return *reinterpret_cast<const u32x4*>(a.q + ((int64_t)r * a.num_q_heads + g * G + tid / 32) * kLocalD +
+                                           8 * (tid % 32));
+  };
+  u32x4 qv = {0u, 0u, 0u, 0u};
+  if (s < a.num_rows && tid < 32 * G) qv = q_chunk(s);
   int row = s;
   if (a.q_indptr) {
     row = ((CI32P)a.q_indptr)[s];
     if (((CI32P)a.q_indptr)[s + 1] - row != 1) return;   // rows of prompts go elsewhere
   }
   const int L = ((CI32P)a.seq_lens)[s];
-  // The page-table row (when it has at most kLocalPtLds entries) and the
-  // group's q are read in the same round trip as the length -- before it is
-  // known which pages the window covers -- and go to LDS.
   const bool pt_lds = a.pt_stride <= kLocalPtLds;
   int ptv[kLocalPtLds / 256] = {};
   if (pt_lds) {
@@ -420,10 +428,6 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     for (int i = 0; i < kLocalPtLds / 256; ++i)
       if (tid + 256 * i < a.pt_stride) ptv[i] = prow[tid + 256 * i];
   }
-  u32x4 qv = {0u, 0u, 0u, 0u};
-  if (tid < 32 * G)   // 16-byte chunk tid % 32 of head tid / 32
-    qv = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * a.num_q_heads + g * G + tid / 32) * kLocalD +
-                                          8 * (tid % 32));
   const int p = L - 1;
   const LocalWindow win = local_window(p, a.window);
   const int nsplit = local_nsplit(win.nv);
@@ -444,6 +448,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     for (int i = 0; i < kLocalPtLds / 256; ++i)
       if (tid + 256 * i < a.pt_stride) sm_pt[tid + 256 * i] = ptv[i];
   }
+  if (row != s && tid < 32 * G) qv = q_chunk(row);
   if (tid < 32 * G) {
     const int j = tid % 32;
     *reinterpret_cast<u32x4*>(&sm_q[tid / 32][4 * (j ^ ((j >> 3) & 7))]) = qv;
