@@ -322,7 +322,7 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
     ap.seq_lens = seq_lens;
     ap.num_seqs = num_seqs;
     ap.skip_single = 1;
-    e = gw::launch_append_local(ap, fp8, rope_cos != nullptr, (hipStream_t)stream);
+    e = gw::launch_append_local_rows(ap, fp8, rope_cos != nullptr, max_q_len, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   e = gw::launch_local_decode(a, group, fp8, (hipStream_t)stream);
@@ -402,7 +402,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     ap.seq_lens = seq_lens;
     ap.num_seqs = num_seqs;
     ap.skip_single = 1;
-    e = gw::launch_append_global(ap, compressed, (hipStream_t)stream);
+    e = gw::launch_append_global_rows(ap, compressed, max_q_len, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   e = gw::launch_global_decode(a, compressed, (hipStream_t)stream);

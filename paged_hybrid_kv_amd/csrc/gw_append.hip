@@ -147,6 +147,183 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   put_global_record<COMPRESSED>(a.pool + (int64_t)page * a.page_bytes, r, ps & 15, l);
 }
 
+// ------------------------------------------------ rows of an attention call
+// One workgroup per (sequence, page of its rows' range[, KV head]): the
+// rows' own tokens that fall in that page are rotated and stored with whole
+// 16-byte units where the unit's tokens are all rows (everywhere but at the
+// ends of a range), so a page of prompt rows is written with coalesced
+// stores, and the page lookup is made once per page.  Row r of sequence s
+// is at position seq_lens[s] - q_len + r (the attention calls' rows); one-
+// row sequences are skipped when skip_single is set (their decode kernel
+// appends them).  The arithmetic is the per-token kernels' exactly.
+struct RowsPage {
+  int r0, p0, pg, t0, t1, page;   // first row and its position, page index, slots [t0, t1], physical page
+};
+
+__device__ __forceinline__ bool rows_page(const AppendArgs& a, int s, int j, RowsPage& rp) {
+  rp.r0 = a.q_indptr ? a.q_indptr[s] : s;
+  const int ql = a.q_indptr ? a.q_indptr[s + 1] - rp.r0 : 1;
+  if (ql <= 0 || (a.skip_single && ql == 1)) return false;
+  const int L = a.seq_lens[s];
+  rp.p0 = L - ql;
+  rp.pg = (rp.p0 >> 4) + j;
+  if (rp.pg * kPage > L - 1) return false;
+  rp.t0 = max(rp.p0 - rp.pg * kPage, 0);
+  rp.t1 = min(L - 1 - rp.pg * kPage, kPage - 1);
+  rp.page = a.page_table[(int64_t)s * a.pt_stride + rp.pg];
+  return true;
+}
+
+template <int N>
+__device__ __forceinline__ void load_bf16_n(const uint16_t* p, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 8; ++q) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + 8 * q);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x[8 * q + 2 * m] = bf16_lo(w[m]);
+      x[8 * q + 2 * m + 1] = bf16_hi(w[m]);
+    }
+  }
+}
+
+// Local family.  K unit (k, t, c) (16 bytes at ((k*16 + t)*4 + c)*16 of the
+// K block) holds dims 64c + W k .. + W-1 of slot t (W = 8 bf16 / 16 e4m3);
+// quarters c and c + 2 are rotation partners, so thread (t, k, c < 2)
+// makes both.  V unit (u, l) (16 bytes at (u*64 + l)*16 of the V block)
+// holds dims 4l .. 4l+3 of slots T u .. T u + T-1 (T = 2 bf16 / 4 e4m3).
+template <bool FP8, bool ROPE>
+__global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
+  constexpr int kW = FP8 ? 16 : 8;           // dims per K unit
+  constexpr int kU = FP8 ? 4 : 8;            // K units per quarter (and V units per 64 lanes... rows)
+  constexpr int kT = FP8 ? 4 : 2;            // slots per V unit
+  constexpr int kVOff = FP8 ? 4096 : 8192;
+  const int s = blockIdx.x, h = blockIdx.z, tid = threadIdx.x;
+  RowsPage rp;
+  if (!rows_page(a, s, blockIdx.y, rp)) return;
+  uint8_t* hb = a.pool + (int64_t)rp.page * a.page_bytes + (int64_t)h * a.head_bytes;
+  auto row_src = [&](int t) __attribute__((always_inline)) {   // element offset of slot t's K / V
+    return ((int64_t)(rp.r0 + rp.pg * kPage + t - rp.p0) * a.num_kv_heads + h) * 256;
+  };
+  if (tid < kPage * kU * 2) {
+    const int t = tid / (kU * 2), k = (tid >> 1) % kU, c = tid & 1;
+    if (t >= rp.t0 && t <= rp.t1) {
+      const int64_t src = row_src(t);
+      const int d = 64 * c + kW * k;
+      float xa[kW], xb[kW], ya[kW], yb[kW];
+      load_bf16_n<kW>(a.k_raw + src + d, xa);
+      load_bf16_n<kW>(a.k_raw + src + d + 128, xb);
+      if constexpr (ROPE) {
+        const float* cp = a.rope_cos + (int64_t)(rp.pg * kPage + t) * 128 + d;
+        const float* sp = a.rope_sin + (int64_t)(rp.pg * kPage + t) * 128 + d;
+#pragma unroll
+        for (int e = 0; e < kW; e += 4) {
+          const float4 cs = *reinterpret_cast<const float4*>(cp + e);
+          const float4 sn = *reinterpret_cast<const float4*>(sp + e);
+          rope_pair(xa[e], xb[e], cs.x, sn.x, ya[e], yb[e]);
+          rope_pair(xa[e + 1], xb[e + 1], cs.y, sn.y, ya[e + 1], yb[e + 1]);
+          rope_pair(xa[e + 2], xb[e + 2], cs.z, sn.z, ya[e + 2], yb[e + 2]);
+          rope_pair(xa[e + 3], xb[e + 3], cs.w, sn.w, ya[e + 3], yb[e + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kW; ++e) { ya[e] = xa[e]; yb[e] = xb[e]; }
+      }
+      uint4 ua, ub;
+      if constexpr (!FP8) {
+        ua = uint4{pack_bf16(ya[0], ya[1]), pack_bf16(ya[2], ya[3]), pack_bf16(ya[4], ya[5]), pack_bf16(ya[6], ya[7])};
+        ub = uint4{pack_bf16(yb[0], yb[1]), pack_bf16(yb[2], yb[3]), pack_bf16(yb[4], yb[5]), pack_bf16(yb[6], yb[7])};
+      } else {
+        uint32_t wa[4], wb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          wa[q] = wb[q] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wa[q] |= f32_to_e4m3(round_bf16(ya[4 * q + e])) << (8 * e);
+            wb[q] |= f32_to_e4m3(round_bf16(yb[4 * q + e])) << (8 * e);
+          }
+        }
+        ua = uint4{wa[0], wa[1], wa[2], wa[3]};
+        ub = uint4{wb[0], wb[1], wb[2], wb[3]};
+      }
+      *reinterpret_cast<uint4*>(hb + ((k * kPage + t) * 4 + c) * 16) = ua;
+      *reinterpret_cast<uint4*>(hb + ((k * kPage + t) * 4 + c + 2) * 16) = ub;
+    }
+  }
+  // V: kPage / kT x 64 units
+  for (int un = tid; un < (kPage / kT) * 64; un += 256) {
+    const int u = un >> 6, l = un & 63;
+    const int ta = kT * u;
+    if (ta + kT - 1 < rp.t0 || ta > rp.t1) continue;
+    uint32_t e[kT][4];   // element j of slot ta + i, as raw bits (bf16) / e4m3 code
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      const int t = ta + i;
+      const bool in = t >= rp.t0 && t <= rp.t1;
+      const uint2 raw = in ? *reinterpret_cast<const uint2*>(a.v + row_src(t) + 4 * l) : uint2{0u, 0u};
+      const uint32_t b16[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) e[i][jj] = FP8 ? f32_to_e4m3(bits_to_f32(b16[jj] << 16)) : b16[jj];
+    }
+    uint8_t* ub = hb + kVOff + un * 16;
+    if (ta >= rp.t0 && ta + kT - 1 <= rp.t1) {   // the whole unit is rows of this call
+      uint32_t wv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (!FP8) wv[jj] = e[0][jj] | (e[1][jj] << 16);
+        else wv[jj] = e[0][jj] | (e[1][jj] << 8) | (e[2][jj] << 16) | (e[3][jj] << 24);
+      }
+      *reinterpret_cast<uint4*>(ub) = uint4{wv[0], wv[1], wv[2], wv[3]};
+    } else {                                     // an end of the range: element by element
+#pragma unroll
+      for (int i = 0; i < kT; ++i) {
+        const int t = ta + i;
+        if (t < rp.t0 || t > rp.t1) continue;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if constexpr (!FP8) reinterpret_cast<uint16_t*>(ub)[jj * 2 + i] = (uint16_t)e[i][jj];
+          else ub[jj * 4 + i] = (uint8_t)e[i][jj];
+        }
+      }
+    }
+  }
+}
+
+// Global family.  V unit (c, t) (16 bytes at (c*16 + t)*16 of the V block)
+// holds dims 8c .. 8c+7 of slot t; K_rot units (c, t) and (c + 8, t), c < 8,
+// hold the rotation of V's chunks c and c + 8 (pairs (i, i + 64)); the full
+// record's K block repeats V's chunks 16 .. 63.
+template <bool COMPRESSED>
+__global__ __launch_bounds__(256) void append_global_rows_kernel(AppendArgs a) {
+  const int s = blockIdx.x, tid = threadIdx.x;
+  RowsPage rp;
+  if (!rows_page(a, s, blockIdx.y, rp)) return;
+  uint8_t* pb = a.pool + (int64_t)rp.page * a.page_bytes;
+  uint8_t* vblock = COMPRESSED ? pb : pb + 16384;
+  uint8_t* kblock = COMPRESSED ? pb + 16384 : pb;
+  auto row_v = [&](int t) __attribute__((always_inline)) {
+    return a.v + (int64_t)(rp.r0 + rp.pg * kPage + t - rp.p0) * 512;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int un = tid + 256 * i, c = un >> 4, t = un & 15;
+    if (t < rp.t0 || t > rp.t1) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(row_v(t) + 8 * c);
+    *reinterpret_cast<uint4*>(vblock + un * 16) = v;
+    if (!COMPRESSED && c >= 16) *reinterpret_cast<uint4*>(kblock + un * 16) = v;
+  }
+  if (tid < 128) {
+    const int c = tid >> 4, t = tid & 15;
+    if (t >= rp.t0 && t <= rp.t1) {
+      const GlobalRecordLane r = global_record_lane(row_v(t), a.rope_cos, a.rope_sin, rp.pg * kPage + t, c);
+      *reinterpret_cast<uint4*>(kblock + (c * 16 + t) * 16) = r.ka;
+      *reinterpret_cast<uint4*>(kblock + ((c + 8) * 16 + t) * 16) = r.kb;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int rot_dim,
@@ -157,6 +334,29 @@ hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int ro
   const int64_t grid = (n + block - 1) / block;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)grid), dim3(block), 0, stream, cos_out,
                      sin_out, max_pos, half, head_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream) {
+  const int pages = (max_q_len + 14) / kPage + 1;   // pages a range of max_q_len tokens can touch
+  if (pages > 65535) return launch_append_local(a, fp8, rope, stream);
+  dim3 grid(a.num_seqs, pages, a.num_kv_heads), block(256);
+  if (fp8) {
+    if (rope) hipLaunchKernelGGL((append_local_rows_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((append_local_rows_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((append_local_rows_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((append_local_rows_kernel<false, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
+  const int pages = (max_q_len + 14) / kPage + 1;
+  if (pages > 65535) return launch_append_global(a, compressed, stream);
+  dim3 grid(a.num_seqs, pages), block(256);
+  if (compressed) hipLaunchKernelGGL((append_global_rows_kernel<true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((append_global_rows_kernel<false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -100,6 +100,9 @@ hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int
 hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream);
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStream_t stream);
+// Rows mode (seq_lens set): one workgroup per (sequence, page of its rows).
+hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream);
+hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream);
 hipError_t launch_append_global(const AppendArgs& a, bool compressed, hipStream_t stream);
 hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int rot_dim,
                              int head_dim, double theta, hipStream_t stream);

@@ -134,8 +134,8 @@ def test_local_mixed_equals_separate_calls():
 def test_local_in_call_append_mixed(fp8):
     """k_new / v_new for every row of a mixed call: the pool ends up as with
     gw_kv_append of those tokens, and the outputs are the same bits."""
-    lens = [700, 40, 1500, 17]
-    q_len = [1, 40, 1, 9]
+    lens = [700, 40, 1500, 17, 30]        # prompts starting on, before and after a page edge
+    q_len = [1, 40, 1, 9, 13]
     case = SY.local_case("append mixed", 95, lens, window=1024, num_q_heads=16, num_kv_heads=8,
                          q_len=q_len, rope=True, fp8=fp8, q_scale=0.5, kv_scale=0.5)
     dc_sep = RT.upload_local(case)
@@ -191,8 +191,8 @@ def test_global_prompt_dominant_keys():
 
 
 def test_global_in_call_append_mixed():
-    lens = [300, 45, 2000]
-    q_len = [1, 45, 1]
+    lens = [300, 45, 2000, 30]
+    q_len = [1, 45, 1, 13]
     case = SY.global_case("global append mixed", 115, lens, q_len=q_len, rope=True)
     for compressed in (True, False):
         dc_sep = RT.upload_global(case, compressed=compressed)
