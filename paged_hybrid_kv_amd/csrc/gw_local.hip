@@ -620,11 +620,13 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();   // every store of the workgroup is issued
+  // Every store of the workgroup is issued, not waited for: the barriers
+  // here order LDS only (a full __syncthreads would wait for the stores).
+  lds_barrier();
   int* counter = a.counters + (int64_t)s * a.num_kv_heads + g;
   if (tid == 0)
     sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
-  __syncthreads();
+  lds_barrier();
   if (!sm_last) return;
   // The heads of the group are merged together, so their loads share one
   // round trip; a row's range of up to 68 pages has at most 4 splits.
