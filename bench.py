@@ -171,6 +171,94 @@ def cpu_baseline(step):
                       f"{nbytes} algorithmic KV bytes; os.cpu_count()={os.cpu_count()}"}
 
 
+def config_throughput(iters=30):
+    """Decode-attention throughput of the three single-family workloads at
+    their full sizes (the parity tests' cases; the page tables come from the
+    same seeded recipes, the pools are filled on the device with torch's
+    seeded generator): local bf16 (16 slots, contexts U[1024, 8192], window
+    1024, 16 q / 8 KV heads), global tied (8 slots x 131072 tokens, 32 q / 1
+    KV head, compressed and full records) and local e4m3 (64 slots x 8192).
+    Calls run back to back over pool replicas whose total exceeds the 256 MB
+    last-level cache; returns {name: {us, GB_s, pct_of_peak, tok_s, bytes}}."""
+    import numpy as np
+    import torch
+    from paged_hybrid_kv_amd import gw, runtime as RT, synth as SY
+
+    dev = "cuda"
+
+    def local_pool(lens, fp8, seed, rep):
+        rng = np.random.default_rng(seed)
+        lens = lens(rng) if callable(lens) else np.asarray(lens)
+        seqs = SY.make_page_table(rng, lens)
+        dt = gw.GW_KV_E4M3 if fp8 else gw.GW_KV_BF16
+        pool = RT.Pool(gw.GW_FAMILY_LOCAL, dt, seqs.num_pages, 8, 256, dev)
+        pt, stride = RT.i32_dev(seqs.page_table), seqs.page_table.shape[1]
+        max_len = int(lens.max())
+        cos, sin = RT.rope_tables(max_len, 256, 256, RT.LOCAL_THETA)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 * seed + rep)
+        for s, L in enumerate(lens):           # the window's tokens (and the rest of its first page)
+            lo = max(0, int(L) - 1024) // 16 * 16
+            n = int(L) - lo
+            k = (torch.randn(n, 8, 256, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+            v = (torch.randn(n, 8, 256, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+            si = torch.full((n,), s, dtype=torch.int32, device=dev)
+            pos = torch.arange(lo, int(L), dtype=torch.int32, device=dev)
+            gw.gw_kv_append(pool.desc, k, v, si, pos, n, pt, stride, cos, sin)
+        q = (torch.randn(len(lens), 16, 256, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+        return RT.DeviceCase(pool, q, None, RT.i32_dev(lens), pt, stride, len(lens), len(lens), 1, max_len,
+                             16, 1 / 16, 1024)
+
+    def global_pool(compressed):
+        rng = np.random.default_rng(3)
+        lens = np.full(8, 131072)
+        seqs = SY.make_page_table(rng, lens)
+        fam = gw.GW_FAMILY_GLOBAL_COMPRESSED if compressed else gw.GW_FAMILY_GLOBAL_FULL
+        pool = RT.Pool(fam, gw.GW_KV_BF16, seqs.num_pages, 1, 128, dev)
+        pt, stride = RT.i32_dev(seqs.page_table), seqs.page_table.shape[1]
+        cos, sin = RT.rope_tables(131072, 128, 512, RT.GLOBAL_THETA)
+        g = torch.Generator(device=dev)
+        g.manual_seed(3000)
+        for s in range(8):
+            for c0 in range(0, 131072, 32768):
+                v = torch.randn(32768, 512, device=dev, generator=g).to(torch.bfloat16)
+                si = torch.full((32768,), s, dtype=torch.int32, device=dev)
+                pos = torch.arange(c0, c0 + 32768, dtype=torch.int32, device=dev)
+                gw.gw_kv_append(pool.desc, None, v, si, pos, 32768, pt, stride, cos, sin)
+        q = torch.randn(8, 32, 512, device=dev, generator=g).to(torch.bfloat16)
+        return RT.DeviceCase(pool, q, None, RT.i32_dev(lens), pt, stride, 8, 8, 1, 131072, 32, 512 ** -0.5, None)
+
+    def timed(dcs, nbytes, slots):
+        ws = RT.Workspace()
+        outs = [RT.attend(dc, ws=ws) for dc in dcs]
+        torch.cuda.synchronize()
+        ms = time_events(lambda: [RT.attend(dc, out=o, ws=ws) for dc, o in zip(dcs, outs)], iters) / len(dcs)
+        return {"us": round(ms * 1e3, 2), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "pct_of_peak": round(nbytes / (ms * 1e-3) / PEAK_HBM * 100, 2),
+                "tok_s": round(slots / (ms * 1e-3), 1), "bytes": nbytes}
+
+    res = {}
+    c2_lens = lambda r: r.integers(1024, 8192, size=16, endpoint=True)
+    lens2 = c2_lens(np.random.default_rng(2))
+    c2 = [local_pool(c2_lens, False, 2, r) for r in range(4)]
+    res["local_bf16"] = timed(c2, int(sum(min(int(L), 1024) for L in lens2)) * 8 * 256 * 2 * 2, 16)
+    del c2
+    torch.cuda.empty_cache()
+    for compressed in (True, False):
+        dc = global_pool(compressed)
+        res["global_" + ("compressed" if compressed else "full")] = timed(
+            [dc], 8 * 131072 * (1280 if compressed else 2048), 8)
+        del dc
+        torch.cuda.empty_cache()
+    c4 = [local_pool([8192] * 64, True, 4, r) for r in range(2)]
+    res["local_fp8"] = timed(c4, 64 * 1024 * 8 * 256 * 2, 64)
+    del c4
+    torch.cuda.empty_cache()
+    for k, v in res.items():
+        log(f"{k}: {v['us']} us/call, {v['GB_s']} GB/s ({v['pct_of_peak']}% of peak), {v['tok_s']} tok/s")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-rounds", type=int, default=10)
     ap.add_argument("--no-mixed", action="store_true", help="skip the step with prompt rows")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the local bf16, global tied and local e4m3 workloads at full size")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -238,6 +328,8 @@ def main():
     if args.copy_calib:
         copy_calibration()
 
+    configs = config_throughput() if args.configs else None
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(step)
     if cpu:
         log(f"cpu baseline: {cpu['value']} GB/s over {cpu['seconds']} s on {cpu['cores']} threads")
@@ -260,6 +352,8 @@ def main():
         "mixed_step": mixed,
         "cpu_baseline": cpu,
     }
+    if configs is not None:
+        line["other_configs"] = configs
     print(json.dumps(line), flush=True)
 
 
