@@ -218,22 +218,12 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   const int n_pairs = (n + 1) >> 1;
   const int head = 16 * hb + l16;
 
-  // ---- everything the page loop needs besides the pages goes out first, in
-  // one round trip: the row's q (64 bytes per thread: head tid / 16, 16-byte
-  // chunks 4 (tid % 16) .. +3), the split's physical page ids (one per lane
-  // and register, read back with readlane; a split has at most 256 pages)
-  // and, on the wave that appends a decode row's own token, that token's
-  // inputs.  They are waited for before the first page transfer is issued:
-  // the compiler does not see the transfers, and a wait of its own placed
-  // later would hold for them too.
-  const int qh = tid >> 4, qc0 = 4 * (tid & 15);
-  const bool q_mine = qh < a.num_q_heads;
-  u32x4 qraw[4] = {};
-  if (q_mine) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((int64_t)row * a.num_q_heads + qh) * kGD) + qc0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
-  }
+  // ---- the split's physical page ids (one per lane and register, read
+  // back with readlane; a split has at most 256 pages) and, on the wave that
+  // appends a decode row's own token, that token's inputs go out first, in
+  // one round trip, and are waited for before anything else is issued: the
+  // compiler does not see the direct-to-LDS transfers below, and a wait of
+  // its own placed after them would hold for them too.
   const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride + pg0;
   auto pt_at = [&](int idx) __attribute__((always_inline)) { return idx < n ? pt[idx] : 0; };
   const int ptv0 = pt_at(lane);
@@ -254,27 +244,33 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   const bool append_here = a.v_new != nullptr && split == nsplit - 1;
   GlobalRecordLane rec{};
   if (append_here && wv == 0) rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qraw[c]));
   asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
   if (append_here && wv == 0)
     put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
                                   p & 15, lane);
-  // q into LDS, in ring slot NP - 1 (free until the loop's first transfer),
-  // 1 KiB per head with 16-byte chunk c of head h at chunk c ^ (h % 8), so
-  // that the Q^T operand reads below hit distinct banks
+
+  // ---- q into LDS by direct transfers, ahead of the pages, in ring slot
+  // NP - 1 (free until the loop's first transfer): 1 KiB per head, the
+  // row's 16-byte chunk c of head h stored at chunk c ^ (h % 8), so that the
+  // Q^T operand reads below hit distinct banks.  Wave wv moves heads
+  // 2 HB wv .. +2 HB - 1; lane i fetches the chunk that lands at position i.
   uint8_t* qs = &ring[NP - 1][0][0];
-  if (q_mine) {
+  {
+    const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(qs + qh * 1024 + (((qc0 + c) ^ (qh & 7)) * 16)) = qraw[c];
+    for (int i = 0; i < 2 * HB; ++i) {
+      const int h = 2 * HB * wv + i;
+      dma16_to_lds(a.q + ((int64_t)row * a.num_q_heads + h) * kGD + 8 * (lane ^ (h & 7)),
+                   qs_lds + (uint32_t)(h * 1024));
+    }
   }
 
   // ---- transfers: group q moves page 2j + q of pair j, wave w of the group
   // the units [kPerWave w, kPerWave (w + 1)) of the page (1 KiB each), so
   // the LDS copy has the pool's layout.  An odd split's last pair repeats
   // its last page as the second one; that copy is never computed on.  The
-  // loop's waits count transfers only; the appending wave's pool stores are
-  // older than all of them, so they are covered too.
+  // loop's waits count transfers only; the appending wave's pool stores and
+  // the q transfers are older than all of them, so they are covered too.
   const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) +
                              (uint32_t)(grp * PG::kBytes + 1024 * kPerWave * w);
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
@@ -288,7 +284,9 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
 
-  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7 (16-byte chunk 4ks + g)
+  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7 (16-byte chunk 4ks + g),
+  // once every wave's q transfers (older than its page transfers) are in
+  wait_groups_after<kPerWave>(min(NP - 1, n_pairs));
   lds_barrier();
   bf16x8 qf[16];
 #pragma unroll
