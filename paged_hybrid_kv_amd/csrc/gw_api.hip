@@ -378,6 +378,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   a.part_ml = w.total ? reinterpret_cast<float*>(ws + w.counter_bytes + w.acc_bytes) : nullptr;
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
+  a.num_rows = num_rows;
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;

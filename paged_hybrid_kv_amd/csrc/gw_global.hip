@@ -364,24 +364,20 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 // p_r = seq_len - q_len + r and attends keys 0 .. p_r.  A workgroup takes two
 // consecutive rows: group q (four waves, as in the decode kernel) row 2m + q,
 // and both groups read the same stream of pages, pages 0 .. p_last / 16 of
-// the pair, through an LDS ring of NS pages moved by group 0.  No split: a
-// row's whole range is one pass, and the output is written directly.  The
-// pairs with the most pages are dispatched first.
+// the pair, through an LDS ring of NS pages that all eight waves fill.  No
+// split: a row's whole range is one pass, and the output is written
+// directly.  Workgroups are numbered compactly over the prompt sequences'
+// row pairs, a sequence's pairs with the most pages first.
 template <bool COMPRESSED, int HB, int NS>
 __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a) {
   using PG = GlobalPage<COMPRESSED>;
   constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
-  constexpr int kPerWave = kUnits / 4;        // units per wave of group 0 per page
   constexpr int kBlocks = 8 * HB;
-  static_assert(NS >= 2 && NS - 2 <= 4 && kPerWave * (NS - 2) < 64, "ring depth");
+  static_assert(kUnits % 4 == 0, "page units");
+  constexpr int kPerWave = kUnits / 8;        // units per wave per page (all eight waves move)
+  constexpr int kPerWaveTail = kUnits % 8;    // the first kUnits % 8 waves move one more
+  static_assert(NS >= 2 && NS - 2 <= 4 && (kPerWave + 1) * (NS - 2) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
-
-  const int s = blockIdx.x;
-  const int row0 = a.q_indptr[s];
-  const int q_len = a.q_indptr[s + 1] - row0;
-  if (q_len < 2) return;
-  const int mp = ((q_len + 1) >> 1) - 1 - (int)blockIdx.y;   // row pair, longest first
-  if (mp < 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform_i32(tid >> 6);
@@ -391,7 +387,48 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   const int g = lane >> 4, l16 = lane & 15;
   const int head = 16 * hb + l16;
 
-  const int L = a.seq_lens[s];
+  // ---- work item: the call's (prompt sequence, row pair) items, numbered
+  // sequence by sequence, a sequence's last pairs (longest ranges) first
+  int s = -1, mp = 0, row0 = 0, q_len = 0, L = 0;
+  {
+    const int item = blockIdx.x;
+    int base = 0;
+    for (int c = 0; c < a.num_seqs; c += 64) {
+      const int sl = c + lane;
+      int cnt = 0, r0 = 0, ql = 0, len = 0;
+      if (sl < a.num_seqs) {
+        r0 = a.q_indptr[sl];
+        ql = a.q_indptr[sl + 1] - r0;
+        len = a.seq_lens[sl];
+        if (ql > 1) cnt = (ql + 1) >> 1;
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int up = __shfl_up(incl, d, 64);
+        incl += lane >= d ? up : 0;
+      }
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (item < base + total) {
+        const int ls = __builtin_ctzll(__ballot(base + incl > item));
+        s = c + ls;
+        const int nb = __builtin_amdgcn_readlane(cnt, ls);
+        mp = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
+        row0 = __builtin_amdgcn_readlane(r0, ls);
+        q_len = __builtin_amdgcn_readlane(ql, ls);
+        L = __builtin_amdgcn_readlane(len, ls);
+        break;
+      }
+      base += total;
+    }
+  }
+  if (s < 0) return;
+  s = uniform_i32(s);
+  mp = uniform_i32(mp);
+  row0 = uniform_i32(row0);
+  q_len = uniform_i32(q_len);
+  L = uniform_i32(L);
+
   const int r = 2 * mp + grp;
   const bool row_ok = r < q_len;                 // uniform in the group
   const int r_last = min(2 * mp + 1, q_len - 1);
@@ -399,15 +436,19 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   const int p_last = L - q_len + r_last;
   const int n = (p_last >> 4) + 1;
 
+  // wave wv moves units [u0, u0 + nu) of every page: kPerWave each, the
+  // first kUnits % 8 waves one more
+  const int nu = kPerWave + (wv < kPerWaveTail ? 1 : 0);
+  const int u0 = kPerWave * wv + min(wv, kPerWaveTail);
   PageIds ids;
   ids.init(a.page_table + (int64_t)s * a.pt_stride, n, lane);
-  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0])) + (uint32_t)(1024 * kPerWave * w);
+  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0])) + (uint32_t)(1024 * u0);
   auto issue_page = [&](int i) __attribute__((always_inline)) {
-    if (grp != 0) return;
-    const uint8_t* src = a.pool + (int64_t)ids.get(i) * a.page_bytes + 1024 * kPerWave * w + 16 * lane;
+    const uint8_t* src = a.pool + (int64_t)ids.get(i) * a.page_bytes + 1024 * u0 + 16 * lane;
     const uint32_t dst = ring_base + (uint32_t)((i % NS) * PG::kBytes);
 #pragma unroll
-    for (int u = 0; u < kPerWave; ++u) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+    for (int u = 0; u < kPerWave + 1; ++u)
+      if (u < nu) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
@@ -429,7 +470,8 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   const int v_lane_off = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
 
   for (int i = 0; i < n; ++i) {
-    wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
+    if (nu > kPerWave) wait_groups_after<kPerWave + 1>(min(NS - 2, n - 1 - i));
+    else wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
     lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
     if (i + NS - 1 < n) issue_page(i + NS - 1);
     if (row_ok && i * 16 <= p)
@@ -525,7 +567,14 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStr
 }
 
 hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
-  dim3 grid(a.num_seqs, (max_q_len + 1) / 2), block(512);
+  // items: (prompt sequence, row pair); at most (rows + sequences) / 2, and
+  // at most sequences * ceil(max_q_len / 2)
+  const int64_t by_rows = ((int64_t)a.num_rows + a.num_seqs) / 2;
+  const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + 1) / 2);
+  const int64_t items = by_rows < by_len ? by_rows : by_len;
+  if (items == 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)items), block(512);
   const bool h32 = a.num_q_heads == 32;
   if (compressed) {
     if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 4>), grid, block, 0, stream, a);

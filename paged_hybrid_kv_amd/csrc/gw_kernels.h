@@ -50,6 +50,7 @@ struct GlobalAttnArgs {
   int* counters;              // [S] splits finished; zero between calls
   int32_t max_splits;
   int32_t num_seqs;
+  int32_t num_rows;
   const uint16_t* v_new;      // bf16 [rows][512] raw V (= K before rotation) of each row's token, or null
   const float* rope_cos;      // [max_pos][64]
   const float* rope_sin;

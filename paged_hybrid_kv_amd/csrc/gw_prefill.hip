@@ -9,23 +9,29 @@
 // KV head g = h / G attends the keys j in [max(0, p_r - W + 1), p_r].
 //
 // With many rows per KV head the score and value steps are dense
-// contractions, so both run on MFMA in 16 x 16 blocks over "query vectors"
-// (a row and one head of its group): lane column l16 of a wave is query
-// vector (row r0 + l16 / G, head l16 % G).
+// contractions, so both run on MFMA over "query vectors" (a row and one head
+// of its group), 16 to a block: lane column l16 of block qb of wave w is
+// query vector v = 32 w + 16 qb + l16 (row r_first + v / G, head v % G).
+// The keys go by in steps of 32 tokens (two pages):
 //   S^T (16 tokens x 16 q vectors) = K (16 x 256) . Q^T (256 x 16)
-//                                     -- v_mfma_f32_16x16x32_bf16, 8 steps
-//   O^T (16 dims x 16 q vectors)  += V^T (16 x 16 tokens) . P^T (16 x 16)
-//                                     -- v_mfma_f32_16x16x16_bf16, 16 dim blocks
-// A workgroup (4 waves, 64 query vectors) takes 64 / G consecutive rows of
-// one (sequence, KV head) and streams the pages of their union range,
-// [max(0, p_first - W + 1), p_last], through an LDS ring (direct global->LDS
-// transfers, each wave moving a quarter of every page).  Each lane masks its
-// own query vector's window; V of tokens outside the union range (slots that
+//         -- v_mfma_f32_16x16x32_bf16, 8 steps, per page and query block
+//   O^T (16 dims x 16 q vectors)  += V^T (16 x 32 tokens) . P^T (32 x 16)
+//         -- v_mfma_f32_16x16x32_bf16, per 16-dim block and query block
+// where lane (l16, gq) holds the scores of tokens 4 gq .. +3 of each page,
+// which it also supplies as the PV step's k slots 8 gq .. +7, so P never
+// leaves the lane.  A workgroup (4 waves, 128 query vectors) takes 128 / G
+// consecutive rows of one (sequence, KV head) and streams the pages of
+// their union range, [max(0, p_first - W + 1), p_last], through an LDS ring
+// (direct global->LDS transfers, each wave moving a quarter of every page),
+// so K/V are read once per 128 query vectors.  Each lane masks its own
+// query vectors' windows; V of tokens outside the union range (slots that
 // may never have been written) is zeroed in the operand registers.  e4m3
 // codes convert to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), so
 // the products are the same as on the bf16 values.  P is rounded to bf16 for
-// PV and the sum l adds exactly those rounded values.  The row blocks with
-// the longest ranges are dispatched first.
+// PV and the sum l adds exactly those rounded values.  Workgroups are
+// numbered compactly over the prompt sequences' row blocks, a sequence's
+// longest ranges first, with the KV head as the fastest index (so one
+// head's blocks share an XCD when there are eight heads).
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -35,16 +41,39 @@ namespace gw {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+// A read-only int32 array read through the constant address space, so that
+// uniform reads become scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* CI32P;
 
+// One (page, KV head) record as the prefill kernel keeps it in LDS.  The
+// transfers move 16-byte chunks, 1 KiB units at a time, and place them so
+// that a fragment read of 16 lanes (bf16 K) or of the whole wave (bf16 V)
+// touches every LDS bank once: K unit chunk (t, c) (token t, quarter c)
+// sits at position 4 t + (c ^ (t / 4)), and chunk c of V unit u at
+// c ^ (4 ((u / 2) % 4)).  e4m3 records keep the pool's layout.
 template <bool FP8>
 struct LocalHead {
   static constexpr int kBytes = FP8 ? 8192 : 16384;   // K block + V block of one KV head
   static constexpr int kVOff = kBytes / 2;
+  static constexpr int kKUnits = kVOff / 1024;
+  // byte offset, inside unit U of the record, of the chunk that the
+  // transfer lane `lane` places at its own position
+  __device__ static __forceinline__ int src_chunk_off(int U, int lane) {
+    if constexpr (FP8) {
+      return 16 * lane;
+    } else {
+      if (U < kKUnits) {
+        const int t = lane >> 2;
+        return 16 * (4 * t + ((lane & 3) ^ (t >> 2)));
+      }
+      return 16 * (lane ^ (4 * (((U - kKUnits) >> 1) & 3)));
+    }
+  }
   // K operand: token t, dims 32 ks + 8 gq .. +7, as 8 bf16
   __device__ static __forceinline__ bf16x8 k_frag(const uint8_t* pg, int ks, int gq, int t) {
     if constexpr (!FP8) {
       const int k = 4 * (ks & 1) + gq, c = ks >> 1;
-      return *reinterpret_cast<const bf16x8*>(pg + ((k * 16 + t) * 4 + c) * 16);
+      return *reinterpret_cast<const bf16x8*>(pg + k * 1024 + (4 * t + (c ^ (t >> 2))) * 16);
     } else {
       const int k = 2 * (ks & 1) + (gq >> 1), c = ks >> 1;
       const uint2 w = *reinterpret_cast<const uint2*>(pg + ((k * 16 + t) * 4 + c) * 16 + 8 * (gq & 1));
@@ -55,7 +84,7 @@ struct LocalHead {
   // V^T operand: dim d, tokens 4 gq .. 4 gq + 3, as 4 bf16 (two dwords)
   __device__ static __forceinline__ uint2 v_frag(const uint8_t* pg, int d, int gq) {
     if constexpr (!FP8) {
-      const uint8_t* b = pg + kVOff + (((2 * gq) * 64 + (d >> 2)) * 4 + (d & 3)) * 4;
+      const uint8_t* b = pg + kVOff + (2 * gq) * 1024 + (d ^ (16 * gq)) * 4;
       return uint2{*reinterpret_cast<const uint32_t*>(b), *reinterpret_cast<const uint32_t*>(b + 1024)};
     } else {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(pg + kVOff + ((gq * 64 + (d >> 2)) * 4 + (d & 3)) * 4);
@@ -64,149 +93,310 @@ struct LocalHead {
   }
 };
 
+// Largest excess, in base-2 exponent, of a score over the running reference
+// max before the reference moves (so unnormalised weights stay <= 2^8).
+constexpr float kLazyMax = 8.f;
+
+// Rows of prompt per workgroup: 128 query vectors, 32 per wave.
+template <int G>
+constexpr int prefill_rows_per_wg() {
+  return 128 / G;
+}
+
 template <int G, bool FP8, int NS>
-__global__ __launch_bounds__(256, 2) void local_prefill_kernel(LocalAttnArgs a) {
+__global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) {
   using LH = LocalHead<FP8>;
-  constexpr int kUnits = LH::kBytes / 1024;   // 1 KiB transfer units per (page, head)
-  constexpr int kPerWave = kUnits / 4;
-  constexpr int kRowsPerWave = 16 / G;
-  constexpr int kRowsPerWG = 4 * kRowsPerWave;
-  static_assert(NS >= 2 && NS - 2 <= 4 && kPerWave * (NS - 2) < 64, "ring depth");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NS][LH::kBytes];
+  constexpr int kUnits = LH::kBytes / 1024;    // 1 KiB transfer units per (page, head)
+  constexpr int kPerWavePage = kUnits / 4;     // units a wave moves of each page
+  constexpr int kPerStep = 2 * kPerWavePage;   // transfers per wave per two-page step
+  constexpr int kRows = prefill_rows_per_wg<G>();
+  static_assert(NS >= 3 && NS - 2 <= 4 && kPerStep * (NS - 2) < 64, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS][2][LH::kBytes];
 
-  const int s = blockIdx.x, gk = blockIdx.y;
-  const int row0 = a.q_indptr[s];
-  const int q_len = a.q_indptr[s + 1] - row0;
-  if (q_len < 2) return;
-  const int rb = cdiv_i(q_len, kRowsPerWG) - 1 - (int)blockIdx.z;   // longest ranges first
-  if (rb < 0) return;
-
+  const int gk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
   const int gq = lane >> 4, l16 = lane & 15;
-  const int L = a.seq_lens[s];
-  const int r_first = rb * kRowsPerWG;
-  const int r_last = min(r_first + kRowsPerWG, q_len) - 1;
-  const int p_last = L - q_len + r_last;
-  const int lo_first = max(0, L - q_len + r_first - a.window + 1);
-  const int pg_lo = lo_first >> 4;
-  const int n = (p_last >> 4) - pg_lo + 1;
 
-  // this lane's query vector
-  const int r = r_first + w * kRowsPerWave + l16 / G, hq = l16 % G;
-  const bool row_ok = r <= r_last;
-  const int rr = row_ok ? r : r_last;
-  const int pq = L - q_len + rr;
-  const int loq = max(0, pq - a.window + 1);
-
-  PageIds ids;
-  ids.init(a.page_table + (int64_t)s * a.pt_stride + pg_lo, n, lane);
-  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0])) + (uint32_t)(1024 * kPerWave * w);
-  const int64_t head_off = (int64_t)gk * a.head_bytes + 1024 * kPerWave * w + 16 * lane;
-  auto issue_page = [&](int i) __attribute__((always_inline)) {
-    const uint8_t* src = a.pool + (int64_t)ids.get(i) * a.page_bytes + head_off;
-    const uint32_t dst = ring_base + (uint32_t)((i % NS) * LH::kBytes);
+  // ---- work item: the call's (prompt sequence, row block) items, numbered
+  // sequence by sequence, the blocks of a sequence from its last (longest
+  // range) to its first; item blockIdx.y, for KV head blockIdx.x
+  int s = -1, rb = 0, row0 = 0, q_len = 0, L = 0;
+  {
+    const int item = blockIdx.y;
+    int base = 0;
+    for (int c = 0; c < a.num_seqs; c += 64) {
+      const int sl = c + lane;
+      int cnt = 0, r0 = 0, ql = 0, len = 0;
+      if (sl < a.num_seqs) {
+        r0 = a.q_indptr[sl];
+        ql = a.q_indptr[sl + 1] - r0;
+        len = a.seq_lens[sl];
+        if (ql > 1) cnt = cdiv_i(ql, kRows);
+      }
+      int incl = cnt;
 #pragma unroll
-    for (int u = 0; u < kPerWave; ++u) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+      for (int d = 1; d < 64; d <<= 1) {
+        const int up = __shfl_up(incl, d, 64);
+        incl += lane >= d ? up : 0;
+      }
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (item < base + total) {
+        const int ls = __builtin_ctzll(__ballot(base + incl > item));
+        s = c + ls;
+        const int nb = __builtin_amdgcn_readlane(cnt, ls);
+        rb = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
+        row0 = __builtin_amdgcn_readlane(r0, ls);
+        q_len = __builtin_amdgcn_readlane(ql, ls);
+        L = __builtin_amdgcn_readlane(len, ls);
+        break;
+      }
+      base += total;
+    }
+  }
+  if (s < 0) return;
+  s = uniform_i32(s);
+  rb = uniform_i32(rb);
+  row0 = uniform_i32(row0);
+  q_len = uniform_i32(q_len);
+  L = uniform_i32(L);
+
+  // rows r_first .. r_last at positions pos0 + r; their union range
+  // [lo_first, p_last] covers pages pg_lo .. pg_lo + n_pages - 1, walked in
+  // steps of two pages (an odd count's last step repeats its last page as
+  // the second, every token of which lies past p_last)
+  const int pos0 = L - q_len;
+  const int r_first = rb * kRows;
+  const int r_last = min(r_first + kRows, q_len) - 1;
+  const int p_last = pos0 + r_last;
+  const int lo_first = max(0, pos0 + r_first - a.window + 1);
+  const int pg_lo = lo_first >> 4;
+  const int n_pages = (p_last >> 4) - pg_lo + 1;
+  const int n_steps = (n_pages + 1) >> 1;
+  // every row of the block attends [lo_max, p_min] (at least)
+  const int lo_max = max(0, pos0 + r_last - a.window + 1);
+  const int p_min = pos0 + r_first;
+
+  // this lane's two query vectors, v = 32 w + 16 qb + l16: row
+  // r_first + v / G, head v % G of the group; each masks its own window
+  int pq[2], loq[2];
+  bool rok[2];
+  bf16x8 qf[2][8];   // Q^T operand: dims 32 ks + 8 gq .. +7
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int v = 32 * w + 16 * qb + l16;
+    const int r = r_first + v / G;
+    rok[qb] = r <= r_last;
+    const int rr = rok[qb] ? r : r_last;
+    pq[qb] = pos0 + rr;
+    loq[qb] = max(0, pq[qb] - a.window + 1);
+    const uint16_t* qp = a.q + ((int64_t)(row0 + rr) * a.num_q_heads + gk * G + v % G) * 256 + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+  }
+  // page ids come through the scalar cache (the page table is read-only
+  // during the call), one uniform load per page as its transfer is issued
+  const CI32P pt = (CI32P)(a.page_table + (int64_t)s * a.pt_stride + pg_lo);
+  // q is not waited for before the transfers: the compiler's own wait at the
+  // first product (it does not see the transfers) holds for those already
+  // issued too, which the first step needs anyway
+
+  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) + (uint32_t)(1024 * kPerWavePage * w);
+  const int64_t head_off = (int64_t)gk * a.head_bytes + 1024 * kPerWavePage * w;
+  int src_off[kPerWavePage];
+#pragma unroll
+  for (int u = 0; u < kPerWavePage; ++u) src_off[u] = 1024 * u + LH::src_chunk_off(kPerWavePage * w + u, lane);
+  auto issue_step = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint8_t* src = a.pool + (int64_t)pt[min(2 * j + h, n_pages - 1)] * a.page_bytes + head_off;
+      const uint32_t dst = ring_base + (uint32_t)(((j % NS) * 2 + h) * LH::kBytes);
+#pragma unroll
+      for (int u = 0; u < kPerWavePage; ++u) dma16_to_lds(src + src_off[u], dst + 1024 * u);
+    }
   };
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (i < n) issue_page(i);
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_steps) issue_step(j);
 
-  // Q^T operand: query vector l16, dims 32 ks + 8 gq .. +7
-  bf16x8 qf[8];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(row0 + rr) * a.num_q_heads + gk * G + hq) * 256 + 8 * gq;
+  f32x4 acc[2][16];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
+    for (int b = 0; b < 16; ++b) acc[qb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // l, in every element
+  const bf16x8 kOnes = __builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-  f32x4 acc[16];
+  // ---- S^T = K . Q^T for both pages (tb) and both query blocks (qb) of a
+  // step in the ring: all 16 K fragments first, then four interleaved
+  // accumulation chains
+  auto scores = [&](int j, f32x4 (&sc)[2][2]) __attribute__((always_inline)) {
+    const uint8_t* pg0 = ring[j % NS][0];
+    const uint8_t* pg1 = ring[j % NS][1];
+    bf16x8 kf[2][8];
 #pragma unroll
-  for (int b = 0; b < 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  for (int i = 0; i < n; ++i) {
-    wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
-    lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
-    if (i + NS - 1 < n) issue_page(i + NS - 1);
-    const uint8_t* pg = ring[i % NS];
-    const int tok_page0 = (pg_lo + i) * 16;
-
-    // ---- S^T = K . Q^T (two accumulation chains)
-    bf16x8 kf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = LH::k_frag(pg, ks, gq, l16);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-    for (int ks = 0; ks < 8; ks += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[0][ks] = LH::k_frag(pg0, ks, gq, l16);
+      kf[1][ks] = LH::k_frag(pg1, ks, gq, l16);
     }
-    const f32x4 sacc = s0 + s1;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sc[tb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sc[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tb][ks], qf[qb][ks], sc[tb][qb], 0, 0, 0);
+  };
 
-    // ---- online softmax of this lane's query vector over the page
-    const int tok0 = tok_page0 + 4 * gq;
-    float z[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      z[k] = (row_ok && tok0 + k >= loq && tok0 + k <= pq) ? sacc[k] * a.scale_log2 : -INFINITY;
-    const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-    const float mnew = fmaxf(m_run, mx);
-    if (__any(mnew > m_run)) {
-      const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-#pragma unroll
-      for (int b = 0; b < 16; ++b) acc[b] *= alpha;
-      l_run *= alpha;
-    }
-    m_run = mnew;
-    float pr[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pr[k] = z[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[k] - m_run);
-    const uint32_t p01 = pack_bf16(pr[0], pr[1]), p23 = pack_bf16(pr[2], pr[3]);
-    l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-    const s16x4 pb = __builtin_bit_cast(s16x4, uint2{p01, p23});
+  // Software pipeline, one step deep: iteration j turns step j's scores
+  // (computed in iteration j - 1) into weights on VALU while step j + 1's
+  // scores run on MFMA, then adds step j's PV.  Steps j and j + 1 are in
+  // LDS during iteration j, so NS - 2 steps are in flight; step j - 1's
+  // slot is refilled once every wave is past iteration j - 1.
+  wait_groups_after<kPerStep>(min(n_steps - 1, NS - 2));
+  lds_barrier();
+  f32x4 sc[2][2];
+  scores(0, sc);
+  for (int j = 0; j < n_steps; ++j) {
+    const int jn = min(j + 1, n_steps - 1);   // the last iteration recomputes its own step's scores, unused
+    wait_groups_after<kPerStep>(max(0, min(n_steps - 2 - j, NS - 3)));
+    lds_barrier();   // step j + 1 is in LDS for every wave; step j - 1 is done
+    if (j + NS - 1 < n_steps) issue_step(j + NS - 1);
+    const uint8_t* pg0 = ring[j % NS][0];
+    const uint8_t* pg1 = ring[j % NS][1];
+    const int tok0 = (pg_lo + 2 * j) * 16;
 
-    // ---- O^T += V^T . P^T; V of tokens outside the union range is zeroed
-    uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
-    if (tok_page0 < lo_first || tok_page0 + 15 > p_last) {
-      auto in = [&](int t) { return t >= lo_first && t <= p_last; };
-      vm0 = (in(tok0) ? 0x0000ffffu : 0u) | (in(tok0 + 1) ? 0xffff0000u : 0u);
-      vm1 = (in(tok0 + 2) ? 0x0000ffffu : 0u) | (in(tok0 + 3) ? 0xffff0000u : 0u);
-    }
-    uint2 vf[16];
+    // ---- scaled scores z; a step inside every row's window and the rows'
+    // range (the common case) takes no masks (rows past the block's last
+    // compute on its last row's q and are not written)
+    const bool full = tok0 >= lo_max && tok0 + 31 <= p_min;
+    float z[2][8];
+    if (full) {
 #pragma unroll
-    for (int b = 0; b < 16; ++b) vf[b] = LH::v_frag(pg, 16 * b + l16, gq);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[qb][i] = sc[i >> 2][qb][i & 3] * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // this query vector's keys, relative to the step: [lo, hi] (empty past r_last)
+        const int lo = rok[qb] ? loq[qb] - tok0 : 64;
+        const int hi = pq[qb] - tok0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int t = 16 * (i >> 2) + 4 * gq + (i & 3);
+          z[qb][i] = ((t >= lo) & (t <= hi)) ? sc[i >> 2][qb][i & 3] * a.scale_log2 : -INFINITY;
+        }
+      }
+    }
+    // The reference max moves only when a score passes it by more than
+    // kLazyMax (weights then stay below 2^kLazyMax), so the accumulators --
+    // in AGPRs -- are rescaled rarely after the first step; whether any
+    // lane needs it is known from its own eight scores, and only then are
+    // the row maxima formed across the four lanes of each query vector.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = fmaxf(fmaxf(fmaxf(z[qb][0], z[qb][1]), fmaxf(z[qb][2], z[qb][3])),
+                       fmaxf(fmaxf(z[qb][4], z[qb][5]), fmaxf(z[qb][6], z[qb][7])));
+      if (__any(mx > m_run[qb] + kLazyMax)) {
+        mx = max_lanes_xor16_32(mx);
+        const bool up = mx > m_run[qb] + kLazyMax;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.f;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) acc[qb][b] *= alpha;
+        lacc[qb] *= alpha;
+        m_run[qb] = up ? mx : m_run[qb];
+      }
+    }
+    const bool edge = tok0 < lo_first || tok0 + 31 > p_last;
+
+    // ---- from here on one block without branches, so that the next
+    // step's score MFMAs interleave with this step's weights (VALU) and V
+    // reads (LDS).  A query vector with no key yet has m = -inf and only
+    // -inf scores: its reference is taken as 0 so that its weights are 0.
+    f32x4 sn[2][2];
+    scores(jn, sn);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mref = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      uint32_t pw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pw[k] = pack_bf16(__builtin_amdgcn_exp2f(z[qb][2 * k] - mref), __builtin_amdgcn_exp2f(z[qb][2 * k + 1] - mref));
+      pb[qb] = __builtin_bit_cast(bf16x8, uint4{pw[0], pw[1], pw[2], pw[3]});
+      // l += the rounded weights, summed over the 32 tokens by MFMA (ones . P^T)
+      lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[qb], lacc[qb], 0, 0, 0);
+    }
+    uint4 vf[16];
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
-      uint2 vv = vf[b];
-      vv.x &= vm0;
-      vv.y &= vm1;
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+      const uint2 v0 = LH::v_frag(pg0, 16 * b + l16, gq), v1 = LH::v_frag(pg1, 16 * b + l16, gq);
+      vf[b] = uint4{v0.x, v0.y, v1.x, v1.y};
     }
+
+    // ---- O^T += V^T . P^T over the 32 tokens: lane (l16, gq) gives dim
+    // 16 b + l16 of the same eight tokens.  At the union range's edges V of
+    // tokens outside it (slots that may never have been written) is zeroed.
+    if (edge) {
+      uint32_t vm[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = tok0 + 16 * (k >> 1) + 4 * gq + 2 * (k & 1);
+        vm[k] = ((t >= lo_first && t <= p_last) ? 0x0000ffffu : 0u) |
+                ((t + 1 >= lo_first && t + 1 <= p_last) ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int b = 0; b < 16; ++b) vf[b] = uint4{vf[b].x & vm[0], vf[b].y & vm[1], vf[b].z & vm[2], vf[b].w & vm[3]};
+    }
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        acc[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[b]), pb[qb], acc[qb][b], 0, 0, 0);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sc[tb][qb] = sn[tb][qb];
   }
 
-  // ---- write: lane holds query vector l16, dims 16 b + 4 gq .. +3
-  const float l_tot = sum_lanes_xor16_32(l_run);
-  if (!row_ok) return;
-  float* op = a.out + ((int64_t)(row0 + r) * a.num_q_heads + gk * G + hq) * 256 + 4 * gq;
-  const float inv = 1.f / l_tot;
+  // ---- write: lane holds query vector l16 of each block, dims 16 b + 4 gq .. +3
 #pragma unroll
-  for (int b = 0; b < 16; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = lacc[qb][0];
+    if (!rok[qb]) continue;
+    const int v = 32 * w + 16 * qb + l16;
+    float* op = a.out + ((int64_t)(row0 + r_first + v / G) * a.num_q_heads + gk * G + v % G) * 256 + 4 * gq;
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[qb][b] * inv;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int max_q_len,
                                 hipStream_t stream) {
-  const int rows_per_wg = 64 / group;
-  dim3 grid(a.num_seqs, a.num_kv_heads, (max_q_len + rows_per_wg - 1) / rows_per_wg), block(256);
-#define GW_PREFILL_CASE(G_, F_) \
-  if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 4>), grid, block, 0, stream, a); return hipGetLastError(); }
+  // items: (prompt sequence, row block); sum over sequences of
+  // ceil(q_len / rows) is at most (rows + sequences * (rows - 1)) / rows
+  auto items = [&](int rows) {
+    const int64_t by_rows = ((int64_t)a.num_rows + (int64_t)a.num_seqs * (rows - 1)) / rows;
+    const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + rows - 1) / rows);
+    return (unsigned)(by_rows < by_len ? by_rows : by_len);
+  };
+#define GW_PREFILL_CASE(G_, F_)                                                                     \
+  if (group == G_ && fp8 == F_) {                                                                   \
+    const unsigned n = items(prefill_rows_per_wg<G_>());                                            \
+    if (n == 0) return hipSuccess;                                                                  \
+    if (n > 65535) return hipErrorInvalidConfiguration;                                             \
+    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 5>), dim3(a.num_kv_heads, n), dim3(256), 0, stream, a); \
+    return hipGetLastError();                                                                       \
+  }
   GW_PREFILL_CASE(1, false) GW_PREFILL_CASE(2, false) GW_PREFILL_CASE(4, false)
   GW_PREFILL_CASE(1, true) GW_PREFILL_CASE(2, true) GW_PREFILL_CASE(4, true)
 #undef GW_PREFILL_CASE
