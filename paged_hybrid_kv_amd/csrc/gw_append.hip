@@ -148,30 +148,57 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------ rows of an attention call
-// One workgroup per (sequence, page of its rows' range[, KV head]): the
-// rows' own tokens that fall in that page are rotated and stored with whole
-// 16-byte units where the unit's tokens are all rows (everywhere but at the
-// ends of a range), so a page of prompt rows is written with coalesced
-// stores, and the page lookup is made once per page.  Row r of sequence s
-// is at position seq_lens[s] - q_len + r (the attention calls' rows); one-
-// row sequences are skipped when skip_single is set (their decode kernel
-// appends them).  The arithmetic is the per-token kernels' exactly.
+// One workgroup per (sequence, page of its rows' range[, KV head]), the
+// (sequence, page) pairs numbered compactly: the rows' own tokens that fall
+// in that page are rotated and stored with whole 16-byte units where the
+// unit's tokens are all rows (everywhere but at the ends of a range), so a
+// page of prompt rows is written with coalesced stores, and the page lookup
+// is made once per page.  Row r of sequence s is at position
+// seq_lens[s] - q_len + r (the attention calls' rows); one-row sequences
+// are skipped when skip_single is set (their decode kernel appends them).
+// The arithmetic is the per-token kernels' exactly.
 struct RowsPage {
   int r0, p0, pg, t0, t1, page;   // first row and its position, page index, slots [t0, t1], physical page
 };
 
-__device__ __forceinline__ bool rows_page(const AppendArgs& a, int s, int j, RowsPage& rp) {
-  rp.r0 = a.q_indptr ? a.q_indptr[s] : s;
-  const int ql = a.q_indptr ? a.q_indptr[s + 1] - rp.r0 : 1;
-  if (ql <= 0 || (a.skip_single && ql == 1)) return false;
-  const int L = a.seq_lens[s];
-  rp.p0 = L - ql;
-  rp.pg = (rp.p0 >> 4) + j;
-  if (rp.pg * kPage > L - 1) return false;
-  rp.t0 = max(rp.p0 - rp.pg * kPage, 0);
-  rp.t1 = min(L - 1 - rp.pg * kPage, kPage - 1);
-  rp.page = a.page_table[(int64_t)s * a.pt_stride + rp.pg];
-  return true;
+// Work item `item` of a rows call: the call's (sequence, page of its rows'
+// range) pairs, numbered sequence by sequence (wave 0's lanes scan 64
+// sequences at a time).  False when item is past the last pair.
+__device__ __forceinline__ bool rows_page(const AppendArgs& a, int item, RowsPage& rp) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c = 0; c < a.num_seqs; c += 64) {
+    const int sl = c + lane;
+    int cnt = 0, r0 = 0, ql = 0, L = 0;
+    if (sl < a.num_seqs) {
+      r0 = a.q_indptr ? a.q_indptr[sl] : sl;
+      ql = a.q_indptr ? a.q_indptr[sl + 1] - r0 : 1;
+      L = a.seq_lens[sl];
+      if (ql > 0 && !(a.skip_single && ql == 1)) cnt = ((L - 1) >> 4) - ((L - ql) >> 4) + 1;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d, 64);
+      incl += lane >= d ? up : 0;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (item < base + total) {
+      const int ls = __builtin_ctzll(__ballot(base + incl > item));
+      const int s = c + ls;
+      const int j = item - (base + __builtin_amdgcn_readlane(incl, ls) - __builtin_amdgcn_readlane(cnt, ls));
+      rp.r0 = __builtin_amdgcn_readlane(r0, ls);
+      const int Ls = __builtin_amdgcn_readlane(L, ls);
+      rp.p0 = Ls - __builtin_amdgcn_readlane(ql, ls);
+      rp.pg = (rp.p0 >> 4) + j;
+      rp.t0 = max(rp.p0 - rp.pg * kPage, 0);
+      rp.t1 = min(Ls - 1 - rp.pg * kPage, kPage - 1);
+      rp.page = a.page_table[(int64_t)s * a.pt_stride + rp.pg];
+      return true;
+    }
+    base += total;
+  }
+  return false;
 }
 
 template <int N>
@@ -199,9 +226,9 @@ __global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
   constexpr int kU = FP8 ? 4 : 8;            // K units per quarter (and V units per 64 lanes... rows)
   constexpr int kT = FP8 ? 4 : 2;            // slots per V unit
   constexpr int kVOff = FP8 ? 4096 : 8192;
-  const int s = blockIdx.x, h = blockIdx.z, tid = threadIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x;
   RowsPage rp;
-  if (!rows_page(a, s, blockIdx.y, rp)) return;
+  if (!rows_page(a, blockIdx.x, rp)) return;
   uint8_t* hb = a.pool + (int64_t)rp.page * a.page_bytes + (int64_t)h * a.head_bytes;
   auto row_src = [&](int t) __attribute__((always_inline)) {   // element offset of slot t's K / V
     return ((int64_t)(rp.r0 + rp.pg * kPage + t - rp.p0) * a.num_kv_heads + h) * 256;
@@ -297,9 +324,9 @@ __global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
 // record's K block repeats V's chunks 16 .. 63.
 template <bool COMPRESSED>
 __global__ __launch_bounds__(256) void append_global_rows_kernel(AppendArgs a) {
-  const int s = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   RowsPage rp;
-  if (!rows_page(a, s, blockIdx.y, rp)) return;
+  if (!rows_page(a, blockIdx.x, rp)) return;
   uint8_t* pb = a.pool + (int64_t)rp.page * a.page_bytes;
   uint8_t* vblock = COMPRESSED ? pb : pb + 16384;
   uint8_t* kblock = COMPRESSED ? pb + 16384 : pb;
@@ -337,10 +364,20 @@ hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int ro
   return hipGetLastError();
 }
 
+// Items of a rows call: a sequence of q rows touches at most
+// (q + 14) / 16 + 1 pages, so the call at most (rows + 30 sequences) / 16
+// (and at most sequences * pages of max_q_len).
+static int64_t rows_items(const AppendArgs& a, int max_q_len) {
+  const int64_t by_rows = ((int64_t)a.n_tok + 30LL * a.num_seqs) / kPage;
+  const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + 14) / kPage + 1);
+  return by_rows < by_len ? by_rows : by_len;
+}
+
 hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream) {
-  const int pages = (max_q_len + 14) / kPage + 1;   // pages a range of max_q_len tokens can touch
-  if (pages > 65535) return launch_append_local(a, fp8, rope, stream);
-  dim3 grid(a.num_seqs, pages, a.num_kv_heads), block(256);
+  const int64_t items = rows_items(a, max_q_len);
+  if (items == 0) return hipSuccess;
+  if (items > 0x7fffffff || a.num_kv_heads > 65535) return launch_append_local(a, fp8, rope, stream);
+  dim3 grid((unsigned)items, a.num_kv_heads), block(256);
   if (fp8) {
     if (rope) hipLaunchKernelGGL((append_local_rows_kernel<true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((append_local_rows_kernel<true, false>), grid, block, 0, stream, a);
@@ -352,9 +389,10 @@ hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, in
 }
 
 hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
-  const int pages = (max_q_len + 14) / kPage + 1;
-  if (pages > 65535) return launch_append_global(a, compressed, stream);
-  dim3 grid(a.num_seqs, pages), block(256);
+  const int64_t items = rows_items(a, max_q_len);
+  if (items == 0) return hipSuccess;
+  if (items > 0x7fffffff) return launch_append_global(a, compressed, stream);
+  dim3 grid((unsigned)items), block(256);
   if (compressed) hipLaunchKernelGGL((append_global_rows_kernel<true>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((append_global_rows_kernel<false>), grid, block, 0, stream, a);
   return hipGetLastError();
