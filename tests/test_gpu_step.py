@@ -1,0 +1,106 @@
+"""The 60-layer hybrid step at full size, in the launch configuration that
+bench.py times (one HIP graph of every layer's attention call, each call
+appending its rows' own tokens first), checked on sampled rows against the
+CPU oracle.
+
+Workload: 16 decode slots with seeded contexts in [2048, 8192] plus 4 new
+512-token prompts (pegainfer "Gemma 4" page, Scheduling: a new prompt's rows
+are computed in the same step as the live streams' next token).  The oracle
+sees only the seeded draws of the layer (q, the step's new K/V and the prior
+context K/V, all bf16) and rotates and rounds them itself; no value comes
+from the GPU path.  After a replay the step's output buffers hold the last
+local layer's and the last global layer's outputs; those are compared on a
+sample of decode rows and prompt rows (first, last, and rows on both sides
+of a page edge).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from oracle import codecs as OC
+from oracle import rope as OR
+from tests.oracle_side import compare
+
+pytestmark = pytest.mark.gpu
+
+# decode slots and (prompt, row) pairs sampled from the step
+DECODE_SAMPLE = [0, 3, 8, 15]
+PROMPT_SAMPLE = [(0, 0), (0, 15), (0, 16), (0, 511), (2, 200), (3, 383)]
+
+
+def _host(t):
+    import torch
+    return None if t is None else t.to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def _sequence_kv(st, layer: int, s: int):
+    """Oracle K, V [L][Hkv][D] of sequence s in layer `layer` (NaN where the
+    step's pool holds no token) and the oracle q rows of s."""
+    from paged_hybrid_kv_amd.synth import layer_draws, step_tokens
+    sh = st.shape
+    local = not sh.is_global(layer)
+    d = layer_draws(sh, layer, True, "cuda")
+    new_s, new_p, pri_s, pri_p = step_tokens(sh, True, local)
+    L = int(st.lens[s])
+    sel_new, sel_pri = new_s == s, pri_s == s
+    pos = np.concatenate([pri_p[sel_pri], new_p[sel_new]])
+    v = OC.bf16_round(np.concatenate([_host(d.v_prior)[sel_pri], _host(d.v_new)[sel_new]]))
+    if local:
+        k = OC.bf16_round(np.concatenate([_host(d.k_prior)[sel_pri], _host(d.k_new)[sel_new]]))
+        k = OC.bf16_round(OR.rotate_local(k, pos[:, None]))
+        K = np.full((L,) + k.shape[1:], np.nan)
+        V = np.full((L,) + v.shape[1:], np.nan)
+    else:
+        k_rot = OC.bf16_round(OR.rotate_global(v, pos)[:, :128])
+        k = OA.k_from_compressed(v, k_rot)[:, None, :]
+        v = v[:, None, :]
+        K = np.full((L, 1, 512), np.nan)
+        V = np.full((L, 1, 512), np.nan)
+    K[pos] = k
+    V[pos] = v
+    indptr = np.concatenate([[0], np.cumsum(st.q_len)])
+    q = OC.bf16_round(_host(d.q)[indptr[s]:indptr[s + 1]])
+    return K, V, q, int(indptr[s])
+
+
+def _check_layer(st, layer: int, out):
+    sh = st.shape
+    local = not sh.is_global(layer)
+    window = sh.window if local else None
+    D = sh.local_head_dim if local else sh.global_head_dim
+    scale = 1.0 / np.sqrt(D)
+    gpu = out.cpu().numpy()
+    picks = {}
+    for s in DECODE_SAMPLE:
+        picks.setdefault(s, []).append(0)
+    for i, r in PROMPT_SAMPLE:
+        picks.setdefault(sh.decode_slots + i, []).append(r)
+    worst = 0.0
+    for s, rows in picks.items():
+        K, V, q, row0 = _sequence_kv(st, layer, s)
+        L, ql = int(st.lens[s]), int(st.q_len[s])
+        rows = np.array(sorted(set(rows)))
+        ref = OA.attend(q[rows], K, V, L - ql + rows, scale, window)
+        mx, _, _ = compare(gpu[row0 + rows], ref, f"layer {layer} seq {s} rows {list(rows)}")
+        worst = max(worst, mx)
+    return worst
+
+
+def test_hybrid_step_graph_sampled_parity():
+    import torch
+    from paged_hybrid_kv_amd.step import HybridStep
+    st = HybridStep(with_prompts=True)
+    st.capture()
+    for _ in range(2):
+        st.replay()
+    torch.cuda.synchronize()
+    sh = st.shape
+    last_local = max(l for l in range(sh.num_layers) if not sh.is_global(l))
+    last_global = max(l for l in range(sh.num_layers) if sh.is_global(l))
+    e_loc = _check_layer(st, last_local, st.out_local)
+    e_glob = _check_layer(st, last_global, st.out_global)
+    print(f"hybrid step: layer {last_local} (local) max abs err {e_loc:.2e}, "
+          f"layer {last_global} (global) max abs err {e_glob:.2e}", flush=True)
