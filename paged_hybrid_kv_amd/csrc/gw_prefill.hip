@@ -81,6 +81,27 @@ struct LocalHead {
                                               e4m3x2_to_bf16x2<false>(w.y), e4m3x2_to_bf16x2<true>(w.y)});
     }
   }
+  // Zero, in the LDS copies of a step's two pages, V of every slot whose
+  // token (tok0 + slot, page 1 from tok0 + 16) lies outside [lo, hi];
+  // thread tid of 256 takes one dim (bf16) or one dword of codes (e4m3).
+  __device__ static __forceinline__ void zero_v_outside(uint8_t* pg0, uint8_t* pg1, int tok0, int lo, int hi,
+                                                        int tid) {
+    for (int t = 0; t < 32; ++t) {
+      const int pos = tok0 + t;
+      if (pos >= lo && pos <= hi) continue;
+      uint8_t* vb = (t < 16 ? pg0 : pg1) + kVOff;
+      const int slot = t & 15;
+      if constexpr (!FP8) {
+        const int u = slot >> 1;
+        const int d = tid;   // dim
+        reinterpret_cast<uint16_t*>(vb + u * 1024 + (d ^ (16 * ((u >> 1) & 3))) * 4)[slot & 1] = 0;
+      } else {
+        const int u = slot >> 2;   // quad of slots, dword per dim
+        const int d = tid;
+        vb[u * 1024 + d * 4 + (slot & 3)] = 0;
+      }
+    }
+  }
   // V^T operand: dim d, tokens 4 gq .. 4 gq + 3, as 4 bf16 (two dwords)
   __device__ static __forceinline__ uint2 v_frag(const uint8_t* pg, int d, int gq) {
     if constexpr (!FP8) {
@@ -270,6 +291,13 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     const uint8_t* pg0 = ring[j % NS][0];
     const uint8_t* pg1 = ring[j % NS][1];
     const int tok0 = (pg_lo + 2 * j) * 16;
+    // At the union range's edges, V of the step's tokens outside it (slots
+    // that may never have been written) is zeroed in LDS before any wave
+    // reads it (its K was read a step earlier; those scores are masked).
+    if (tok0 < lo_first || tok0 + 31 > p_last) {
+      LH::zero_v_outside(ring[j % NS][0], ring[j % NS][1], tok0, lo_first, p_last, tid);
+      lds_barrier();
+    }
 
     // ---- scaled scores z; a step inside every row's window and the rows'
     // range (the common case) takes no masks (rows past the block's last
@@ -313,7 +341,6 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
         m_run[qb] = up ? mx : m_run[qb];
       }
     }
-    const bool edge = tok0 < lo_first || tok0 + 31 > p_last;
 
     // ---- from here on one block without branches, so that the next
     // step's score MFMAs interleave with this step's weights (VALU) and V
@@ -341,19 +368,7 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     }
 
     // ---- O^T += V^T . P^T over the 32 tokens: lane (l16, gq) gives dim
-    // 16 b + l16 of the same eight tokens.  At the union range's edges V of
-    // tokens outside it (slots that may never have been written) is zeroed.
-    if (edge) {
-      uint32_t vm[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = tok0 + 16 * (k >> 1) + 4 * gq + 2 * (k & 1);
-        vm[k] = ((t >= lo_first && t <= p_last) ? 0x0000ffffu : 0u) |
-                ((t + 1 >= lo_first && t + 1 <= p_last) ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int b = 0; b < 16; ++b) vf[b] = uint4{vf[b].x & vm[0], vf[b].y & vm[1], vf[b].z & vm[2], vf[b].w & vm[3]};
-    }
+    // 16 b + l16 of the same eight tokens
 #pragma unroll
     for (int b = 0; b < 16; ++b)
 #pragma unroll
