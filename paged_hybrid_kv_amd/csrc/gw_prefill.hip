@@ -11,7 +11,7 @@
 // With many rows per KV head the score and value steps are dense
 // contractions, so both run on MFMA over "query vectors" (a row and one head
 // of its group), 16 to a block: lane column l16 of block qb of wave w is
-// query vector v = 32 w + 16 qb + l16 (row r_first + v / G, head v % G).
+// query vector v = 16 QB w + 16 qb + l16 (row r_first + v / G, head v % G).
 // The keys go by in steps of 32 tokens (two pages):
 //   S^T (16 tokens x 16 q vectors) = K (16 x 256) . Q^T (256 x 16)
 //         -- v_mfma_f32_16x16x32_bf16, 8 steps, per page and query block
@@ -19,15 +19,19 @@
 //         -- v_mfma_f32_16x16x32_bf16, per 16-dim block and query block
 // where lane (l16, gq) holds the scores of tokens 4 gq .. +3 of each page,
 // which it also supplies as the PV step's k slots 8 gq .. +7, so P never
-// leaves the lane.  A workgroup (4 waves, 128 query vectors) takes 128 / G
-// consecutive rows of one (sequence, KV head) and streams the pages of
-// their union range, [max(0, p_first - W + 1), p_last], through an LDS ring
-// (direct global->LDS transfers, each wave moving a quarter of every page),
-// so K/V are read once per 128 query vectors.  Each lane masks its own
-// query vectors' windows; V of tokens outside the union range (slots that
-// may never have been written) is zeroed in the operand registers.  e4m3
-// codes convert to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), so
-// the products are the same as on the bf16 values.  P is rounded to bf16 for
+// leaves the lane.  A workgroup of 8 / QB waves (QB query blocks each; 128
+// query vectors in all) takes 128 / G consecutive rows of one (sequence,
+// KV head) and streams the pages of their union range,
+// [max(0, p_first - W + 1), p_last], through an LDS ring (direct
+// global->LDS transfers, every wave moving its share of every page), so K/V
+// are read once per 128 query vectors.  With one block per wave there are
+// two waves per SIMD, so one wave's weights (VALU) and reads (LDS) overlap
+// the other's products; that beats the halved LDS traffic of two blocks per
+// wave at one wave per SIMD.  Each lane masks its own query vectors'
+// windows; V of tokens outside the union range (slots that may never have
+// been written) is zeroed in LDS on the range's edge steps.  e4m3 codes
+// convert to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the
+// products are the same as on the bf16 values.  P is rounded to bf16 for
 // PV and the sum l adds exactly those rounded values.  Workgroups are
 // numbered compactly over the prompt sequences' row blocks, a sequence's
 // longest ranges first, with the KV head as the fastest index (so one
@@ -118,17 +122,24 @@ struct LocalHead {
 // max before the reference moves (so unnormalised weights stay <= 2^8).
 constexpr float kLazyMax = 8.f;
 
-// Rows of prompt per workgroup: 128 query vectors, 32 per wave.
+// Query blocks (16 query vectors) per wave: 8 / kPrefillQB waves per workgroup.
+#ifndef GW_PREFILL_QB
+#define GW_PREFILL_QB 1
+#endif
+constexpr int kPrefillQB = GW_PREFILL_QB;
+
+// Rows of prompt per workgroup: 128 query vectors.
 template <int G>
 constexpr int prefill_rows_per_wg() {
   return 128 / G;
 }
 
-template <int G, bool FP8, int NS>
-__global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) {
+template <int G, bool FP8, int NS, int QB>
+__global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAttnArgs a) {
   using LH = LocalHead<FP8>;
   constexpr int kUnits = LH::kBytes / 1024;    // 1 KiB transfer units per (page, head)
-  constexpr int kPerWavePage = kUnits / 4;     // units a wave moves of each page
+  constexpr int kWaves = 8 / QB;               // waves per workgroup, QB query blocks each
+  constexpr int kPerWavePage = kUnits / kWaves;   // units a wave moves of each page
   constexpr int kPerStep = 2 * kPerWavePage;   // transfers per wave per two-page step
   constexpr int kRows = prefill_rows_per_wg<G>();
   static_assert(NS >= 3 && NS - 2 <= 4 && kPerStep * (NS - 2) < 64, "ring depth");
@@ -200,12 +211,12 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
 
   // this lane's two query vectors, v = 32 w + 16 qb + l16: row
   // r_first + v / G, head v % G of the group; each masks its own window
-  int pq[2], loq[2];
-  bool rok[2];
-  bf16x8 qf[2][8];   // Q^T operand: dims 32 ks + 8 gq .. +7
+  int pq[QB], loq[QB];
+  bool rok[QB];
+  bf16x8 qf[QB][8];   // Q^T operand: dims 32 ks + 8 gq .. +7
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int v = 32 * w + 16 * qb + l16;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int v = 16 * QB * w + 16 * qb + l16;
     const int r = r_first + v / G;
     rok[qb] = r <= r_last;
     const int rr = rok[qb] ? r : r_last;
@@ -240,19 +251,24 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
   for (int j = 0; j < NS - 1; ++j)
     if (j < n_steps) issue_step(j);
 
-  f32x4 acc[2][16];
+  f32x4 acc[QB][16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int b = 0; b < 16; ++b) acc[qb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // l, in every element
+  float m_run[QB];
+  f32x4 lacc[QB];   // l, in every element
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const bf16x8 kOnes = __builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   // ---- S^T = K . Q^T for both pages (tb) and both query blocks (qb) of a
   // step in the ring: all 16 K fragments first, then four interleaved
   // accumulation chains
-  auto scores = [&](int j, f32x4 (&sc)[2][2]) __attribute__((always_inline)) {
+  auto scores = [&](int j, f32x4 (&sc)[2][QB]) __attribute__((always_inline)) {
     const uint8_t* pg0 = ring[j % NS][0];
     const uint8_t* pg1 = ring[j % NS][1];
     bf16x8 kf[2][8];
@@ -264,13 +280,13 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sc[tb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb) sc[tb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
           sc[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tb][ks], qf[qb][ks], sc[tb][qb], 0, 0, 0);
   };
 
@@ -281,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
   // slot is refilled once every wave is past iteration j - 1.
   wait_groups_after<kPerStep>(min(n_steps - 1, NS - 2));
   lds_barrier();
-  f32x4 sc[2][2];
+  f32x4 sc[2][QB];
   scores(0, sc);
   for (int j = 0; j < n_steps; ++j) {
     const int jn = min(j + 1, n_steps - 1);   // the last iteration recomputes its own step's scores, unused
@@ -295,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     // that may never have been written) is zeroed in LDS before any wave
     // reads it (its K was read a step earlier; those scores are masked).
     if (tok0 < lo_first || tok0 + 31 > p_last) {
-      LH::zero_v_outside(ring[j % NS][0], ring[j % NS][1], tok0, lo_first, p_last, tid);
+      if (tid < 256) LH::zero_v_outside(ring[j % NS][0], ring[j % NS][1], tok0, lo_first, p_last, tid);
       lds_barrier();
     }
 
@@ -303,15 +319,15 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     // range (the common case) takes no masks (rows past the block's last
     // compute on its last row's q and are not written)
     const bool full = tok0 >= lo_max && tok0 + 31 <= p_min;
-    float z[2][8];
+    float z[QB][8];
     if (full) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) z[qb][i] = sc[i >> 2][qb][i & 3] * a.scale_log2;
     } else {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         // this query vector's keys, relative to the step: [lo, hi] (empty past r_last)
         const int lo = rok[qb] ? loq[qb] - tok0 : 64;
         const int hi = pq[qb] - tok0;
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     // lane needs it is known from its own eight scores, and only then are
     // the row maxima formed across the four lanes of each query vector.
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = fmaxf(fmaxf(fmaxf(z[qb][0], z[qb][1]), fmaxf(z[qb][2], z[qb][3])),
                        fmaxf(fmaxf(z[qb][4], z[qb][5]), fmaxf(z[qb][6], z[qb][7])));
       if (__any(mx > m_run[qb] + kLazyMax)) {
@@ -346,11 +362,11 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
     // step's score MFMAs interleave with this step's weights (VALU) and V
     // reads (LDS).  A query vector with no key yet has m = -inf and only
     // -inf scores: its reference is taken as 0 so that its weights are 0.
-    f32x4 sn[2][2];
+    f32x4 sn[2][QB];
     scores(jn, sn);
-    bf16x8 pb[2];
+    bf16x8 pb[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const float mref = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       uint32_t pw[4];
 #pragma unroll
@@ -372,20 +388,20 @@ __global__ __launch_bounds__(256, 1) void local_prefill_kernel(LocalAttnArgs a) 
 #pragma unroll
     for (int b = 0; b < 16; ++b)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
         acc[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[b]), pb[qb], acc[qb][b], 0, 0, 0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sc[tb][qb] = sn[tb][qb];
+      for (int qb = 0; qb < QB; ++qb) sc[tb][qb] = sn[tb][qb];
   }
 
   // ---- write: lane holds query vector l16 of each block, dims 16 b + 4 gq .. +3
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = lacc[qb][0];
     if (!rok[qb]) continue;
-    const int v = 32 * w + 16 * qb + l16;
+    const int v = 16 * QB * w + 16 * qb + l16;
     float* op = a.out + ((int64_t)(row0 + r_first + v / G) * a.num_q_heads + gk * G + v % G) * 256 + 4 * gq;
     const float inv = 1.f / l_tot;
 #pragma unroll
@@ -409,7 +425,7 @@ hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int
     const unsigned n = items(prefill_rows_per_wg<G_>());                                            \
     if (n == 0) return hipSuccess;                                                                  \
     if (n > 65535) return hipErrorInvalidConfiguration;                                             \
-    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 5>), dim3(a.num_kv_heads, n), dim3(256), 0, stream, a); \
+    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 5, kPrefillQB>), dim3(a.num_kv_heads, n), dim3(64 * (8 / kPrefillQB)), 0, stream, a); \
     return hipGetLastError();                                                                       \
   }
   GW_PREFILL_CASE(1, false) GW_PREFILL_CASE(2, false) GW_PREFILL_CASE(4, false)
