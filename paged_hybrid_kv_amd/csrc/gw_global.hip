@@ -75,7 +75,7 @@ struct GlobalPage {
 // into the wave's output-dim slice.  pg: the page in LDS; tok_page0: the
 // position of the page's first token; p: the row's position (tokens past it
 // are masked, and their V zeroed, so unwritten slots never reach the output).
-template <bool COMPRESSED, int HB>
+template <bool COMPRESSED, int HB, bool LAZY = false>
 __device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
                                                  const uint8_t* pg, const bf16x8 (&qf)[16],
                                                  int tok_page0, int p, int g, int l16, int v_lane_off,
@@ -103,14 +103,27 @@ __device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_
 #pragma unroll
   for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * scale_log2 : -INFINITY;
   const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-  const float mnew = fmaxf(m_run, mx);
-  if (__any(mnew > m_run)) {
-    const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+  if constexpr (LAZY) {
+    // the reference max moves only when a score passes it by more than
+    // 2^8 (the weights then stay below 2^8), so rescales are rare
+    if (__any(mx > m_run + 8.f)) {
+      const bool up = mx > m_run + 8.f;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
-    l_run *= alpha;
+      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
+      l_run *= alpha;
+      m_run = up ? mx : m_run;
+    }
+  } else {
+    const float mnew = fmaxf(m_run, mx);
+    if (__any(mnew > m_run)) {
+      const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
+      l_run *= alpha;
+    }
+    m_run = mnew;
   }
-  m_run = mnew;
   const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
   const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
   l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
     lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
     if (i + NS - 1 < n) issue_page(i + NS - 1);
     if (row_ok && i * 16 <= p)
-      global_page_step<COMPRESSED, HB>(acc, m_run, l_run, ring[i % NS], qf, i * 16, p, g, l16, v_lane_off,
+      global_page_step<COMPRESSED, HB, true>(acc, m_run, l_run, ring[i % NS], qf, i * 16, p, g, l16, v_lane_off,
                                        a.scale_log2);
   }
   if (!row_ok) return;
