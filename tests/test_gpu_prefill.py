@@ -227,3 +227,61 @@ def test_global_decode_in_call_append_one_row_per_sequence():
     torch.cuda.synchronize()
     assert torch.equal(dc_f.pool.buf, dc_sep.pool.buf)
     assert np.array_equal(out_f, out_sep)
+
+
+# ------------------------------------------------------- many sequences --
+def _many_seqs(seed, n=150, max_len=300):
+    """n sequences (several 64-sequence chunks of the kernels' work scans),
+    most of them decode rows, every fifth a prompt of 2..40 rows, some
+    prompts starting mid-sequence."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(20, max_len, size=n)
+    q_len = np.ones(n, dtype=np.int64)
+    q_len[::5] = rng.integers(2, 41, size=q_len[::5].shape[0])
+    q_len = np.minimum(q_len, lens)
+    return lens, q_len
+
+
+def test_local_many_sequences_in_call_append():
+    """150 sequences mixing decode and prompt rows, every row's token
+    appended in the call: all rows against the oracle, and the pool and the
+    outputs equal to a standalone append followed by the call."""
+    lens, q_len = _many_seqs(120)
+    case = SY.local_case("many local", 121, lens, window=64, num_q_heads=4, num_kv_heads=2,
+                         q_len=q_len, rope=True, q_scale=0.5, kv_scale=0.5)
+    dc_sep = RT.upload_local(case)
+    out_sep = RT.attend(dc_sep).cpu().numpy()
+    check(case, out_sep, "many local")
+    is_row = np.zeros(case.tok_seq.shape[0], bool)
+    for s, (L, ql) in enumerate(zip(lens, q_len)):
+        is_row |= (case.tok_seq == s) & (case.tok_pos >= L - ql)
+    c2 = copy.copy(case)
+    c2.k, c2.v = case.k[~is_row], case.v[~is_row]
+    c2.tok_seq, c2.tok_pos = case.tok_seq[~is_row], case.tok_pos[~is_row]
+    dc_f = RT.upload_local(c2)
+    k_new, v_new = RT.to_bf16_dev(case.k[is_row]), RT.to_bf16_dev(case.v[is_row])
+    rope_t = RT.rope_tables(int(max(lens)), 256, 256, RT.LOCAL_THETA)
+    out_f = RT.attend(dc_f, k_new=k_new, v_new=v_new, rope=rope_t).cpu().numpy()
+    torch.cuda.synchronize()
+    assert torch.equal(dc_f.pool.buf, dc_sep.pool.buf), "pool bytes differ"
+    assert np.array_equal(out_f, out_sep)
+
+
+def test_global_many_sequences_in_call_append():
+    lens, q_len = _many_seqs(130, max_len=400)
+    case = SY.global_case("many global", 131, lens, num_q_heads=16, q_len=q_len, rope=True)
+    dc_sep, out_sep = run_global(case)
+    check(case, out_sep, "many global")
+    is_row = np.zeros(case.tok_seq.shape[0], bool)
+    for s, (L, ql) in enumerate(zip(lens, q_len)):
+        is_row |= (case.tok_seq == s) & (case.tok_pos >= L - ql)
+    c2 = copy.copy(case)
+    c2.v = case.v[~is_row]
+    c2.tok_seq, c2.tok_pos = case.tok_seq[~is_row], case.tok_pos[~is_row]
+    dc_f = RT.upload_global(c2, compressed=True)
+    v_new = RT.to_bf16_dev(case.v[is_row])
+    rope_t = RT.rope_tables(int(max(lens)), 128, 512, RT.GLOBAL_THETA)
+    out_f = RT.attend(dc_f, v_new=v_new, rope=rope_t).cpu().numpy()
+    torch.cuda.synchronize()
+    assert torch.equal(dc_f.pool.buf, dc_sep.pool.buf), "pool bytes differ"
+    assert np.array_equal(out_f, out_sep)
