@@ -220,39 +220,90 @@ __device__ __forceinline__ void load_bf16_n(const uint16_t* p, float (&x)[N]) {
 // quarters c and c + 2 are rotation partners, so thread (t, k, c < 2)
 // makes both.  V unit (u, l) (16 bytes at (u*64 + l)*16 of the V block)
 // holds dims 4l .. 4l+3 of slots T u .. T u + T-1 (T = 2 bf16 / 4 e4m3).
+// A workgroup takes kRowsHeads KV heads of its page: every head's inputs
+// are loaded first, in one round trip, and the rotary factors of a slot
+// (the same for every head) once.
+constexpr int kRowsHeads = 4;
+
 template <bool FP8, bool ROPE>
 __global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
   constexpr int kW = FP8 ? 16 : 8;           // dims per K unit
-  constexpr int kU = FP8 ? 4 : 8;            // K units per quarter (and V units per 64 lanes... rows)
+  constexpr int kU = FP8 ? 4 : 8;            // K units per quarter
   constexpr int kT = FP8 ? 4 : 2;            // slots per V unit
   constexpr int kVOff = FP8 ? 4096 : 8192;
-  const int h = blockIdx.y, tid = threadIdx.x;
+  constexpr int kVUnits = (kPage / kT) * 64;          // V units per (page, head)
+  constexpr int kVPer = (kVUnits + 255) / 256;        // V units per thread
+  const int h0 = blockIdx.y * kRowsHeads, tid = threadIdx.x;
   RowsPage rp;
   if (!rows_page(a, blockIdx.x, rp)) return;
-  uint8_t* hb = a.pool + (int64_t)rp.page * a.page_bytes + (int64_t)h * a.head_bytes;
-  auto row_src = [&](int t) __attribute__((always_inline)) {   // element offset of slot t's K / V
+  auto row_src = [&](int t, int h) __attribute__((always_inline)) {   // element offset of slot t's K / V
     return ((int64_t)(rp.r0 + rp.pg * kPage + t - rp.p0) * a.num_kv_heads + h) * 256;
   };
-  if (tid < kPage * kU * 2) {
-    const int t = tid / (kU * 2), k = (tid >> 1) % kU, c = tid & 1;
-    if (t >= rp.t0 && t <= rp.t1) {
-      const int64_t src = row_src(t);
-      const int d = 64 * c + kW * k;
-      float xa[kW], xb[kW], ya[kW], yb[kW];
-      load_bf16_n<kW>(a.k_raw + src + d, xa);
-      load_bf16_n<kW>(a.k_raw + src + d + 128, xb);
-      if constexpr (ROPE) {
-        const float* cp = a.rope_cos + (int64_t)(rp.pg * kPage + t) * 128 + d;
-        const float* sp = a.rope_sin + (int64_t)(rp.pg * kPage + t) * 128 + d;
+  // K role of this thread: slot t, unit k, quarter pair c
+  const int t = tid / (kU * 2), k = (tid >> 1) % kU, c = tid & 1;
+  const bool k_on = tid < kPage * kU * 2 && t >= rp.t0 && t <= rp.t1;
+  const int d = 64 * c + kW * k;
+  float cs[kW], sn[kW];
+  if (ROPE && k_on) {
+    const float* cp = a.rope_cos + (int64_t)(rp.pg * kPage + t) * 128 + d;
+    const float* sp = a.rope_sin + (int64_t)(rp.pg * kPage + t) * 128 + d;
 #pragma unroll
-        for (int e = 0; e < kW; e += 4) {
-          const float4 cs = *reinterpret_cast<const float4*>(cp + e);
-          const float4 sn = *reinterpret_cast<const float4*>(sp + e);
-          rope_pair(xa[e], xb[e], cs.x, sn.x, ya[e], yb[e]);
-          rope_pair(xa[e + 1], xb[e + 1], cs.y, sn.y, ya[e + 1], yb[e + 1]);
-          rope_pair(xa[e + 2], xb[e + 2], cs.z, sn.z, ya[e + 2], yb[e + 2]);
-          rope_pair(xa[e + 3], xb[e + 3], cs.w, sn.w, ya[e + 3], yb[e + 3]);
+    for (int e = 0; e < kW; e += 4) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cp + e);
+      const float4 s4 = *reinterpret_cast<const float4*>(sp + e);
+      cs[e] = c4.x; cs[e + 1] = c4.y; cs[e + 2] = c4.z; cs[e + 3] = c4.w;
+      sn[e] = s4.x; sn[e + 1] = s4.y; sn[e + 2] = s4.z; sn[e + 3] = s4.w;
+    }
+  }
+  // ---- every head's raw inputs
+  uint4 kra[kRowsHeads][kW / 8], krb[kRowsHeads][kW / 8];
+  uint2 vr[kRowsHeads][kVPer][kT];
+#pragma unroll
+  for (int i = 0; i < kRowsHeads; ++i) {
+    const int h = h0 + i;
+    if (h >= a.num_kv_heads) break;
+    if (k_on) {
+      const uint16_t* kp = a.k_raw + row_src(t, h) + d;
+#pragma unroll
+      for (int q = 0; q < kW / 8; ++q) {
+        kra[i][q] = *reinterpret_cast<const uint4*>(kp + 8 * q);
+        krb[i][q] = *reinterpret_cast<const uint4*>(kp + 128 + 8 * q);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int un = tid + 256 * j, u = un >> 6, l = un & 63;
+#pragma unroll
+      for (int e = 0; e < kT; ++e) {
+        const int ts = kT * u + e;
+        const bool in = un < kVUnits && ts >= rp.t0 && ts <= rp.t1;
+        vr[i][j][e] = in ? *reinterpret_cast<const uint2*>(a.v + row_src(ts, h) + 4 * l) : uint2{0u, 0u};
+      }
+    }
+  }
+  // ---- rotate, round and store, head by head
+#pragma unroll
+  for (int i = 0; i < kRowsHeads; ++i) {
+    const int h = h0 + i;
+    if (h >= a.num_kv_heads) break;
+    uint8_t* hb = a.pool + (int64_t)rp.page * a.page_bytes + (int64_t)h * a.head_bytes;
+    if (k_on) {
+      float xa[kW], xb[kW], ya[kW], yb[kW];
+#pragma unroll
+      for (int q = 0; q < kW / 8; ++q) {
+        const uint32_t wa[4] = {kra[i][q].x, kra[i][q].y, kra[i][q].z, kra[i][q].w};
+        const uint32_t wb[4] = {krb[i][q].x, krb[i][q].y, krb[i][q].z, krb[i][q].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          xa[8 * q + 2 * m] = bf16_lo(wa[m]);
+          xa[8 * q + 2 * m + 1] = bf16_hi(wa[m]);
+          xb[8 * q + 2 * m] = bf16_lo(wb[m]);
+          xb[8 * q + 2 * m + 1] = bf16_hi(wb[m]);
         }
+      }
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int e = 0; e < kW; ++e) rope_pair(xa[e], xb[e], cs[e], sn[e], ya[e], yb[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < kW; ++e) { ya[e] = xa[e]; yb[e] = xb[e]; }
@@ -278,40 +329,41 @@ __global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
       *reinterpret_cast<uint4*>(hb + ((k * kPage + t) * 4 + c) * 16) = ua;
       *reinterpret_cast<uint4*>(hb + ((k * kPage + t) * 4 + c + 2) * 16) = ub;
     }
-  }
-  // V: kPage / kT x 64 units
-  for (int un = tid; un < (kPage / kT) * 64; un += 256) {
-    const int u = un >> 6, l = un & 63;
-    const int ta = kT * u;
-    if (ta + kT - 1 < rp.t0 || ta > rp.t1) continue;
-    uint32_t e[kT][4];   // element j of slot ta + i, as raw bits (bf16) / e4m3 code
+    // V: kPage / kT x 64 units
 #pragma unroll
-    for (int i = 0; i < kT; ++i) {
-      const int t = ta + i;
-      const bool in = t >= rp.t0 && t <= rp.t1;
-      const uint2 raw = in ? *reinterpret_cast<const uint2*>(a.v + row_src(t) + 4 * l) : uint2{0u, 0u};
-      const uint32_t b16[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
+    for (int j = 0; j < kVPer; ++j) {
+      const int un = tid + 256 * j;
+      if (un >= kVUnits) continue;
+      const int u = un >> 6;
+      const int ta = kT * u;
+      if (ta + kT - 1 < rp.t0 || ta > rp.t1) continue;
+      uint32_t ev[kT][4];   // element jj of slot ta + e, as raw bits (bf16) / e4m3 code
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) e[i][jj] = FP8 ? f32_to_e4m3(bits_to_f32(b16[jj] << 16)) : b16[jj];
-    }
-    uint8_t* ub = hb + kVOff + un * 16;
-    if (ta >= rp.t0 && ta + kT - 1 <= rp.t1) {   // the whole unit is rows of this call
-      uint32_t wv[4];
+      for (int e = 0; e < kT; ++e) {
+        const uint2 raw = vr[i][j][e];
+        const uint32_t b16[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if constexpr (!FP8) wv[jj] = e[0][jj] | (e[1][jj] << 16);
-        else wv[jj] = e[0][jj] | (e[1][jj] << 8) | (e[2][jj] << 16) | (e[3][jj] << 24);
+        for (int jj = 0; jj < 4; ++jj) ev[e][jj] = FP8 ? f32_to_e4m3(bits_to_f32(b16[jj] << 16)) : b16[jj];
       }
-      *reinterpret_cast<uint4*>(ub) = uint4{wv[0], wv[1], wv[2], wv[3]};
-    } else {                                     // an end of the range: element by element
-#pragma unroll
-      for (int i = 0; i < kT; ++i) {
-        const int t = ta + i;
-        if (t < rp.t0 || t > rp.t1) continue;
+      uint8_t* ub = hb + kVOff + un * 16;
+      if (ta >= rp.t0 && ta + kT - 1 <= rp.t1) {   // the whole unit is rows of this call
+        uint32_t wv[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          if constexpr (!FP8) reinterpret_cast<uint16_t*>(ub)[jj * 2 + i] = (uint16_t)e[i][jj];
-          else ub[jj * 4 + i] = (uint8_t)e[i][jj];
+          if constexpr (!FP8) wv[jj] = ev[0][jj] | (ev[1][jj] << 16);
+          else wv[jj] = ev[0][jj] | (ev[1][jj] << 8) | (ev[2][jj] << 16) | (ev[3][jj] << 24);
+        }
+        *reinterpret_cast<uint4*>(ub) = uint4{wv[0], wv[1], wv[2], wv[3]};
+      } else {                                     // an end of the range: element by element
+#pragma unroll
+        for (int e = 0; e < kT; ++e) {
+          const int ts = ta + e;
+          if (ts < rp.t0 || ts > rp.t1) continue;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            if constexpr (!FP8) reinterpret_cast<uint16_t*>(ub)[jj * 2 + e] = (uint16_t)ev[e][jj];
+            else ub[jj * 4 + e] = (uint8_t)ev[e][jj];
+          }
         }
       }
     }
@@ -376,8 +428,8 @@ static int64_t rows_items(const AppendArgs& a, int max_q_len) {
 hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream) {
   const int64_t items = rows_items(a, max_q_len);
   if (items == 0) return hipSuccess;
-  if (items > 0x7fffffff || a.num_kv_heads > 65535) return launch_append_local(a, fp8, rope, stream);
-  dim3 grid((unsigned)items, a.num_kv_heads), block(256);
+  if (items > 0x7fffffff) return launch_append_local(a, fp8, rope, stream);
+  dim3 grid((unsigned)items, (a.num_kv_heads + kRowsHeads - 1) / kRowsHeads), block(256);
   if (fp8) {
     if (rope) hipLaunchKernelGGL((append_local_rows_kernel<true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((append_local_rows_kernel<true, false>), grid, block, 0, stream, a);
