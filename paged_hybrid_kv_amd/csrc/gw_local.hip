@@ -10,10 +10,10 @@
 // When the call carries the rows' new K/V, the token at p is rotated and
 // stored first (the prep step), exactly as gw_kv_append stores it.
 //
-// Work split: one workgroup per (split, KV head, sequence); a split is a
-// balanced run of the row's range in virtual pages (gw_plan.h: the two
-// partial pages at the ends of a full window are walked as one, so a
-// 1024-token window is 64 pages of work, 16 per split).  Four waves per
+// Work split: one workgroup per (split, KV head, sequence), numbered
+// split-major; a split is a balanced run of the row's range in virtual
+// pages (gw_plan.h: the two partial pages at the ends of a full window are
+// walked as one, so a 1024-token window is 64 pages of work, 16 per split).  Four waves per
 // workgroup take every fourth page of the split, each with its own online
 // softmax state (running max m, sum l, accumulator), merged in LDS at the end.
 // The last workgroup of a (sequence, KV head) to finish merges the splits'
@@ -399,7 +399,12 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
 
 template <int G, bool FP8>
 __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(LocalAttnArgs a) {
-  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // workgroups go split-major (every pair's split 0, then every pair's
+  // split 1, ...), rows fastest: a pair's splits are dispatched apart, which
+  // measures faster than dispatching them side by side
+  const int npairs = a.num_kv_heads * a.num_seqs;
+  const int split = uniform_i32((int)blockIdx.x / npairs), rem = (int)blockIdx.x % npairs;
+  const int g = uniform_i32(rem / a.num_seqs), s = uniform_i32(rem % a.num_seqs);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
 
@@ -649,7 +654,9 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
 }  // namespace
 
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
-  dim3 grid(a.max_splits, a.num_kv_heads, a.num_seqs), block(256);
+  const int64_t n = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
+  if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)n), block(256);
 #define GW_LOCAL_CASE(G_, F_) \
   if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, block, 0, stream, a); return hipGetLastError(); }
   GW_LOCAL_CASE(1, false) GW_LOCAL_CASE(2, false) GW_LOCAL_CASE(4, false)
