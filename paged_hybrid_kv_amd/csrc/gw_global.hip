@@ -495,8 +495,10 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   const float l_tot = sum_lanes_xor16_32(l_run);
   float* op = a.out + ((int64_t)(row0 + r) * a.num_q_heads + head) * kGD + d_lo + 4 * g;
   const float inv = 1.f / l_tot;
+  // streaming stores (written back now rather than evicted later during a
+  // decode kernel's stream)
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
+  for (int b = 0; b < kBlocks; ++b) __builtin_nontemporal_store(acc[b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),

@@ -404,8 +404,12 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
     const int v = 16 * QB * w + 16 * qb + l16;
     float* op = a.out + ((int64_t)(row0 + r_first + v / G) * a.num_q_heads + gk * G + v % G) * 256 + 4 * gq;
     const float inv = 1.f / l_tot;
+    // streaming stores: nothing in this step reads the rows' outputs again,
+    // so they go out to memory now, while this kernel leaves HBM idle,
+    // instead of sitting dirty in the caches until the next decode kernel's
+    // stream evicts them
 #pragma unroll
-    for (int b = 0; b < 16; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[qb][b] * inv;
+    for (int b = 0; b < 16; ++b) __builtin_nontemporal_store(acc[qb][b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
   }
 }
 
