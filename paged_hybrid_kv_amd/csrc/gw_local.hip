@@ -353,7 +353,13 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
                                              uint64_t tag) {
   uint64_t mi[GH][NS], li[GH][NS], ai[GH][NS];
   // one copy of the load code (the kernel's tail runs from a cold
-  // instruction cache): read everything, and again while any pair is stale
+  // instruction cache): read everything, and again while any pair is stale.
+  // The first read is a plain one: the splits of a (sequence, KV head) are
+  // dispatched (KV heads x sequences) workgroups apart, a multiple of the 8
+  // XCDs that workgroups are dealt to in turn when the KV heads number 8, so
+  // they share an XCD and its L2, which the writers' stores pass through.  Wherever the
+  // workgroups ran, a pair read from a stale line carries an old tag and is
+  // read again at device scope, so the result never depends on placement.
   bool ok = true;
   for (int spin = 0;; ++spin) {
     bool all = true;
@@ -364,9 +370,15 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
         mi[h][i] = li[h][i] = ai[h][i] = tag;
         if (i < nsplit) {
           const int64_t ic = ((int64_t)s * a.num_q_heads + h0 + h) * a.max_splits + i;
-          mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (spin == 0) {   // may be served by this XCD's L2
+            mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else {           // from the memory side
+            mi[h][i] = __hip_atomic_load(a.part_ml + ic * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            li[h][i] = __hip_atomic_load(a.part_ml + ic * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ai[h][i] = __hip_atomic_load(a.part_acc + ic * kLocalD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
 #pragma unroll
@@ -608,9 +620,9 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   // out as one 64-bit (value, tag) pair, tag = this call's epoch, with
   // device-scope atomic stores, and the arrival counter moves right after
   // the stores are issued, without waiting for them: the last workgroup
-  // reads each pair with a device-scope atomic load and reads again, until
-  // its tag is this call's, the few pairs whose stores are still on their
-  // way.  Every pair it waits for was stored before its writer's arrival,
+  // reads each pair (atomic 64-bit loads: plain first, then device scope)
+  // and reads again, until its tag is this call's, the few pairs whose
+  // stores are still on their way.  Every pair it waits for was stored before its writer's arrival,
   // so each wait ends; a bound on the re-reads turns a broken invariant
   // into NaN output instead of a hang.
   const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
