@@ -193,8 +193,11 @@ int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const v
  *     k_new/v_new: the pool already holds every row's token.
  *   workspace : at least gw_attn_workspace_bytes(...) bytes (NULL when that
  *     is 0), 256-byte aligned, ZERO-FILLED before its first use; every call
- *     that completes leaves it ready for the next call (it holds split
- *     counters that the call's last workgroups reset).  Calls that overlap
+ *     that completes leaves it ready for the next call of the same shape (it
+ *     holds split counters that the call's last workgroups reset, and
+ *     per-sequence call epochs).  Where those sit depends on the shape
+ *     (num_seqs, KV and q heads, num_rows, max_q_len, max_seq_len, window):
+ *     zero-fill it again before a call of another shape.  Calls that overlap
  *     in time must not share a workspace.
  *
  * Results are deterministic, and each row's result depends only on that

@@ -156,17 +156,24 @@ def upload_global(case: GlobalCase, compressed: bool = True, device="cuda",
 
 class Workspace:
     """Grow-only device workspace, 256-byte aligned, zero-filled when
-    (re)allocated; the library leaves it ready for the next call."""
+    (re)allocated.  The library leaves it ready for the next call of the same
+    shape; where its split counters and call epochs sit depends on the shape,
+    so a call of another shape (another `key`: the arguments the size was
+    asked for with) gets it zero-filled again first."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
+        self.key = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, key=None):
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes + 256:
             self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+        elif key != self.key:
+            self.buf.zero_()
+        self.key = key
         addr = self.buf.data_ptr()
         aligned = (addr + 255) // 256 * 256
         return aligned, nbytes
@@ -183,9 +190,10 @@ def attend(dc: DeviceCase, out: torch.Tensor | None = None, ws: Workspace | None
     if out is None:
         out = torch.empty((dc.num_rows, dc.num_q_heads, D), dtype=torch.float32, device=dc.q.device)
     ws = ws or Workspace(dc.q.device)
-    need = gw.gw_attn_workspace_bytes(dc.pool.family, dc.num_seqs, dc.num_rows, dc.num_q_heads, D,
-                                      dc.max_seq_len, dc.window if local else 0, dc.max_q_len)
-    wptr, wbytes = ws.get(need)
+    shape = (dc.pool.family, dc.num_seqs, dc.num_rows, dc.num_q_heads, D, dc.max_seq_len,
+             dc.window if local else 0, dc.max_q_len)
+    need = gw.gw_attn_workspace_bytes(*shape)
+    wptr, wbytes = ws.get(need, (shape, dc.pool.num_kv_heads))
     cos, sin = rope if rope is not None else (None, None)
     if local:
         gw.gw_decode_attn_local(dc.pool.desc, dc.q, dc.num_q_heads, k_new, v_new, cos, sin,

@@ -184,6 +184,22 @@ def test_workspace_plan():
     assert gw.gw_attn_workspace_bytes(gw.GW_FAMILY_GLOBAL_FULL, 1, 1, 32, 512, 256, 0, 1) == 0
 
 
+def test_workspace_rezeroed_for_another_shape():
+    # the library leaves a workspace ready for the next call of the same
+    # shape only: the host-side holder zero-fills it again when the shape
+    # (the arguments its size was asked for with) changes
+    import torch
+    from paged_hybrid_kv_amd import runtime as RT
+    ws = RT.Workspace("cpu")
+    ws.get(4096, "a")
+    ws.buf.fill_(7)
+    ws.get(4096, "a")
+    assert int(ws.buf.sum()) == 7 * ws.buf.numel()   # same shape: kept
+    ws.get(1024, "b")
+    assert int(ws.buf.count_nonzero()) == 0          # another shape: zero-filled
+    assert ws.get(0, "c") == (None, 0)
+
+
 def test_error_message_is_thread_local_and_cleared():
     with pytest.raises(gw.GwError):
         local(win=0)

@@ -194,6 +194,21 @@ def test_repeat_determinism():
         assert np.array_equal(o1, RT.attend(dc, ws=ws).cpu().numpy())
 
 
+def test_workspace_shared_across_shapes():
+    # calls of two shapes (more sequences, so more split counters, in the
+    # second) take turns on one workspace: each result equals the one from a
+    # fresh workspace, bit for bit
+    ca = SY.local_case("ws_a", 21, [5000, 2000, 8000], window=1024, num_q_heads=16, num_kv_heads=8, rope=True)
+    cb = SY.local_case("ws_b", 22, [3000, 7000, 1500, 6000, 4000, 2500, 8000], window=1024, num_q_heads=16,
+                       num_kv_heads=8, rope=True)
+    da, oa = run(ca)
+    db, ob = run(cb)
+    ws = RT.Workspace()
+    for _ in range(3):
+        assert np.array_equal(oa, RT.attend(da, ws=ws).cpu().numpy())
+        assert np.array_equal(ob, RT.attend(db, ws=ws).cpu().numpy())
+
+
 # ------------------------------------------------------------- append ------
 def pool_bytes(dc):
     torch.cuda.synchronize()
