@@ -14,7 +14,10 @@ step's new token per slot (RoPE + store) then paged decode attention of the
 value = algorithmic decode KV bytes of one step (50 local layers x 16 slots x
 1024 tokens x 8 KiB + 10 global layers x sum(L) x 1280 B) / step time.
 The mixed step (the same plus 4 new 512-token prompts whose causal rows are
-computed in the same step) is reported beside it when served.
+computed in the same step) is reported beside it, and so is the same step
+with the prompt rows as a 512-token chunk after a cached 3584-token prefix
+(chunked prefill: every row attends a full local window and 3585..4096
+global keys).
 
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
@@ -304,26 +307,44 @@ def main():
     roof = dominant_kernel(step, args.kernel_rounds)
     log(f"dominant kernel: {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s ({roof['frac'] * 100:.1f}%)")
 
-    mixed = None
-    try:
-        if args.no_mixed:
-            raise gw.GwError(0, "skipped (--no-mixed)")
-        ms_step = HybridStep(with_prompts=True)
+    def prompt_step(shape, label):
+        ms_step = HybridStep(shape=shape, with_prompts=True)
         if not args.no_graph:
             ms_step.capture()
         for _ in range(args.warmup):
             ms_step.replay()
         mms = time_events(ms_step.replay, args.steps)
         mb = ms_step.mixed_step_bytes()
-        mixed = {"ms_per_step": round(mms, 4), "decode_tok_s": round(16 / (mms * 1e-3), 1),
-                 "rows_per_s": round(ms_step.rows / (mms * 1e-3), 1), "rows": ms_step.rows,
-                 "algorithmic_bytes": mb,
-                 "GB_per_s": round(mb["total"] / (mms * 1e-3) / 1e9, 1),
-                 "pct_of_peak": round(mb["total"] / (mms * 1e-3) / PEAK_HBM * 100, 2)}
+        fl = ms_step.prompt_flops()
+        res = {"ms_per_step": round(mms, 4), "decode_tok_s": round(16 / (mms * 1e-3), 1),
+               "rows_per_s": round(ms_step.rows / (mms * 1e-3), 1), "rows": ms_step.rows,
+               "prompt_prefix": ms_step.shape.prompt_prefix,
+               "algorithmic_bytes": mb,
+               "GB_per_s": round(mb["total"] / (mms * 1e-3) / 1e9, 1),
+               "pct_of_peak": round(mb["total"] / (mms * 1e-3) / PEAK_HBM * 100, 2),
+               "prompt_row_gflop": round(fl / 1e9, 1)}
+        log(f"{label}: {mms:.3f} ms, {res['GB_per_s']} GB/s ({res['pct_of_peak']}% of peak), "
+            f"{res['prompt_row_gflop']} GFLOP of prompt-row products")
         del ms_step
-    except gw.GwError as e:
-        mixed = {"served": False, "reason": e.message}
-    torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
+        return res
+
+    mixed = chunked = None
+    if args.no_mixed:
+        mixed = chunked = {"served": False, "reason": "skipped (--no-mixed)"}
+    else:
+        from paged_hybrid_kv_amd.synth import HybridShape
+        for key, shape, label in (("mixed", None, "mixed step"),
+                                  ("chunked", HybridShape(prompt_prefix=3584),
+                                   "mixed step, prompt chunk after a 3584-token cached prefix")):
+            try:
+                r = prompt_step(shape, label)
+            except gw.GwError as e:
+                r = {"served": False, "reason": e.message}
+            if key == "mixed":
+                mixed = r
+            else:
+                chunked = r
 
     if args.copy_calib:
         copy_calibration()
@@ -350,6 +371,7 @@ def main():
                    "contexts": [int(x) for x in sh.decode_lens], "graph": not args.no_graph},
         "roofline": roof,
         "mixed_step": mixed,
+        "chunked_prefill_step": chunked,
         "cpu_baseline": cpu,
     }
     if configs is not None:

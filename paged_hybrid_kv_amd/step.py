@@ -171,11 +171,31 @@ class HybridStep:
         prompts = [int(x) for x in self.q_len[sh.decode_slots:]]
         pre_tok = sum(prompts)
         new_tok = sh.decode_slots + pre_tok
-        kv = self.decode_kv_bytes() + n_loc * pre_tok * loc_tok + n_glob * pre_tok * glob_tok
+        # a prompt's rows (positions P .. P + n - 1) attend the union
+        # [max(0, P - W + 1), P + n - 1] (local) or [0, P + n - 1] (global)
+        P = sh.prompt_prefix if self.with_prompts else 0
+        loc_rng = sum(P + n - max(0, P - sh.window + 1) for n in prompts)
+        glob_rng = sum(P + n for n in prompts)
+        kv = self.decode_kv_bytes() + n_loc * loc_rng * loc_tok + n_glob * glob_rng * glob_tok
         app = (n_loc * new_tok * (loc_tok + loc_tok) + n_glob * new_tok * (512 * 2 + glob_tok))
         rows = self.rows
         qo = (n_loc * rows * sh.local_q_heads * 256 * (2 + 4) + n_glob * rows * sh.global_q_heads * 512 * (2 + 4))
         return {"kv_read": kv, "append": app, "q_out": qo, "total": kv + app + qo}
+
+    def prompt_flops(self) -> int:
+        """2 x the multiply-adds of the prompt rows' two products (scores and
+        weighted values) over the keys each row attends, all layers."""
+        sh = self.shape
+        n_glob = sum(1 for l in range(sh.num_layers) if sh.is_global(l))
+        n_loc = sh.num_layers - n_glob
+        P = sh.prompt_prefix if self.with_prompts else 0
+        loc = glob = 0
+        for n in (int(x) for x in self.q_len[sh.decode_slots:]):
+            p = P + np.arange(n, dtype=np.int64)
+            loc += int(np.minimum(p + 1, sh.window).sum())
+            glob += int((p + 1).sum())
+        return (n_loc * loc * sh.local_q_heads * 256 * 4 +
+                n_glob * glob * sh.global_q_heads * 512 * 4)
 
     def local_decode_kv_bytes_per_layer(self) -> int:
         sh = self.shape

@@ -233,7 +233,11 @@ class HybridShape:
     60 layers, layer i global iff (i+1) % 6 == 0 or i is the last layer.
     16 decode slots with contexts drawn in [2048, 8192] (seed 5), each
     advancing one token; 4 new prompts of 512 tokens whose rows are computed
-    in the same step (causal within the prompt, no prior context).
+    in the same step (causal within the prompt, no prior context).  With
+    prompt_prefix P > 0 the prompt rows are instead a 512-token chunk of
+    longer prompts whose first P tokens are already in the cache: rows at
+    positions P .. P + 511, each attending its window (local) or everything
+    before it (global), cached prefix included.
     """
     num_layers: int = 60
     decode_slots: int = 16
@@ -241,6 +245,7 @@ class HybridShape:
     ctx_hi: int = 8192
     prompts: int = 4
     prompt_len: int = 512
+    prompt_prefix: int = 0
     window: int = 1024
     local_q_heads: int = 16
     local_kv_heads: int = 8
@@ -263,7 +268,7 @@ class HybridShape:
 
     def lens(self, with_prompts: bool = True) -> np.ndarray:
         """Context length of every sequence in the step (current token included)."""
-        extra = [self.prompt_len] * self.prompts if with_prompts else []
+        extra = [self.prompt_prefix + self.prompt_len] * self.prompts if with_prompts else []
         return np.concatenate([self.decode_lens, np.array(extra, dtype=np.int64)])
 
     def q_len(self, with_prompts: bool = True) -> np.ndarray:
@@ -298,8 +303,10 @@ def step_tokens(shape: HybridShape, with_prompts: bool, local: bool):
     """(seq, pos) of the tokens appended in the step and of the prior context.
 
     Decode slot s appends its current token at L_s - 1; prompt i (sequence
-    16 + i) appends positions 0..511.  Prior context: positions from the first
-    allocated page (local: the window's first page; global: 0) to L_s - 2.
+    16 + i) appends positions P..P+511 (P = prompt_prefix).  Prior context:
+    positions from the first allocated page (local: the first page of the
+    earliest row's window; global: 0) to the position before the first
+    appended one; the prompts' prior context follows the decode slots'.
     """
     lens = shape.lens(with_prompts)
     new_s, new_p, pri_s, pri_p = [], [], [], []
@@ -309,9 +316,15 @@ def step_tokens(shape: HybridShape, with_prompts: bool, local: bool):
         lo = (max(0, L - shape.window) // PAGE) * PAGE if local else 0
         pri_s.append(np.full(L - 1 - lo, s)); pri_p.append(np.arange(lo, L - 1))
     if with_prompts:
+        P = shape.prompt_prefix
         for i in range(shape.prompts):
             s = shape.decode_slots + i
-            new_s.append(np.full(shape.prompt_len, s)); new_p.append(np.arange(shape.prompt_len))
+            new_s.append(np.full(shape.prompt_len, s)); new_p.append(P + np.arange(shape.prompt_len))
+        for i in range(shape.prompts):
+            if P > 0:
+                s = shape.decode_slots + i
+                lo = (max(0, P - shape.window + 1) // PAGE) * PAGE if local else 0
+                pri_s.append(np.full(P - lo, s)); pri_p.append(np.arange(lo, P))
     cat = lambda xs: np.concatenate([np.asarray(x, dtype=np.int32) for x in xs]) if xs else np.zeros(0, np.int32)
     return cat(new_s), cat(new_p), cat(pri_s), cat(pri_p)
 

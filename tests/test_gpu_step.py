@@ -5,7 +5,9 @@ CPU oracle.
 
 Workload: 16 decode slots with seeded contexts in [2048, 8192] plus 4 new
 512-token prompts (pegainfer "Gemma 4" page, Scheduling: a new prompt's rows
-are computed in the same step as the live streams' next token).  The oracle
+are computed in the same step as the live streams' next token), and the same
+step with the prompt rows as a 512-token chunk after a cached 3584-token
+prefix (chunked prefill against cached context).  The oracle
 sees only the seeded draws of the layer (q, the step's new K/V and the prior
 context K/V, all bf16) and rotates and rounds them itself; no value comes
 from the GPU path.  After a replay the step's output buffers hold the last
@@ -89,10 +91,10 @@ def _check_layer(st, layer: int, out):
     return worst
 
 
-def test_hybrid_step_graph_sampled_parity():
+def _run_and_check(shape, label):
     import torch
     from paged_hybrid_kv_amd.step import HybridStep
-    st = HybridStep(with_prompts=True)
+    st = HybridStep(shape=shape, with_prompts=True)
     st.capture()
     for _ in range(2):
         st.replay()
@@ -102,5 +104,17 @@ def test_hybrid_step_graph_sampled_parity():
     last_global = max(l for l in range(sh.num_layers) if sh.is_global(l))
     e_loc = _check_layer(st, last_local, st.out_local)
     e_glob = _check_layer(st, last_global, st.out_global)
-    print(f"hybrid step: layer {last_local} (local) max abs err {e_loc:.2e}, "
+    print(f"{label}: layer {last_local} (local) max abs err {e_loc:.2e}, "
           f"layer {last_global} (global) max abs err {e_glob:.2e}", flush=True)
+
+
+def test_hybrid_step_graph_sampled_parity():
+    _run_and_check(None, "hybrid step")
+
+
+def test_hybrid_step_chunked_prefill_sampled_parity():
+    # the prompt rows are the last 512-token chunk of 4096-token prompts
+    # whose first 3584 tokens are already cached: each row attends a full
+    # local window, or 3585..4096 global keys, the cached prefix included
+    from paged_hybrid_kv_amd.synth import HybridShape
+    _run_and_check(HybridShape(prompt_prefix=3584), "hybrid step, chunk after a 3584-token prefix")
