@@ -75,7 +75,7 @@ struct GlobalPage {
 // into the wave's output-dim slice.  pg: the page in LDS; tok_page0: the
 // position of the page's first token; p: the row's position (tokens past it
 // are masked, and their V zeroed, so unwritten slots never reach the output).
-template <bool COMPRESSED, int HB, bool LAZY = false>
+template <bool COMPRESSED, int HB>
 __device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
                                                  const uint8_t* pg, const bf16x8 (&qf)[16],
                                                  int tok_page0, int p, int g, int l16, int v_lane_off,
@@ -103,27 +103,14 @@ __device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_
 #pragma unroll
   for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * scale_log2 : -INFINITY;
   const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-  if constexpr (LAZY) {
-    // the reference max moves only when a score passes it by more than
-    // 2^8 (the weights then stay below 2^8), so rescales are rare
-    if (__any(mx > m_run + 8.f)) {
-      const bool up = mx > m_run + 8.f;
-      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+  const float mnew = fmaxf(m_run, mx);
+  if (__any(mnew > m_run)) {
+    const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
 #pragma unroll
-      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
-      l_run *= alpha;
-      m_run = up ? mx : m_run;
-    }
-  } else {
-    const float mnew = fmaxf(m_run, mx);
-    if (__any(mnew > m_run)) {
-      const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-#pragma unroll
-      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
-      l_run *= alpha;
-    }
-    m_run = mnew;
+    for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
+    l_run *= alpha;
   }
+  m_run = mnew;
   const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
   const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
   l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
@@ -371,38 +358,116 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   }
 }
 
-// Prompt rows (sequences with more than one query row: a new prompt's
-// rows, computed in the same step as the decode rows -- pegainfer "Gemma 4"
-// page, Scheduling).  Row r of sequence s sits at position
-// p_r = seq_len - q_len + r and attends keys 0 .. p_r.  A workgroup takes two
-// consecutive rows: group q (four waves, as in the decode kernel) row 2m + q,
-// and both groups read the same stream of pages, pages 0 .. p_last / 16 of
-// the pair, through an LDS ring of NS pages that all eight waves fill.  No
-// split: a row's whole range is one pass, and the output is written
-// directly.  Workgroups are numbered compactly over the prompt sequences'
-// row pairs, a sequence's pairs with the most pages first.
-template <bool COMPRESSED, int HB, int NS>
-__global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a) {
+// One page for the prompt rows: a wave takes one head block (16 heads) of NR
+// rows over all 512 dims, so no wave repeats another's scores and each K
+// and V fragment it reads from LDS feeds NR rows' products.  Per page:
+// S^T = K . Q^T per row (16 steps, K read in batches of 4 fragments), the
+// lazy online-softmax update per row, then O^T += V^T . P^T over 32 output
+// blocks of 16 dims (V read in batches of 4 blocks).  V of tokens past p_v
+// (slots past the workgroup's last row, possibly never written) is zeroed
+// in the operand registers.
+template <bool COMPRESSED, int NR>
+__device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m_run)[NR], float (&l_run)[NR],
+                                                 const uint8_t* pg, const bf16x8 (&qf)[NR][16], int tok_page0,
+                                                 const int (&p)[NR], int p_v, int g, int l16, int v_lane_off,
+                                                 float scale_log2) {
   using PG = GlobalPage<COMPRESSED>;
-  constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
-  constexpr int kBlocks = 8 * HB;
-  static_assert(kUnits % 4 == 0, "page units");
-  constexpr int kPerWave = kUnits / 8;        // units per wave per page (all eight waves move)
-  constexpr int kPerWaveTail = kUnits % 8;    // the first kUnits % 8 waves move one more
+  f32x4 s[NR][2];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) s[r][0] = s[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int hk = 0; hk < 4; ++hk) {
+    bf16x8 kf[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (4 * hk + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        s[r][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[r][4 * hk + k], s[r][k & 1], 0, 0, 0);
+  }
+  const int tok0 = tok_page0 + 4 * g;
+  s16x4 pb[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const f32x4 sacc = s[r][0] + s[r][1];
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = (tok0 + i <= p[r]) ? sacc[i] * scale_log2 : -INFINITY;
+    const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    // the reference max moves only when a score passes it by more than 2^8
+    if (__any(mx > m_run[r] + 8.f)) {
+      const bool up = mx > m_run[r] + 8.f;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run[r] - mx) : 1.f;
+#pragma unroll
+      for (int b = 0; b < 32; ++b) acc[r][b] *= alpha;
+      l_run[r] *= alpha;
+      m_run[r] = up ? mx : m_run[r];
+    }
+    const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run[r]), __builtin_amdgcn_exp2f(z[1] - m_run[r]));
+    const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run[r]), __builtin_amdgcn_exp2f(z[3] - m_run[r]));
+    l_run[r] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+    pb[r] = __builtin_bit_cast(s16x4, uint2{p01, p23});
+  }
+  const bool tail = tok_page0 + 15 > p_v;   // uniform
+  uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
+  if (tail) {
+    vm0 = (tok0 + 0 <= p_v ? 0x0000ffffu : 0u) | (tok0 + 1 <= p_v ? 0xffff0000u : 0u);
+    vm1 = (tok0 + 2 <= p_v ? 0x0000ffffu : 0u) | (tok0 + 3 <= p_v ? 0xffff0000u : 0u);
+  }
+  lds_u8* vrow = (lds_u8*)pg + v_lane_off;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    uint2 vf[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * (4 * bb + b))));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint2 vv = vf[b];
+      vv.x &= vm0;
+      vv.y &= vm1;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        acc[r][4 * bb + b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb[r],
+                                                                       acc[r][4 * bb + b], 0, 0, 0);
+    }
+  }
+}
+
+// Prompt rows (sequences with more than one query row: a new prompt's
+// rows, or a chunk of one after a cached prefix, computed in the same step
+// as the decode rows -- pegainfer "Gemma 4" page, Scheduling).  Row r of
+// sequence s sits at position p_r = seq_len - q_len + r and attends keys
+// 0 .. p_r.  kW = 8 / NR waves; wave (hb, rp) takes head block hb of rows
+// NR rp .. NR rp + NR - 1 of the workgroup's kW NR / HB rows (NR = 1: two
+// waves per SIMD; two rows per wave do not fit the registers), through a
+// ring of NS pages that all waves fill.  No split: a row's whole range is
+// one pass, and the output is written directly.  Items are (prompt
+// sequence, row group), numbered compactly, a sequence's last groups
+// (longest ranges) first.
+template <bool COMPRESSED, int HB, int NR, int NS>
+__global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(GlobalAttnArgs a) {
+  using PG = GlobalPage<COMPRESSED>;
+  constexpr int kW = 8 / NR;                  // waves
+  constexpr int kUnits = PG::kBytes / 1024;
+  constexpr int kPerWave = kUnits / kW;       // units per wave per page ...
+  constexpr int kPerWaveTail = kUnits % kW;   // ... the first kUnits % kW waves one more
+  constexpr int kRows = kW * NR / HB;         // rows per workgroup
   static_assert(NS >= 2 && NS - 2 <= 4 && (kPerWave + 1) * (NS - 2) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform_i32(tid >> 6);
-  const int grp = wv >> 2, w = wv & 3;
-  const int hb = HB == 2 ? (w & 1) : 0;
-  const int d_lo = HB == 2 ? 256 * (w >> 1) : 128 * w;
+  const int hb = HB == 2 ? (wv & 1) : 0;
+  const int rp = HB == 2 ? (wv >> 1) : wv;
   const int g = lane >> 4, l16 = lane & 15;
   const int head = 16 * hb + l16;
 
-  // ---- work item: the call's (prompt sequence, row pair) items, numbered
-  // sequence by sequence, a sequence's last pairs (longest ranges) first
-  int s = -1, mp = 0, row0 = 0, q_len = 0, L = 0;
+  int s = -1, mg = 0, row0 = 0, q_len = 0, L = 0;
   {
     const int item = blockIdx.x;
     int base = 0;
@@ -413,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
         r0 = a.q_indptr[sl];
         ql = a.q_indptr[sl + 1] - r0;
         len = a.seq_lens[sl];
-        if (ql > 1) cnt = (ql + 1) >> 1;
+        if (ql > 1) cnt = (ql + kRows - 1) / kRows;
       }
       int incl = cnt;
 #pragma unroll
@@ -426,7 +491,7 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
         const int ls = __builtin_ctzll(__ballot(base + incl > item));
         s = c + ls;
         const int nb = __builtin_amdgcn_readlane(cnt, ls);
-        mp = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
+        mg = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
         row0 = __builtin_amdgcn_readlane(r0, ls);
         q_len = __builtin_amdgcn_readlane(ql, ls);
         L = __builtin_amdgcn_readlane(len, ls);
@@ -437,20 +502,26 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   }
   if (s < 0) return;
   s = uniform_i32(s);
-  mp = uniform_i32(mp);
+  mg = uniform_i32(mg);
   row0 = uniform_i32(row0);
   q_len = uniform_i32(q_len);
   L = uniform_i32(L);
 
-  const int r = 2 * mp + grp;
-  const bool row_ok = r < q_len;                 // uniform in the group
-  const int r_last = min(2 * mp + 1, q_len - 1);
-  const int p = L - q_len + (row_ok ? r : r_last);
+  // the workgroup's rows kRows mg .. r_last; this wave's rows compute on
+  // r_last's query and position when they lie past it (and are not written)
+  const int r_last = min(kRows * mg + kRows - 1, q_len - 1);
   const int p_last = L - q_len + r_last;
   const int n = (p_last >> 4) + 1;
+  int rw[NR], pr[NR];
+  bool rok[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    rw[i] = kRows * mg + NR * rp + i;
+    rok[i] = rw[i] <= r_last;
+    pr[i] = L - q_len + (rok[i] ? rw[i] : r_last);
+  }
 
-  // wave wv moves units [u0, u0 + nu) of every page: kPerWave each, the
-  // first kUnits % 8 waves one more
+  // wave wv moves units [u0, u0 + nu) of every page
   const int nu = kPerWave + (wv < kPerWaveTail ? 1 : 0);
   const int u0 = kPerWave * wv + min(wv, kPerWaveTail);
   PageIds ids;
@@ -467,38 +538,45 @@ __global__ __launch_bounds__(512, 1) void global_prefill_kernel(GlobalAttnArgs a
   for (int i = 0; i < NS - 1; ++i)
     if (i < n) issue_page(i);
 
-  bf16x8 qf[16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(row0 + (row_ok ? r : r_last)) * a.num_q_heads + head) * kGD + 8 * g;
+  bf16x8 qf[NR][16];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
+  for (int i = 0; i < NR; ++i) {
+    const uint16_t* qp = a.q + ((int64_t)(row0 + (rok[i] ? rw[i] : r_last)) * a.num_q_heads + head) * kGD + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < 16; ++ks) qf[i][ks] = __builtin_bit_cast(bf16x8, ld16_cached(qp + 32 * ks));
   }
 
-  f32x4 acc[kBlocks];
+  f32x4 acc[NR][32];
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const int v_lane_off = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int b = 0; b < 32; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NR], l_run[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+  const int v_lane_off = global_v_lane_off<COMPRESSED>(0, g, l16);
 
   for (int i = 0; i < n; ++i) {
     if (nu > kPerWave) wait_groups_after<kPerWave + 1>(min(NS - 2, n - 1 - i));
     else wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
     lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
     if (i + NS - 1 < n) issue_page(i + NS - 1);
-    if (row_ok && i * 16 <= p)
-      global_page_step<COMPRESSED, HB, true>(acc, m_run, l_run, ring[i % NS], qf, i * 16, p, g, l16, v_lane_off,
-                                       a.scale_log2);
+    global_rows_page<COMPRESSED, NR>(acc, m_run, l_run, ring[i % NS], qf, i * 16, pr, p_last, g, l16, v_lane_off,
+                                     a.scale_log2);
   }
-  if (!row_ok) return;
-  const float l_tot = sum_lanes_xor16_32(l_run);
-  float* op = a.out + ((int64_t)(row0 + r) * a.num_q_heads + head) * kGD + d_lo + 4 * g;
-  const float inv = 1.f / l_tot;
-  // streaming stores (written back now rather than evicted later during a
-  // decode kernel's stream)
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) __builtin_nontemporal_store(acc[b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
+  for (int i = 0; i < NR; ++i) {
+    if (!rok[i]) continue;
+    const float inv = 1.f / sum_lanes_xor16_32(l_run[i]);
+    float* op = a.out + ((int64_t)(row0 + rw[i]) * a.num_q_heads + head) * kGD + 4 * g;
+    // streaming stores (written back now rather than evicted later during a
+    // decode kernel's stream)
+#pragma unroll
+    for (int b = 0; b < 32; ++b) __builtin_nontemporal_store(acc[i][b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
+  }
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
@@ -582,21 +660,23 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStr
 }
 
 hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
-  // items: (prompt sequence, row pair); at most (rows + sequences) / 2, and
-  // at most sequences * ceil(max_q_len / 2)
-  const int64_t by_rows = ((int64_t)a.num_rows + a.num_seqs) / 2;
-  const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + 1) / 2);
+  // items: (prompt sequence, group of 8 / HB rows); at most
+  // (rows + sequences * (group - 1)) / group, and at most
+  // sequences * ceil(max_q_len / group)
+  const bool h32 = a.num_q_heads == 32;
+  const int rows = h32 ? 4 : 8;
+  const int64_t by_rows = ((int64_t)a.num_rows + (int64_t)a.num_seqs * (rows - 1)) / rows;
+  const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + rows - 1) / rows);
   const int64_t items = by_rows < by_len ? by_rows : by_len;
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)items), block(512);
-  const bool h32 = a.num_q_heads == 32;
   if (compressed) {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 4>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 4>), grid, block, 0, stream, a);
   } else {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 3>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 3>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 1, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 1, 4>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
