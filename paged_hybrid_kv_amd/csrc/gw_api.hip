@@ -87,8 +87,10 @@ int check_pool(const gw_pool_desc* p, const char* fn) {
 }
 
 // Largest split count of any decode row of a call.
-int max_splits_for(int family, int max_seq_len, int window) {
-  if (family == GW_FAMILY_LOCAL) return gw::local_nsplit(gw::local_max_range_pages(max_seq_len, window));
+// group: the call's query-group size (local family); the size query, which
+// does not know it, passes 4, the size with the most splits.
+int max_splits_for(int family, int max_seq_len, int window, int group) {
+  if (family == GW_FAMILY_LOCAL) return gw::local_nsplit(gw::local_max_range_pages(max_seq_len, window), group);
   return gw::global_nsplit(gw::cdiv_i(max_seq_len, 16));
 }
 
@@ -104,9 +106,9 @@ struct WsPlan {
 };
 
 WsPlan plan_workspace(int family, int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
-                      int max_seq_len, int window) {
+                      int max_seq_len, int window, int group) {
   WsPlan w{};
-  w.max_splits = max_splits_for(family, max_seq_len, window);
+  w.max_splits = max_splits_for(family, max_seq_len, window, group);
   if (w.max_splits <= 1 || num_seqs <= 0) return w;
   const bool local = family == GW_FAMILY_LOCAL;
   const size_t units = (size_t)num_seqs * num_q_heads * w.max_splits;
@@ -234,7 +236,7 @@ size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_row
   if (family == GW_FAMILY_LOCAL && window < 1) return 0;
   if (!is_local(family) && !is_global(family)) return 0;
   // one counter per (sequence, q head) bounds the per-(sequence, KV head) need
-  return plan_workspace(family, num_seqs, num_q_heads, num_q_heads, head_dim, max_seq_len, window).total;
+  return plan_workspace(family, num_seqs, num_q_heads, num_q_heads, head_dim, max_seq_len, window, 4).total;
 }
 
 int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
@@ -267,7 +269,7 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
   if (v_new && pool->rot_dim == 0 && rope_cos)
     return fail(GW_ERR_INVALID_ARG, fn, "rot_dim 0 takes no rotary tables");
   const WsPlan w = plan_workspace(GW_FAMILY_LOCAL, num_seqs, pool->num_kv_heads, num_q_heads, 256,
-                                  max_seq_len, window);
+                                  max_seq_len, window, group);
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
@@ -353,7 +355,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
-  const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0);
+  const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0, 1);
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");

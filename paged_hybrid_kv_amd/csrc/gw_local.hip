@@ -13,9 +13,11 @@
 // Work split: one workgroup per (split, KV head, sequence), numbered
 // split-major; a split is a balanced run of the row's range in virtual
 // pages (gw_plan.h: the two partial pages at the ends of a full window are
-// walked as one, so a 1024-token window is 64 pages of work, 16 per split).  Four waves per
-// workgroup take every fourth page of the split, each with its own online
-// softmax state (running max m, sum l, accumulator), merged in LDS at the end.
+// walked as one, so a 1024-token window is 64 pages of work: 2 splits of 32
+// at group size 1 or 2, 4 of 16 at group size 4).  The W waves of a
+// workgroup (8, or 4 at group size 4) take every W-th page of the split, 4
+// pages each on a full window, each wave with its own online softmax state
+// (running max m, sum l, accumulator), merged in LDS at the end.
 // The last workgroup of a (sequence, KV head) to finish merges the splits'
 // partials in split order (a counter per pair, reset by that workgroup).
 //
@@ -40,7 +42,6 @@ namespace gw {
 namespace {
 
 constexpr int kLocalD = 256;
-constexpr int kLocalWaves = 4;
 // Page-table rows up to this many entries are read whole into LDS.
 constexpr int kLocalPtLds = 2048;
 // Re-reads of one partial before the reducing workgroup gives up on it.
@@ -410,44 +411,83 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
 }
 
 template <int G, bool FP8>
-__global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(LocalAttnArgs a) {
-  // workgroups go split-major (every pair's split 0, then every pair's
-  // split 1, ...), rows fastest: a pair's splits are dispatched apart, which
-  // measures faster than dispatching them side by side
-  const int npairs = a.num_kv_heads * a.num_seqs;
-  const int split = uniform_i32((int)blockIdx.x / npairs), rem = (int)blockIdx.x % npairs;
-  const int g = uniform_i32(rem / a.num_seqs), s = uniform_i32(rem % a.num_seqs);
+__global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(LocalAttnArgs a) {
+  constexpr int kLocalWaves = local_waves(G);
+  constexpr int kLocalThreads = 64 * kLocalWaves;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
+  // Workgroups go split-major (every pair's split 0, then every pair's
+  // split 1, ...), rows fastest: a pair's splits are dispatched apart, which
+  // measures faster than dispatching them side by side.  With one row per
+  // sequence the sequences are the rows; with q_indptr the decode sequences
+  // (one row each; prompt rows go elsewhere) are numbered compactly, in
+  // order, so that the workgroups the grid holds for the prompt sequences
+  // come last and leave, instead of holding CUs ahead of working ones.
+  int split, g, s, row;
+  if (a.q_indptr == nullptr) {
+    const int npairs = a.num_kv_heads * a.num_seqs;
+    split = (int)blockIdx.x / npairs;
+    const int rem = (int)blockIdx.x % npairs;
+    g = rem / a.num_seqs;
+    s = row = rem % a.num_seqs;
+  } else {
+    // the decode sequences of 64-sequence chunk c0, as a lane mask, and
+    // the rows where each lane's sequence starts
+    auto chunk = [&](int c0, int& r0) __attribute__((always_inline)) {
+      const int sl = c0 + lane;
+      r0 = sl < a.num_seqs ? a.q_indptr[sl] : 0;
+      return (uint64_t)__ballot(sl < a.num_seqs && a.q_indptr[sl + 1] - r0 == 1);
+    };
+    int r0 = 0;
+    uint64_t m = chunk(0, r0);
+    int n_dec = __popcll(m);
+    for (int c0 = 64; c0 < a.num_seqs; c0 += 64) {
+      int r1;
+      n_dec += __popcll(chunk(c0, r1));
+    }
+    const int ndp = a.num_kv_heads * n_dec;
+    if (ndp == 0 || (int)blockIdx.x >= a.max_splits * ndp) return;
+    split = (int)blockIdx.x / ndp;
+    const int rem = (int)blockIdx.x % ndp;
+    g = rem / n_dec;
+    int k = rem % n_dec;   // rank of the sequence among the decode sequences
+    int c0 = 0;
+    while (k >= __popcll(m)) {   // ends: k < n_dec, the total count
+      k -= __popcll(m);
+      c0 += 64;
+      m = chunk(c0, r0);
+    }
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const int ls = __builtin_ctzll(__ballot(((m >> lane) & 1) && rank == k));
+    s = c0 + ls;
+    row = __builtin_amdgcn_readlane(r0, ls);
+  }
+  split = uniform_i32(split);
+  g = uniform_i32(g);
+  s = uniform_i32(s);
+  row = uniform_i32(row);
 
   // The page-table row (when it has at most kLocalPtLds entries) and the
-  // group's q are read in the same round trip as the sequence's length and
-  // row -- before it is known which pages the window covers -- and go to LDS.
-  // q is read from row s, which is the row whenever the decode sequences
-  // come first (or one row per sequence); it is read again otherwise.
+  // group's q are read in the same round trip as the sequence's length --
+  // before it is known which pages the window covers -- and go to LDS.
   const auto q_chunk = [&](int r) __attribute__((always_inline)) {   // chunk tid % 32 of head tid / 32
     return *reinterpret_cast<const u32x4*>(a.q + ((int64_t)r * a.num_q_heads + g * G + tid / 32) * kLocalD +
                                            8 * (tid % 32));
   };
   u32x4 qv = {0u, 0u, 0u, 0u};
-  if (s < a.num_rows && tid < 32 * G) qv = q_chunk(s);
-  int row = s;
-  if (a.q_indptr) {
-    row = ((CI32P)a.q_indptr)[s];
-    if (((CI32P)a.q_indptr)[s + 1] - row != 1) return;   // rows of prompts go elsewhere
-  }
+  if (tid < 32 * G) qv = q_chunk(row);
   const int L = ((CI32P)a.seq_lens)[s];
   const bool pt_lds = a.pt_stride <= kLocalPtLds;
-  int ptv[kLocalPtLds / 256] = {};
+  int ptv[kLocalPtLds / kLocalThreads] = {};
   if (pt_lds) {
     const int32_t* prow = a.page_table + (int64_t)s * a.pt_stride;
 #pragma unroll
-    for (int i = 0; i < kLocalPtLds / 256; ++i)
-      if (tid + 256 * i < a.pt_stride) ptv[i] = prow[tid + 256 * i];
+    for (int i = 0; i < kLocalPtLds / kLocalThreads; ++i)
+      if (tid + kLocalThreads * i < a.pt_stride) ptv[i] = prow[tid + kLocalThreads * i];
   }
   const int p = L - 1;
   const LocalWindow win = local_window(p, a.window);
-  const int nsplit = local_nsplit(win.nv);
+  const int nsplit = local_nsplit(win.nv, G);
   if (split >= nsplit) return;
   const int v0 = split_lo(win.nv, nsplit, split);
   const int v1 = split_lo(win.nv, nsplit, split + 1);
@@ -462,10 +502,9 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   __shared__ __attribute__((aligned(16))) uint32_t sm_q[G][128];
   if (pt_lds) {
 #pragma unroll
-    for (int i = 0; i < kLocalPtLds / 256; ++i)
-      if (tid + 256 * i < a.pt_stride) sm_pt[tid + 256 * i] = ptv[i];
+    for (int i = 0; i < kLocalPtLds / kLocalThreads; ++i)
+      if (tid + kLocalThreads * i < a.pt_stride) sm_pt[tid + kLocalThreads * i] = ptv[i];
   }
-  if (row != s && tid < 32 * G) qv = q_chunk(row);
   if (tid < 32 * G) {
     const int j = tid % 32;
     *reinterpret_cast<u32x4*>(&sm_q[tid / 32][4 * (j ^ ((j >> 3) & 7))]) = qv;
@@ -591,7 +630,10 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   }
   __syncthreads();
 
-  const int d = tid;   // 256 threads, one output dim each
+  // the first 256 threads take one output dim each; with 8 waves the others
+  // mirror dim 0, write nothing, and only meet the barriers
+  const bool dt = tid < kLocalD;
+  const int d = dt ? tid : 0;
   float o[G], M[G], lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -609,6 +651,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
     }
   }
   if (nsplit == 1) {
+    if (!dt) return;
 #pragma unroll
     for (int h = 0; h < G; ++h)
       a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = o[h] / lsum[h];
@@ -628,6 +671,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    if (!dt) break;
     const int64_t pi = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits + split;
     __hip_atomic_store(a.part_acc + pi * kLocalD + d, tag | f32_to_bits(o[h]), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -644,7 +688,7 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
   if (tid == 0)
     sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   lds_barrier();
-  if (!sm_last) return;
+  if (!sm_last || !dt) return;
   // The heads of the group are merged together, so their loads share one
   // round trip; a row's range of up to 68 pages has at most 4 splits.
   bool ok;
@@ -668,9 +712,9 @@ __global__ __launch_bounds__(256, G >= 4 ? 1 : 2) void local_decode_kernel(Local
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
   const int64_t n = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)n), block(256);
+  dim3 grid((unsigned)n);
 #define GW_LOCAL_CASE(G_, F_) \
-  if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, block, 0, stream, a); return hipGetLastError(); }
+  if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, dim3(64 * local_waves(G_)), 0, stream, a); return hipGetLastError(); }
   GW_LOCAL_CASE(1, false) GW_LOCAL_CASE(2, false) GW_LOCAL_CASE(4, false)
   GW_LOCAL_CASE(1, true) GW_LOCAL_CASE(2, true) GW_LOCAL_CASE(4, true)
 #undef GW_LOCAL_CASE

@@ -8,11 +8,15 @@
 
 namespace gw {
 
-// Local family: ranges up to the window (65 pages at window 1024) cut into
-// splits of at least 17 pages: 4 splits of 16-17 pages for a full window,
-// so 16 rows x 8 KV heads fill the GPU with 512 workgroups in one round.
-constexpr int kLocalMinPagesPerSplit = 17;
+// Local family: ranges up to the window (65 pages at window 1024).  A
+// workgroup has 8 waves at query-group size 1 or 2 and takes splits of at
+// least 33 pages: a full window is 2 splits, so 16 rows x 8 KV heads fill
+// the GPU with 256 workgroups of 8 waves in one round.  At group size 4 the
+// registers of 8 waves do not suffice: 4 waves, splits of at least 17 pages
+// (4 per full window, 512 workgroups).
 constexpr int kLocalMaxSplits = 16;
+__host__ __device__ constexpr int local_waves(int group) { return group >= 4 ? 4 : 8; }
+__host__ __device__ constexpr int local_min_pages_per_split(int group) { return group >= 4 ? 17 : 33; }
 
 // Global family: splits of at least 20 pages (320 tokens), at most 64 per
 // row unless that would put more than 256 pages in one split: 16 rows of
@@ -24,8 +28,8 @@ constexpr int kGlobalMaxPagesPerSplit = 256;
 
 __host__ __device__ inline int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 
-__host__ __device__ inline int local_nsplit(int n_pages) {
-  int k = cdiv_i(n_pages, kLocalMinPagesPerSplit);
+__host__ __device__ inline int local_nsplit(int n_pages, int group) {
+  int k = cdiv_i(n_pages, local_min_pages_per_split(group));
   k = k < 1 ? 1 : k;
   return k > kLocalMaxSplits ? kLocalMaxSplits : k;
 }
