@@ -611,7 +611,7 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   }
 
   asm volatile("" : "+v"(epoch));
-  // ---- merge the four waves in LDS, in wave order
+  // ---- merge the waves in LDS, in wave order
   __shared__ float sm_acc[kLocalWaves][G][kLocalD];
   __shared__ float sm_m[kLocalWaves][G], sm_l[kLocalWaves][G];
   __shared__ int sm_last;
@@ -690,7 +690,8 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   lds_barrier();
   if (!sm_last || !dt) return;
   // The heads of the group are merged together, so their loads share one
-  // round trip; a row's range of up to 68 pages has at most 4 splits.
+  // round trip; a row's range of up to 68 pages has at most 4 splits (at
+  // either split size).
   bool ok;
   if (nsplit <= 4) {
     ok = merge_splits<G, 4>(a, s, g * G, row, d, nsplit, tag);

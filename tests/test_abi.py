@@ -174,7 +174,8 @@ def test_empty_batches_are_noops():
 
 
 def test_workspace_plan():
-    # one window of 1024 tokens is 64 pages of work -> 4 splits of 16 pages;
+    # one window of 1024 tokens is 64 pages of work -> at most 4 splits of 16
+    # pages (the size query assumes query-group size 4, the most splits);
     # local partials are 8-byte (value, tag) pairs
     ws = gw.gw_attn_workspace_bytes(gw.GW_FAMILY_LOCAL, 16, 16, 16, 256, 8192, 1024, 1)
     assert ws >= 16 * 16 * 4 * 258 * 8
