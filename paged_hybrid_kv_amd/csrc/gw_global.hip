@@ -358,21 +358,13 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   }
 }
 
-// One page for the prompt rows: a wave takes one head block (16 heads) of NR
-// rows over all 512 dims, so no wave repeats another's scores and each K
-// and V fragment it reads from LDS feeds NR rows' products.  Per page:
-// S^T = K . Q^T per row (16 steps, K read in batches of 4 fragments), the
-// lazy online-softmax update per row, then O^T += V^T . P^T over 32 output
-// blocks of 16 dims (V read in batches of 4 blocks).  V of tokens past p_v
-// (slots past the workgroup's last row, possibly never written) is zeroed
-// in the operand registers.
+// The scores half of the page for the prompt rows: S^T = K . Q^T per row
+// (16 steps over 512 dims, two accumulation chains, K read in batches of 4
+// fragments).
 template <bool COMPRESSED, int NR>
-__device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m_run)[NR], float (&l_run)[NR],
-                                                 const uint8_t* pg, const bf16x8 (&qf)[NR][16], int tok_page0,
-                                                 const int (&p)[NR], int p_v, int g, int l16, int v_lane_off,
-                                                 float scale_log2) {
+__device__ __forceinline__ void global_rows_scores(f32x4 (&s)[NR][2], const uint8_t* pg, const bf16x8 (&qf)[NR][16],
+                                                   int g, int l16) {
   using PG = GlobalPage<COMPRESSED>;
-  f32x4 s[NR][2];
 #pragma unroll
   for (int r = 0; r < NR; ++r) s[r][0] = s[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -381,13 +373,27 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (4 * hk + k) + g, l16));
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         s[r][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[r][4 * hk + k], s[r][k & 1], 0, 0, 0);
   }
+}
+
+// One page for the prompt rows: a wave takes one head block (16 heads) of NR
+// rows over all 512 dims, so no wave repeats another's scores and each K
+// and V fragment it reads from LDS feeds NR rows' products.  Per page:
+// the scores (global_rows_scores, issued a page ahead), the lazy
+// online-softmax update per row, then O^T += V^T . P^T over 32 output
+// blocks of 16 dims (V read in batches of 4 blocks).  V of tokens past p_v
+// (slots past the workgroup's last row, possibly never written) is zeroed
+// in the operand registers.
+template <bool COMPRESSED, int NR>
+__device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m_run)[NR], float (&l_run)[NR],
+                                                 const uint8_t* pg, const f32x4 (&s)[NR][2], int tok_page0,
+                                                 const int (&p)[NR], int p_v, int g, int l16, int v_lane_off,
+                                                 float scale_log2) {
   const int tok0 = tok_page0 + 4 * g;
   s16x4 pb[NR];
 #pragma unroll
@@ -559,13 +565,24 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   }
   const int v_lane_off = global_v_lane_off<COMPRESSED>(0, g, l16);
 
+  // software pipeline, one page deep: iteration i has pages i and i + 1 in
+  // LDS; page i + 1's scores go out beside page i's weights and products
+  if (nu > kPerWave) wait_groups_after<kPerWave + 1>(min(NS - 2, n - 1));
+  else wait_groups_after<kPerWave>(min(NS - 2, n - 1));
+  lds_barrier();
+  f32x4 sc[NR][2];
+  global_rows_scores<COMPRESSED, NR>(sc, ring[0], qf, g, l16);
   for (int i = 0; i < n; ++i) {
-    if (nu > kPerWave) wait_groups_after<kPerWave + 1>(min(NS - 2, n - 1 - i));
-    else wait_groups_after<kPerWave>(min(NS - 2, n - 1 - i));
-    lds_barrier();   // page i is in LDS for every wave; page i - 1 is done
+    if (nu > kPerWave) wait_groups_after<kPerWave + 1>(max(0, min(NS - 3, n - 2 - i)));
+    else wait_groups_after<kPerWave>(max(0, min(NS - 3, n - 2 - i)));
+    lds_barrier();   // pages i and i + 1 are in LDS for every wave; page i - 1 is done
     if (i + NS - 1 < n) issue_page(i + NS - 1);
-    global_rows_page<COMPRESSED, NR>(acc, m_run, l_run, ring[i % NS], qf, i * 16, pr, p_last, g, l16, v_lane_off,
+    f32x4 sn[NR][2];
+    global_rows_scores<COMPRESSED, NR>(sn, ring[min(i + 1, n - 1) % NS], qf, g, l16);
+    global_rows_page<COMPRESSED, NR>(acc, m_run, l_run, ring[i % NS], sc, i * 16, pr, p_last, g, l16, v_lane_off,
                                      a.scale_log2);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) { sc[r][0] = sn[r][0]; sc[r][1] = sn[r][1]; }
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -672,8 +689,8 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int m
   if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)items), block(512);
   if (compressed) {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 4>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 5>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 5>), grid, block, 0, stream, a);
   } else {
     if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 1, 4>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 1, 4>), grid, block, 0, stream, a);
