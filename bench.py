@@ -119,8 +119,9 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 def cpu_baseline(step):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    the decode rows of layers 0 and 1 (local) and 5 (global)."""
+    """The oracle as it stands, on a bounded sample of the same workload
+    (about 10-15 s of host work): the decode rows of layers 0-4 and 6
+    (local) and 5 and 11 (global)."""
     import numpy as np
     import torch
     from oracle import attention as OA, codecs as OC, rope as OR
@@ -132,7 +133,7 @@ def cpu_baseline(step):
     except Exception:  # pragma: no cover
         threads = 1
     sh = step.shape
-    layers = [0, 1, 5]
+    layers = [0, 1, 2, 3, 4, 5, 6, 11]
     host = {}
     for l in layers:
         d = layer_draws(sh, l, False, "cuda")
@@ -154,13 +155,11 @@ def cpu_baseline(step):
             if local:
                 k = OC.bf16_round(np.concatenate([h["k_prior"][sel_p], h["k_new"][sel_n]]).astype(np.float64))
                 k = OC.bf16_round(OR.rotate_local(k, pos[:, None]))
-                lo = int(pos[0])
                 K = np.full((L, sh.local_kv_heads, 256), np.nan)
                 V = np.full((L, sh.local_kv_heads, 256), np.nan)
                 K[pos], V[pos] = k, v
                 OA.attend_sequence(q, K, V, 1 / 16, sh.window)
                 nbytes += min(L, sh.window) * sh.local_kv_heads * 256 * 4
-                del lo
             else:
                 k_rot = OC.bf16_round(OR.rotate_global(v, pos)[:, :128])
                 K = OA.k_from_compressed(v, k_rot)[:, None, :]
@@ -169,7 +168,8 @@ def cpu_baseline(step):
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": "decode rows (16 slots) of layers 0, 1 (local) and 5 (global) of the same step: "
+            "sample": f"decode rows (16 slots) of layers {', '.join(str(l) for l in layers if not sh.is_global(l))} "
+                      f"(local) and {', '.join(str(l) for l in layers if sh.is_global(l))} (global) of the same step: "
                       "fp64 rotation, bf16 rounding and naive masked softmax over contiguous K/V; "
                       f"{nbytes} algorithmic KV bytes; os.cpu_count()={os.cpu_count()}"}
 
