@@ -223,7 +223,7 @@ __device__ __forceinline__ void load_bf16_n(const uint16_t* p, float (&x)[N]) {
 // A workgroup takes kRowsHeads KV heads of its page: every head's inputs
 // are loaded first, in one round trip, and the rotary factors of a slot
 // (the same for every head) once.
-constexpr int kRowsHeads = 4;
+constexpr int kRowsHeads = 2;
 
 template <bool FP8, bool ROPE>
 __global__ __launch_bounds__(256) void append_local_rows_kernel(AppendArgs a) {
