@@ -689,8 +689,8 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int m
   if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)items), block(512);
   if (compressed) {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 5>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 5>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 4>), grid, block, 0, stream, a);
   } else {
     if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 1, 4>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 1, 4>), grid, block, 0, stream, a);
