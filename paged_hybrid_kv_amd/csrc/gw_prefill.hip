@@ -429,7 +429,7 @@ hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int
     const unsigned n = items(prefill_rows_per_wg<G_>());                                            \
     if (n == 0) return hipSuccess;                                                                  \
     if (n > 65535) return hipErrorInvalidConfiguration;                                             \
-    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 5, kPrefillQB>), dim3(a.num_kv_heads, n), dim3(64 * (8 / kPrefillQB)), 0, stream, a); \
+    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 4, kPrefillQB>), dim3(a.num_kv_heads, n), dim3(64 * (8 / kPrefillQB)), 0, stream, a); \
     return hipGetLastError();                                                                       \
   }
   GW_PREFILL_CASE(1, false) GW_PREFILL_CASE(2, false) GW_PREFILL_CASE(4, false)
