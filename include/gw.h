@@ -141,7 +141,14 @@ int gw_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t rot_d
  * record is V plus the rotated quarter of K).
  *
  *   k_raw : bf16 [n_tok][num_kv_heads][head_dim], K before rotation.
- *           LOCAL only; must be NULL for the GLOBAL families (K is V).
+ *           LOCAL: required.  GLOBAL families: optional -- NULL when K is V
+ *           before rotation (the tied store); otherwise only its first 128
+ *           dims are read, the quarter that rotates into K_rot.  The record
+ *           keeps V for dims 128..511 in both global layouts, so a model whose
+ *           K there is V * w_k (a per-dim norm weight on K: Gewell post, "the
+ *           Why" -- only the rotated quarter differs in what is stored) passes
+ *           q with dims 128..511 multiplied by w_k to the attention call,
+ *           which gives the same scores.
  *   v     : bf16 [n_tok][num_kv_heads][head_dim].
  *   seq_idx, pos : int32 [n_tok]; token i goes to sequence seq_idx[i] at
  *           position pos[i], i.e. page page_table[seq_idx[i]*pt_stride +
@@ -155,8 +162,9 @@ int gw_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t rot_d
  * round to bf16 (nearest-even); for e4m3 round that bf16 value once more to
  * e4m3 (nearest-even, saturating to +-448, NaN kept).
  *   LOCAL:             K block <- rotated K, V block <- V.
- *   GLOBAL_COMPRESSED: V block <- V, K_rot block <- rotated V[0:128].
- *   GLOBAL_FULL:       K block <- [rotated V[0:128], V[128:512]], V <- V.
+ *   GLOBAL_COMPRESSED: V block <- V, K_rot block <- rotated K[0:128]
+ *                      (K = k_raw, or V when k_raw is NULL).
+ *   GLOBAL_FULL:       K block <- [rotated K[0:128], V[128:512]], V <- V.
  * E4M3 with a GLOBAL family: GW_ERR_UNSUPPORTED ("gw_kv_append: e4m3
  * supports only the local family").  n_tok == 0 is a no-op returning GW_OK.
  */

@@ -36,6 +36,8 @@ import math
 
 import numpy as np
 
+from . import rope as _rope
+
 
 def window_lo(p: int, window: int | None) -> int:
     """First attended key position for a query at position p."""
@@ -157,3 +159,17 @@ def k_from_compressed(v, k_rot):
     k_rot = np.asarray(k_rot, dtype=np.float64)
     r = k_rot.shape[-1]
     return np.concatenate([k_rot, v[..., r:]], axis=-1)
+
+
+def global_k(v, pos, w_k=None):
+    """A global layer's K at positions pos, from its V and K's norm weight.
+
+    pegainfer "Gemma 4" page, Architecture notes: V is the K projection's
+    output after a norm with no scale; K is that same output after k_norm,
+    whose learned per-dim weight w_k is the only difference, and then the
+    proportional RoPE (first 128 of 512 dims).  So K = RoPE(V * w_k); with
+    w_k None (or all ones) K is V before rotation, the tied store.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    k = v if w_k is None else v * np.asarray(w_k, dtype=np.float64)
+    return _rope.rotate_global(k, pos)

@@ -197,7 +197,6 @@ int gw_kv_append(const gw_pool_desc* pool, const void* k_raw, const void* v, con
     if (pool->rot_dim != 0 && !rope)
       return fail(GW_ERR_INVALID_ARG, fn, "rot_dim %d needs rotary tables", pool->rot_dim);
   } else {
-    if (k_raw) return fail(GW_ERR_INVALID_ARG, fn, "k_raw must be null for the global family (K is V)");
     if (!rope) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
   }
   if (n_tok == 0) return ok();

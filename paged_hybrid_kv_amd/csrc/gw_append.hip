@@ -143,7 +143,9 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   int s, ps;
   if (!append_target(a, tok, s, ps)) return;
   const int page = a.page_table[(int64_t)s * a.pt_stride + (ps >> 4)];
-  const GlobalRecordLane r = global_record_lane(a.v + (int64_t)tok * 512, a.rope_cos, a.rope_sin, ps, l);
+  const uint16_t* vsrc = a.v + (int64_t)tok * 512;
+  const uint16_t* ksrc = a.k_raw ? a.k_raw + (int64_t)tok * 512 : vsrc;
+  const GlobalRecordLane r = global_record_lane(vsrc, ksrc, a.rope_cos, a.rope_sin, ps, l);
   put_global_record<COMPRESSED>(a.pool + (int64_t)page * a.page_bytes, r, ps & 15, l);
 }
 
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(256) void append_global_rows_kernel(AppendArgs a) {
   if (tid < 128) {
     const int c = tid >> 4, t = tid & 15;
     if (t >= rp.t0 && t <= rp.t1) {
-      const GlobalRecordLane r = global_record_lane(row_v(t), a.rope_cos, a.rope_sin, rp.pg * kPage + t, c);
+      const GlobalRecordLane r = global_record_lane(row_v(t), row_v(t), a.rope_cos, a.rope_sin, rp.pg * kPage + t, c);
       *reinterpret_cast<uint4*>(kblock + (c * 16 + t) * 16) = r.ka;
       *reinterpret_cast<uint4*>(kblock + ((c + 8) * 16 + t) * 16) = r.kb;
     }

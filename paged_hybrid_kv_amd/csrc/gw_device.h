@@ -222,19 +222,23 @@ struct PageIds {
 // "the Why": K and V are tied and only K's first 128 dims rotate, so the
 // record is V plus the rotated quarter of K).  Lane l holds V chunk l (dims
 // 8l .. 8l+7, bf16 as given); lanes 0..7 also hold K chunks l and l + 8
-// (dims 8l .. and 64 + 8l ..), rotated as rotate-half pairs (i, i + 64) by
-// position pos from the fp32 tables [pos][64], rounded to bf16.
+// (dims 8l .. and 64 + 8l ..) of ksrc -- V itself when K is V before
+// rotation, or the caller's K when it differs there (a norm weight on K) --
+// rotated as rotate-half pairs (i, i + 64) by position pos from the fp32
+// tables [pos][64], rounded to bf16.
 struct GlobalRecordLane {
   uint4 v, ka, kb;
 };
-__device__ __forceinline__ GlobalRecordLane global_record_lane(const uint16_t* vsrc, const float* rope_cos,
-                                                               const float* rope_sin, int pos, int l) {
+__device__ __forceinline__ GlobalRecordLane global_record_lane(const uint16_t* vsrc, const uint16_t* ksrc,
+                                                               const float* rope_cos, const float* rope_sin, int pos,
+                                                               int l) {
   GlobalRecordLane r;
   r.v = *reinterpret_cast<const uint4*>(vsrc + 8 * l);
   r.ka = r.kb = uint4{0u, 0u, 0u, 0u};
   if (l < 8) {
-    const uint4 praw = *reinterpret_cast<const uint4*>(vsrc + 64 + 8 * l);
-    const uint32_t xa_p[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+    const uint4 araw = ksrc == vsrc ? r.v : *reinterpret_cast<const uint4*>(ksrc + 8 * l);
+    const uint4 praw = *reinterpret_cast<const uint4*>(ksrc + 64 + 8 * l);
+    const uint32_t xa_p[4] = {araw.x, araw.y, araw.z, araw.w};
     const uint32_t xb_p[4] = {praw.x, praw.y, praw.z, praw.w};
     const float* cp = rope_cos + (int64_t)pos * 64 + 8 * l;
     const float* sp = rope_sin + (int64_t)pos * 64 + 8 * l;

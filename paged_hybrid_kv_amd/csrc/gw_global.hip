@@ -243,7 +243,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   // page once the page has landed
   const bool append_here = a.v_new != nullptr && split == nsplit - 1;
   GlobalRecordLane rec{};
-  if (append_here && wv == 0) rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+  if (append_here && wv == 0)
+    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
   asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
   if (append_here && wv == 0)
     put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,

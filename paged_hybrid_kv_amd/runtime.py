@@ -128,7 +128,12 @@ def upload_local(case: LocalCase, device="cuda", fill_byte: int | None = 0xFF,
 
 
 def upload_global(case: GlobalCase, compressed: bool = True, device="cuda",
-                  fill_byte: int | None = 0xFF, append_chunk: int = 1 << 17) -> DeviceCase:
+                  fill_byte: int | None = 0xFF, append_chunk: int = 1 << 17,
+                  k_raw: np.ndarray | None = None, q: np.ndarray | None = None) -> DeviceCase:
+    """Append the case's tokens into a fresh pool and stage its queries.
+    k_raw [n_tok][512] (fp32, sent as bf16), when given, is K before rotation
+    for the tokens (its first 128 dims make the rotated quarter); q, when
+    given, replaces the case's queries (the caller's own q for that K)."""
     require_gpu()
     fam = gw.GW_FAMILY_GLOBAL_COMPRESSED if compressed else gw.GW_FAMILY_GLOBAL_FULL
     pool = Pool(fam, gw.GW_KV_BF16, case.seqs.num_pages, 1, 128, device, fill_byte)
@@ -143,9 +148,10 @@ def upload_global(case: GlobalCase, compressed: bool = True, device="cuda",
     for c0 in range(0, n, append_chunk):
         c1 = min(n, c0 + append_chunk)
         v = to_bf16_dev(case.v[c0:c1], device)
-        gw.gw_kv_append(pool.desc, None, v, i32_dev(case.tok_seq[c0:c1], device),
+        k = None if k_raw is None else to_bf16_dev(k_raw[c0:c1], device)
+        gw.gw_kv_append(pool.desc, k, v, i32_dev(case.tok_seq[c0:c1], device),
                         i32_dev(case.tok_pos[c0:c1], device), c1 - c0, pt, stride, cos, sin)
-    q = to_bf16_dev(case.q, device)
+    q = to_bf16_dev(case.q if q is None else q, device)
     single = bool((case.q_len == 1).all())
     return DeviceCase(pool=pool, q=q, q_indptr=None if single else i32_dev(case.q_indptr, device),
                       seq_lens=i32_dev(case.seqs.lens, device), page_table=pt, pt_stride=stride,

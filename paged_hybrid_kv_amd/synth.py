@@ -118,6 +118,9 @@ class GlobalCase:
     tok_pos: np.ndarray
     rope: bool                  # rotate K's first rot_dim dims (theta 1e6, denominator 512)
     scale: float
+    # K's per-dim norm weight [512] (K = V * w_k before rotation), None when K = V;
+    # every value is 1 + k/64, |k| <= 32, so exact in bf16
+    w_k: np.ndarray | None = None
 
     @property
     def q_indptr(self) -> np.ndarray:
@@ -177,7 +180,7 @@ def local_case(name, seed, lens, window, num_q_heads, num_kv_heads, q_len=None,
 
 def global_case(name, seed, lens, num_q_heads=32, q_len=None, q_scale=1.0,
                 v_scale=1.0, rope=True, head_dim=512, rot_dim=128,
-                extra_pages=0) -> GlobalCase:
+                extra_pages=0, k_norm=False) -> GlobalCase:
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens(rng) if callable(lens) else lens, dtype=np.int64)
     S = lens.shape[0]
@@ -186,9 +189,11 @@ def global_case(name, seed, lens, num_q_heads=32, q_len=None, q_scale=1.0,
     tok_seq, tok_pos = _stored_tokens(seqs, None)
     q = _normal(rng, (int(q_len.sum()), num_q_heads, head_dim), q_scale)
     v = _normal(rng, (tok_seq.shape[0], head_dim), v_scale)
+    w_k = (1.0 + rng.integers(-32, 32, size=head_dim, endpoint=True) / 64.0).astype(np.float32) \
+        if k_norm else None
     return GlobalCase(name=name, seqs=seqs, num_q_heads=num_q_heads, head_dim=head_dim,
                       rot_dim=rot_dim, q_len=q_len, q=q, v=v, tok_seq=tok_seq,
-                      tok_pos=tok_pos, rope=rope, scale=float(1.0 / np.sqrt(head_dim)))
+                      tok_pos=tok_pos, rope=rope, scale=float(1.0 / np.sqrt(head_dim)), w_k=w_k)
 
 
 # ----------------------------------------------------------------------------

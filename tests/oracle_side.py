@@ -37,14 +37,23 @@ def local_seq(case, s):
 
 
 def global_seq(case, s):
-    """fp64 K, V [L][1][512] of global sequence s (K rebuilt from the record)."""
+    """fp64 K, V [L][1][512] of global sequence s (K rebuilt from the record).
+
+    With a norm weight on K (case.w_k), K before rotation is the model's
+    bf16(V * w_k): its rotated quarter is stored rounded to bf16, and dims
+    128..511 are that K itself, not V."""
     sel = case.tok_seq == s
     pos = case.tok_pos[sel]
     v = OC.bf16_round(case.v[sel].astype(np.float64))
-    k_rot = v[:, :128]
-    if case.rope:
-        k_rot = OC.bf16_round(OR.rotate_global(v, pos)[:, :128])
-    k = OA.k_from_compressed(v, k_rot)
+    if case.w_k is None:
+        k_rot = v[:, :128]
+        if case.rope:
+            k_rot = OC.bf16_round(OR.rotate_global(v, pos)[:, :128])
+        k = OA.k_from_compressed(v, k_rot)
+    else:
+        k_pre = OC.bf16_round(v * case.w_k.astype(np.float64))
+        k = OA.global_k(k_pre, pos if case.rope else np.zeros_like(pos))
+        k[:, :128] = OC.bf16_round(k[:, :128])
     L = int(case.seqs.lens[s])
     K = np.full((L, 512), np.nan)
     V = np.full((L, 512), np.nan)

@@ -90,7 +90,6 @@ def append(d, k=FAKE, v=FAKE, n=4, stride=8, cos=FAKE, sin=FAKE):
     (lambda: append(desc(), cos=None), gw.GW_ERR_INVALID_ARG, "both"),
     (lambda: append(desc(), cos=None, sin=None), gw.GW_ERR_INVALID_ARG, "needs rotary tables"),
     (lambda: append(desc(rot=0)), gw.GW_ERR_INVALID_ARG, "takes no rotary tables"),
-    (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_FULL)), gw.GW_ERR_INVALID_ARG, "k_raw must be null"),
     (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_FULL), k=None, cos=None, sin=None),
      gw.GW_ERR_INVALID_ARG, "needs rotary tables"),
     (lambda: append(desc(), k=None), gw.GW_ERR_INVALID_ARG, "k_raw is null"),

@@ -134,3 +134,64 @@ def test_append_global(compressed):
         tol = np.maximum(np.abs(k_rot), 2.0 ** -126) * 2.0 ** -7
         assert np.all(np.abs(Kr - k_rot) <= tol)
         assert np.mean(Kr == k_rot) > 0.95
+
+
+def k_before_rotation(case):
+    """The K a k_norm model hands over: the stored bf16 V times w_k.  Both
+    carry at most 8 significant bits, so the fp32 product is exact and the
+    bf16 cast on upload rounds it once, as the oracle side does."""
+    vb = torch.from_numpy(case.v).to(torch.bfloat16).float().numpy()
+    return vb * case.w_k
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_norm_weighted_k(rope):
+    """K = V * w_k before rotation (a per-dim norm weight on K): the append
+    takes that K for the rotated quarter and the caller folds w_k into q's
+    dims 128..511; the output matches the oracle's attention over the true K,
+    and both records agree bit for bit."""
+    lens = [1, 33, 700, 4097]
+    case = SY.global_case("knorm", 38, lens, num_q_heads=32, rope=rope, k_norm=True)
+    k_raw = k_before_rotation(case)
+    q_fold = case.q.copy()
+    q_fold[..., 128:] *= case.w_k[128:]
+    outs = []
+    for compressed in (True, False):
+        dc = RT.upload_global(case, compressed=compressed, k_raw=k_raw, q=q_fold)
+        outs.append(RT.attend(dc).cpu().numpy())
+        del dc
+    assert np.array_equal(outs[0], outs[1]), "compressed and full records differ"
+    mx = check(case, outs[0], f"k_norm rope={rope}")
+    print(f"global k_norm rope={rope} max abs err {mx:.2e}", flush=True)
+    # the tied store of the same V gives another answer: the weight matters
+    tied = SY.global_case("knorm", 38, lens, num_q_heads=32, rope=rope)
+    _, ot = run(tied)
+    assert np.abs(ot - outs[0]).max() > 1e-2
+
+
+def test_append_global_norm_weighted_k():
+    """The record's rotated quarter comes from k_raw, V from v, in both layouts."""
+    case = SY.global_case("append_knorm", 39, [40, 300], rope=True, k_norm=True)
+    k_raw = k_before_rotation(case)
+    for compressed in (True, False):
+        dc = RT.upload_global(case, compressed=compressed, k_raw=k_raw)
+        torch.cuda.synchronize()
+        pb = dc.pool.buf.cpu().numpy()
+        for s in range(case.seqs.S):
+            L = int(case.seqs.lens[s])
+            A, B = OP.global_codes(pb, case.seqs.page_table[s], L, compressed)
+            sel = case.tok_seq == s
+            v = OC.bf16_round(case.v[sel].astype(np.float64))
+            k_pre = OC.bf16_round(v * case.w_k.astype(np.float64))
+            k_rot = OC.bf16_round(OR.rotate_global(k_pre, case.tok_pos[sel])[:, :128])
+            if compressed:
+                Vg, Kr = OC.bf16_decode(A), OC.bf16_decode(B)
+            else:
+                Kg, Vg = OC.bf16_decode(A), OC.bf16_decode(B)
+                assert np.array_equal(Kg[:, 128:], v[:, 128:])
+                Kr = Kg[:, :128]
+            assert np.array_equal(Vg, v)
+            tol = np.maximum(np.abs(k_rot), 2.0 ** -126) * 2.0 ** -7
+            assert np.all(np.abs(Kr - k_rot) <= tol)
+            assert np.mean(Kr == k_rot) > 0.95
+        del dc

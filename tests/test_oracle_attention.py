@@ -170,3 +170,52 @@ def test_keys_outside_the_window_are_never_read():
     got0 = A.attend(q[:1], Kn, Vn, pos[:1], 0.5, 16)   # row 0's window 25..40 holds NaN at 30..39
     assert np.isnan(got0[0, 2:]).all()      # heads of KV head 1 read it: NaN propagates
     assert np.max(np.abs(got0[0, :2] - ref[0, :2])) < 1e-13
+
+
+def test_global_k_with_unit_weight_is_the_tied_k():
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((30, 512))
+    pos = rng.integers(0, 100000, size=30)
+    assert np.array_equal(A.global_k(v, pos), R.rotate_global(v, pos))
+    assert np.array_equal(A.global_k(v, pos, np.ones(512)), R.rotate_global(v, pos))
+
+
+def test_global_k_weight_applies_before_rotation():
+    """Dims 128..511 never rotate, so there K is V * w_k itself; dims 0..127
+    are a rotation of (V * w_k) in the pairs (i, i + 64), which keeps each
+    pair's length.  Weighting after rotation would break the second."""
+    rng = np.random.default_rng(22)
+    v = rng.standard_normal((25, 512))
+    w = rng.uniform(0.25, 2.0, size=512)
+    pos = rng.integers(1, 200000, size=25)
+    k = A.global_k(v, pos, w)
+    kw = v * w
+    assert np.array_equal(k[:, 128:], kw[:, 128:])
+    np.testing.assert_allclose(k[:, :64] ** 2 + k[:, 64:128] ** 2,
+                               kw[:, :64] ** 2 + kw[:, 64:128] ** 2, rtol=1e-12)
+    assert not np.allclose(k[:, :128], kw[:, :128])
+    after = R.rotate_global(v, pos)[:, :128] * w[:128]
+    assert not np.allclose(after[:, :64] ** 2 + after[:, 64:128] ** 2,
+                           kw[:, :64] ** 2 + kw[:, 64:128] ** 2)
+
+
+def test_norm_weight_folds_into_q():
+    """Attention over K = RoPE(V * w_k) equals attention over the stored record
+    (rotated quarter of that K, V for dims 128..511) with q's dims 128..511
+    multiplied by w_k: each score sum_d q_d K_d is the same sum."""
+    rng = np.random.default_rng(23)
+    L = 50
+    v = rng.standard_normal((L, 512))
+    w = rng.uniform(0.25, 2.0, size=512)
+    pos = np.arange(L)
+    k = A.global_k(v, pos, w)
+    q = rng.standard_normal((2, 8, 512))
+    o_true = A.attend(q, k[:, None], v[:, None], [L - 2, L - 1], 512 ** -0.5, None)
+    q_fold = q.copy()
+    q_fold[..., 128:] *= w[128:]
+    k_rec = A.k_from_compressed(v, k[:, :128])
+    o_fold = A.attend(q_fold, k_rec[:, None], v[:, None], [L - 2, L - 1], 512 ** -0.5, None)
+    np.testing.assert_allclose(o_fold, o_true, rtol=1e-12, atol=1e-13)
+    # without the fold the weight is lost beyond dim 128
+    o_nofold = A.attend(q, k_rec[:, None], v[:, None], [L - 2, L - 1], 512 ** -0.5, None)
+    assert np.abs(o_nofold - o_true).max() > 1e-3
