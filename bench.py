@@ -180,7 +180,8 @@ def config_throughput(iters=30):
     same seeded recipes, the pools are filled on the device with torch's
     seeded generator): local bf16 (16 slots, contexts U[1024, 8192], window
     1024, 16 q / 8 KV heads), global tied (8 slots x 131072 tokens, 32 q / 1
-    KV head, compressed and full records) and local e4m3 (64 slots x 8192).
+    KV head, compressed and full records, in bf16 and in e4m3 pools) and
+    local e4m3 (64 slots x 8192).
     Calls run back to back over pool replicas whose total exceeds the 256 MB
     last-level cache; returns {name: {us, GB_s, pct_of_peak, tok_s, bytes}}."""
     import numpy as np
@@ -212,12 +213,12 @@ def config_throughput(iters=30):
         return RT.DeviceCase(pool, q, None, RT.i32_dev(lens), pt, stride, len(lens), len(lens), 1, max_len,
                              16, 1 / 16, 1024)
 
-    def global_pool(compressed):
+    def global_pool(compressed, fp8=False):
         rng = np.random.default_rng(3)
         lens = np.full(8, 131072)
         seqs = SY.make_page_table(rng, lens)
         fam = gw.GW_FAMILY_GLOBAL_COMPRESSED if compressed else gw.GW_FAMILY_GLOBAL_FULL
-        pool = RT.Pool(fam, gw.GW_KV_BF16, seqs.num_pages, 1, 128, dev)
+        pool = RT.Pool(fam, gw.GW_KV_E4M3 if fp8 else gw.GW_KV_BF16, seqs.num_pages, 1, 128, dev)
         pt, stride = RT.i32_dev(seqs.page_table), seqs.page_table.shape[1]
         cos, sin = RT.rope_tables(131072, 128, 512, RT.GLOBAL_THETA)
         g = torch.Generator(device=dev)
@@ -247,12 +248,13 @@ def config_throughput(iters=30):
     res["local_bf16"] = timed(c2, int(sum(min(int(L), 1024) for L in lens2)) * 8 * 256 * 2 * 2, 16)
     del c2
     torch.cuda.empty_cache()
-    for compressed in (True, False):
-        dc = global_pool(compressed)
-        res["global_" + ("compressed" if compressed else "full")] = timed(
-            [dc], 8 * 131072 * (1280 if compressed else 2048), 8)
-        del dc
-        torch.cuda.empty_cache()
+    for fp8 in (False, True):
+        for compressed in (True, False):
+            dc = global_pool(compressed, fp8)
+            res["global_" + ("compressed" if compressed else "full") + ("_e4m3" if fp8 else "")] = timed(
+                [dc], 8 * 131072 * (640 if compressed else 1024) * (1 if fp8 else 2), 8)
+            del dc
+            torch.cuda.empty_cache()
     c4 = [local_pool([8192] * 64, True, 4, r) for r in range(2)]
     res["local_fp8"] = timed(c4, 64 * 1024 * 8 * 256 * 2, 64)
     del c4

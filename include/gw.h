@@ -46,7 +46,7 @@ extern "C" {
 typedef enum gw_status {
   GW_OK = 0,
   GW_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum value   */
-  GW_ERR_UNSUPPORTED = -2, /* valid but not served (e.g. e4m3 global pool)  */
+  GW_ERR_UNSUPPORTED = -2, /* valid but not served (e.g. group size > 8)     */
   GW_ERR_GEOMETRY = -3,    /* shape does not match the family's layout      */
   GW_ERR_WORKSPACE = -4,   /* workspace smaller than gw_attn_workspace_bytes */
   GW_ERR_HIP = -5          /* a HIP launch failed; message has the reason   */
@@ -62,7 +62,7 @@ typedef enum gw_family {
 
 typedef enum gw_kv_dtype {
   GW_KV_BF16 = 1, /* 2-byte bfloat16                                        */
-  GW_KV_E4M3 = 2  /* 1-byte OCP e4m3 (E4M3FN), scale 1.0; local family only */
+  GW_KV_E4M3 = 2  /* 1-byte OCP e4m3 (E4M3FN), scale 1.0                    */
 } gw_kv_dtype;
 
 /* ------------------------------------------------------------ the pool -- */
@@ -75,7 +75,7 @@ typedef enum gw_kv_dtype {
  *   LOCAL:             page_size 16, head_dim 256, rot_dim 256 (or 0 = K is
  *                      stored as given), num_kv_heads >= 1, bf16 or e4m3.
  *   GLOBAL_COMPRESSED: page_size 16, head_dim 512, rot_dim 128, one KV head,
- *                      bf16.
+ *                      bf16 or e4m3 (e4m3: decode rows only).
  *   GLOBAL_FULL:       as GLOBAL_COMPRESSED.
  *
  * Element order inside a page (elements of kv_dtype):
@@ -90,7 +90,10 @@ typedef enum gw_kv_dtype {
  *             (u < 4, l < 64, j < 4, i < 4)
  *   GLOBAL_COMPRESSED page = V block [16][512], then K_rot block [16][128]
  *   GLOBAL_FULL page       = K block [16][512], then V block [16][512]
- *     each block chunk-major: element (c*16 + t)*8 + e holds X[t][8c + e].
+ *     each block chunk-major, a chunk being 16 bytes of one token:
+ *     bf16: element (c*16 + t)*8 + e   holds X[t][8c + e]
+ *     e4m3: element (c*16 + t)*16 + e  holds X[t][16c + e]
+ *   (page bytes: compressed 20480 bf16 / 10240 e4m3, full 32768 / 16384)
  * (The orders put the 16 bytes one GPU lane loads next to the 16 bytes its
  * neighbour lane loads, so every page is read with whole 1 KiB wave loads.)
  */
@@ -165,8 +168,8 @@ int gw_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t rot_d
  *   GLOBAL_COMPRESSED: V block <- V, K_rot block <- rotated K[0:128]
  *                      (K = k_raw, or V when k_raw is NULL).
  *   GLOBAL_FULL:       K block <- [rotated K[0:128], V[128:512]], V <- V.
- * E4M3 with a GLOBAL family: GW_ERR_UNSUPPORTED ("gw_kv_append: e4m3
- * supports only the local family").  n_tok == 0 is a no-op returning GW_OK.
+ * For an e4m3 pool every stored element, K_rot and V alike, is the e4m3
+ * code of the bf16 record element.  n_tok == 0 is a no-op returning GW_OK.
  */
 int gw_kv_append(const gw_pool_desc* pool /* host */, const void* k_raw, const void* v,
                  const int32_t* seq_idx, const int32_t* pos, int32_t n_tok,
@@ -229,8 +232,10 @@ int gw_decode_attn_local(const gw_pool_desc* pool /* host */, const void* q,
                          int32_t max_seq_len, int32_t window, float scale, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16).
- * num_q_heads 16 or 32.  The two layouts give bit-identical results.
+/* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16
+ * or e4m3).  num_q_heads 16 or 32.  The two layouts give bit-identical
+ * results.  An e4m3 pool is read as the exact bf16 values of its codes; it
+ * serves decode rows only: max_q_len > 1 returns GW_ERR_UNSUPPORTED.
  * v_new: bf16 [num_rows][512] (K is V before rotation), with the rotary
  * tables fp32 [max_pos][64]; NULL when the pool already holds the rows. */
 int gw_decode_attn_global(const gw_pool_desc* pool /* host */, const void* q,

@@ -25,7 +25,9 @@ Local family, per page: [Hkv][K, V][block], block = 16 tokens x 256 dims.
                       u<4, l<64, j<4, i<4
 Global family, compressed page: V block [16][512] then K_rot block [16][128];
 Global family, full page:       K block [16][512] then V block [16][512];
-  each block in chunk-major order: element (c*16 + t)*8 + e = X[t][8c + e].
+  each block in chunk-major order, a chunk being 16 bytes of one token:
+  bf16:  element (c*16 + t)*8 + e  = X[t][8c + e]
+  e4m3:  element (c*16 + t)*16 + e = X[t][16c + e]
 """
 
 from __future__ import annotations
@@ -46,17 +48,17 @@ def local_bytes_per_token(num_kv_heads: int, head_dim: int, elem_bytes: int) -> 
     return 2 * num_kv_heads * head_dim * elem_bytes
 
 
-def global_bytes_per_token(head_dim: int, rot_dim: int, compressed: bool) -> int:
-    """One global layer, bf16: full K+V, or V plus the rotated part of K."""
-    return (head_dim + rot_dim) * 2 if compressed else 2 * head_dim * 2
+def global_bytes_per_token(head_dim: int, rot_dim: int, compressed: bool, elem_bytes: int = 2) -> int:
+    """One global layer: full K+V, or V plus the rotated part of K."""
+    return (head_dim + rot_dim) * elem_bytes if compressed else 2 * head_dim * elem_bytes
 
 
 def local_page_bytes(num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     return PAGE * local_bytes_per_token(num_kv_heads, head_dim, elem_bytes)
 
 
-def global_page_bytes(head_dim: int, rot_dim: int, compressed: bool) -> int:
-    return PAGE * global_bytes_per_token(head_dim, rot_dim, compressed)
+def global_page_bytes(head_dim: int, rot_dim: int, compressed: bool, elem_bytes: int = 2) -> int:
+    return PAGE * global_bytes_per_token(head_dim, rot_dim, compressed, elem_bytes)
 
 
 # ----------------------------------------------------------------------------
@@ -86,11 +88,13 @@ def local_v_index(elem_bytes: int) -> np.ndarray:
     return ((u * 64 + l) * 4 + j) * 4 + i
 
 
-def chunk_index(width: int) -> np.ndarray:
-    """idx[t, d] = element offset of X[t][d] in a chunk-major [16][width] block."""
+def chunk_index(width: int, elem_bytes: int = 2) -> np.ndarray:
+    """idx[t, d] = element offset of X[t][d] in a chunk-major [16][width]
+    block whose chunks are 16 bytes (8 bf16 or 16 e4m3 elements) of a token."""
+    e = 16 // elem_bytes
     t = np.arange(PAGE)[:, None]
     d = np.arange(width)[None, :]
-    return ((d // 8) * 16 + t) * 8 + d % 8
+    return ((d // e) * 16 + t) * e + d % e
 
 
 # ----------------------------------------------------------------------------
@@ -130,13 +134,15 @@ def local_codes(pool_bytes: np.ndarray, page_row, L: int, num_kv_heads: int,
     return K[:L], V[:L]
 
 
-def global_codes(pool_bytes: np.ndarray, page_row, L: int, compressed: bool):
-    """Contiguous bf16 codes of one sequence from a global pool.
+def global_codes(pool_bytes: np.ndarray, page_row, L: int, compressed: bool, elem_bytes: int = 2):
+    """Contiguous codes of one sequence from a global pool, uint16 (bf16)
+    or uint8 (e4m3); unwritten pages read as the all-ones code (NaN).
 
     compressed: returns (V [L][512], K_rot [L][128]);
     full:       returns (K [L][512], V [L][512]).
     """
-    elems = np.asarray(pool_bytes, dtype=np.uint8).view(np.uint16)
+    dt = np.uint16 if elem_bytes == 2 else np.uint8
+    elems = np.asarray(pool_bytes, dtype=np.uint8).view(dt)
     pages = _pages_of(page_row, L)
     if compressed:
         per_page = PAGE * (GLOBAL_D + GLOBAL_ROT)
@@ -144,9 +150,9 @@ def global_codes(pool_bytes: np.ndarray, page_row, L: int, compressed: bool):
     else:
         per_page = PAGE * 2 * GLOBAL_D
         widths = (GLOBAL_D, GLOBAL_D)
-    A = np.full((len(pages) * PAGE, widths[0]), 0xFFFF, dtype=np.uint16)
-    B = np.full((len(pages) * PAGE, widths[1]), 0xFFFF, dtype=np.uint16)
-    ia, ib = chunk_index(widths[0]), chunk_index(widths[1])
+    A = np.full((len(pages) * PAGE, widths[0]), np.iinfo(dt).max, dtype=dt)
+    B = np.full((len(pages) * PAGE, widths[1]), np.iinfo(dt).max, dtype=dt)
+    ia, ib = chunk_index(widths[0], elem_bytes), chunk_index(widths[1], elem_bytes)
     for lp, pp in enumerate(pages):
         if pp < 0:
             continue

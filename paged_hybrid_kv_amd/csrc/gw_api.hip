@@ -58,8 +58,6 @@ int check_geometry(const gw_pool_desc* p, const char* fn) {
     if (p->num_kv_heads < 1 || p->num_kv_heads > 65535)
       return fail(GW_ERR_GEOMETRY, fn, "local num_kv_heads %d", p->num_kv_heads);
   } else {
-    if (p->kv_dtype != GW_KV_BF16)
-      return fail(GW_ERR_UNSUPPORTED, fn, "e4m3 supports only the local family");
     if (p->head_dim != 512) return fail(GW_ERR_GEOMETRY, fn, "global head_dim %d (must be 512)", p->head_dim);
     if (p->rot_dim != 128) return fail(GW_ERR_GEOMETRY, fn, "global rot_dim %d (must be 128)", p->rot_dim);
     if (p->num_kv_heads != 1)
@@ -72,8 +70,8 @@ int64_t page_bytes_of(const gw_pool_desc* p) {
   const int64_t eb = p->kv_dtype == GW_KV_E4M3 ? 1 : 2;
   switch (p->family) {
     case GW_FAMILY_LOCAL: return 16LL * 2 * p->num_kv_heads * 256 * eb;
-    case GW_FAMILY_GLOBAL_COMPRESSED: return 16LL * (512 + 128) * 2;
-    case GW_FAMILY_GLOBAL_FULL: return 16LL * 1024 * 2;
+    case GW_FAMILY_GLOBAL_COMPRESSED: return 16LL * (512 + 128) * eb;
+    case GW_FAMILY_GLOBAL_FULL: return 16LL * 1024 * eb;
   }
   return -1;
 }
@@ -222,7 +220,8 @@ int gw_kv_append(const gw_pool_desc* pool, const void* k_raw, const void* v, con
   if (is_local(pool->family))
     e = gw::launch_append_local(a, pool->kv_dtype == GW_KV_E4M3, rope, (hipStream_t)stream);
   else
-    e = gw::launch_append_global(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, (hipStream_t)stream);
+    e = gw::launch_append_global(a, pool->family == GW_FAMILY_GLOBAL_COMPRESSED, pool->kv_dtype == GW_KV_E4M3,
+                                 (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }
@@ -351,6 +350,9 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if (rc != GW_OK) return rc;
   if (num_q_heads != 16 && num_q_heads != 32)
     return fail(GW_ERR_UNSUPPORTED, fn, "num_q_heads %d (served: 16, 32)", num_q_heads);
+  const bool fp8 = pool->kv_dtype == GW_KV_E4M3;
+  if (fp8 && max_q_len > 1)
+    return fail(GW_ERR_UNSUPPORTED, fn, "an e4m3 global pool serves decode rows only (max_q_len %d)", max_q_len);
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
@@ -407,7 +409,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     e = gw::launch_append_global_rows(ap, compressed, max_q_len, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
-  e = gw::launch_global_decode(a, compressed, (hipStream_t)stream);
+  e = gw::launch_global_decode(a, compressed, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (w.max_splits > 1) {
     gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, w.max_splits};

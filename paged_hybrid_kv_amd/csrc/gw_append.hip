@@ -136,8 +136,9 @@ __global__ __launch_bounds__(64) void append_local_kernel(AppendArgs a) {
 // One wave per token.  Lane l holds V dims 8l..8l+7 (chunk l).  Lanes 0..7
 // rotate chunk l with its rotate-half partner chunk l + 8 (pairs (i, i+64),
 // i < 64).  COMPRESSED: page = V[16][512] | K_rot[16][128]; FULL: page =
-// K[16][512] | V[16][512]; blocks chunk-major ((c*16 + t)*8 + e).
-template <bool COMPRESSED>
+// K[16][512] | V[16][512]; blocks chunk-major ((c*16 + t)*8 + e), or with
+// FP8 the e4m3 codes of the same bf16 record in 16-dim chunks.
+template <bool COMPRESSED, bool FP8>
 __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   const int tok = blockIdx.x, l = threadIdx.x;
   int s, ps;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64) void append_global_kernel(AppendArgs a) {
   const uint16_t* vsrc = a.v + (int64_t)tok * 512;
   const uint16_t* ksrc = a.k_raw ? a.k_raw + (int64_t)tok * 512 : vsrc;
   const GlobalRecordLane r = global_record_lane(vsrc, ksrc, a.rope_cos, a.rope_sin, ps, l);
-  put_global_record<COMPRESSED>(a.pool + (int64_t)page * a.page_bytes, r, ps & 15, l);
+  put_global_record_as<COMPRESSED, FP8>(a.pool + (int64_t)page * a.page_bytes, r, ps & 15, l);
 }
 
 // ------------------------------------------------ rows of an attention call
@@ -445,7 +446,7 @@ hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, in
 hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
   const int64_t items = rows_items(a, max_q_len);
   if (items == 0) return hipSuccess;
-  if (items > 0x7fffffff) return launch_append_global(a, compressed, stream);
+  if (items > 0x7fffffff) return launch_append_global(a, compressed, false, stream);
   dim3 grid((unsigned)items), block(256);
   if (compressed) hipLaunchKernelGGL((append_global_rows_kernel<true>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((append_global_rows_kernel<false>), grid, block, 0, stream, a);
@@ -464,10 +465,15 @@ hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_append_global(const AppendArgs& a, bool compressed, hipStream_t stream) {
+hipError_t launch_append_global(const AppendArgs& a, bool compressed, bool fp8, hipStream_t stream) {
   dim3 grid(a.n_tok), block(64);
-  if (compressed) hipLaunchKernelGGL((append_global_kernel<true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((append_global_kernel<false>), grid, block, 0, stream, a);
+  if (fp8) {
+    if (compressed) hipLaunchKernelGGL((append_global_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((append_global_kernel<false, true>), grid, block, 0, stream, a);
+  } else {
+    if (compressed) hipLaunchKernelGGL((append_global_kernel<true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((append_global_kernel<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

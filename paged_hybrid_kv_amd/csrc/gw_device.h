@@ -276,6 +276,43 @@ __device__ __forceinline__ void put_global_record(uint8_t* pb, const GlobalRecor
   }
 }
 
+// Eight bf16 (a 16-byte chunk) -> their eight e4m3 codes, in order.
+__device__ __forceinline__ uint2 e4m3x8_of_bf16x8(const uint4& c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t b[8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    b[2 * m] = f32_to_e4m3(bf16_lo(w[m]));
+    b[2 * m + 1] = f32_to_e4m3(bf16_hi(w[m]));
+  }
+  return uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+}
+
+// The same record in an e4m3 global page: each element is the e4m3 code of
+// its bf16 value; compressed page = V[16][512] | K_rot[16][128], full page =
+// K[16][512] | V[16][512], blocks chunk-major with 16-dim chunks
+// ((c*16 + t)*16 + e): lane l's 8 dims are half (l & 1) of chunk l / 2.
+template <bool COMPRESSED>
+__device__ __forceinline__ void put_global_record_e4m3(uint8_t* pb, const GlobalRecordLane& r, int slot, int l) {
+  uint8_t* vblock = COMPRESSED ? pb : pb + 8192;
+  uint8_t* kblock = COMPRESSED ? pb + 8192 : pb;
+  auto at = [&](uint8_t* blk, int c8) { return blk + ((c8 >> 1) * 16 + slot) * 16 + 8 * (c8 & 1); };
+  const uint2 v8 = e4m3x8_of_bf16x8(r.v);
+  *reinterpret_cast<uint2*>(at(vblock, l)) = v8;
+  if (l < 8) {
+    *reinterpret_cast<uint2*>(at(kblock, l)) = e4m3x8_of_bf16x8(r.ka);
+    *reinterpret_cast<uint2*>(at(kblock, l + 8)) = e4m3x8_of_bf16x8(r.kb);
+  } else if (!COMPRESSED && l >= 16) {
+    *reinterpret_cast<uint2*>(at(kblock, l)) = v8;   // K dims >= 128 are V's
+  }
+}
+
+template <bool COMPRESSED, bool FP8>
+__device__ __forceinline__ void put_global_record_as(uint8_t* pb, const GlobalRecordLane& r, int slot, int l) {
+  if constexpr (FP8) put_global_record_e4m3<COMPRESSED>(pb, r, slot, l);
+  else put_global_record<COMPRESSED>(pb, r, slot, l);
+}
+
 // Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
 // With n <= 2^20 pages (the entry points cap sequences at 2^24 tokens) and
 // i <= k <= n / 256 + 64, n * i stays below 2^32, so a 32-bit unsigned

@@ -17,7 +17,7 @@
 //                                  -- v_mfma_f32_16x16x16_bf16, per dim block
 // The S^T result already sits in the lanes as the P^T operand wants it (lane
 // l: head l % 16, tokens 4(l/16) .. +3), so the softmax of a page stays in
-// the wave: no score exchange between waves.
+// the wave.
 //
 // Work split: one workgroup per (sequence, split) item, numbered compactly
 // (workgroup b takes item b); a split is a balanced run of the row's pages
@@ -25,11 +25,15 @@
 // pages of the split, each with its own online-softmax state, merged at the
 // end.  Inside a group, wave w takes head block w % 2 (16 heads; with 16 q
 // heads, the only block) and a slice of the output dims (256 dims per wave
-// with 32 heads, 128 with 16).  Pages stream straight from HBM into a ring
-// of LDS page pairs (global_load_lds_dwordx4, each wave moving a quarter of
-// its group's page), NP - 1 pairs in flight while one is read; after an
-// LDS-only barrier each wave reads K (as stored) and V^T (through the gfx950
-// transposing LDS read ds_read_b64_tr_b16) from its group's page.  On the
+// with 32 heads, 128 with 16); the waves of a head block split the score
+// contraction's 512 dims the same way and add their partial scores through
+// LDS, in a fixed order, so each score is computed once.  Pages stream
+// straight from HBM into a ring of LDS page pairs (global_load_lds_dwordx4,
+// each wave moving a quarter of its group's page), NP - 1 pairs in flight
+// while one is read; after an LDS-only barrier each wave reads K (as stored)
+// and V^T (through the gfx950 transposing LDS read ds_read_b64_tr_b16, or
+// for an e4m3 page plain reads and a byte transpose across lanes) from its
+// group's page.  On the
 // row's last page, V of tokens past the row's position is zeroed in the
 // operand registers and their scores are masked, so unwritten slots (possibly
 // NaN) never reach the output.  P is rounded to bf16 for PV and the sum l
@@ -52,51 +56,88 @@ constexpr int kGD = 512;
 #ifndef GW_GLOBAL_NP_F
 #define GW_GLOBAL_NP_F 2
 #endif
+// e4m3 pages (10 and 16 KiB): 6 x 20 KiB and 3 x 32 KiB, q in a 32 KiB
+// region of its own
+#ifndef GW_GLOBAL_NP_C8
+#define GW_GLOBAL_NP_C8 6
+#endif
+#ifndef GW_GLOBAL_NP_F8
+#define GW_GLOBAL_NP_F8 3
+#endif
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-template <bool COMPRESSED>
+// FP8: the e4m3 page, its blocks in 16-dim chunks (16 bytes of a token).
+template <bool COMPRESSED, bool FP8 = false>
 struct GlobalPage {
-  static constexpr int kBytes = COMPRESSED ? 20480 : 32768;
-  static constexpr int kLoads = kBytes / 4096;            // 16-byte loads per thread (256 threads)
-  static constexpr int kVOff = COMPRESSED ? 0 : 16384;    // V block inside the page
-  // byte offset of chunk c (8 dims) of token t of K inside the page
+  static constexpr int kBlock = FP8 ? 8192 : 16384;      // one [16][512] block
+  static constexpr int kBytes = (COMPRESSED ? 5 : 8) * kBlock / 4;
+  static constexpr int kVOff = COMPRESSED ? 0 : kBlock;  // V block inside the page
+  // byte offset of dims 8c .. 8c+7 of token t of K inside the page
   __device__ static __forceinline__ int k_off(int c, int t) {
-    if constexpr (COMPRESSED) return c < 16 ? 16384 + (c * 16 + t) * 16 : (c * 16 + t) * 16;
-    else return (c * 16 + t) * 16;
+    const int kb = COMPRESSED && c < 16 ? kBlock : 0;   // compressed: dims < 128 from K_rot
+    if constexpr (FP8) return kb + ((c >> 1) * 16 + t) * 16 + 8 * (c & 1);
+    else return kb + (c * 16 + t) * 16;
   }
 };
 
-// One page of one wave: scores of the wave's 16 heads against the page's 16
-// tokens over all 512 dims, the online-softmax update, and the PV product
-// into the wave's output-dim slice.  pg: the page in LDS; tok_page0: the
-// position of the page's first token; p: the row's position (tokens past it
-// are masked, and their V zeroed, so unwritten slots never reach the output).
-template <bool COMPRESSED, int HB>
-__device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
-                                                 const uint8_t* pg, const bf16x8 (&qf)[16],
-                                                 int tok_page0, int p, int g, int l16, int v_lane_off,
-                                                 float scale_log2) {
-  using PG = GlobalPage<COMPRESSED>;
-  constexpr int kBlocks = 8 * HB;
-  // ---- S^T = K . Q^T: all 16 K fragments are read first (their LDS
-  // latencies overlap), then two accumulation chains; lane holds head l16,
-  // tokens 4g .. 4g+3
-  bf16x8 kf[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * ks + g, l16));
-  __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+// A page for one wave: its share of the scores of its 16 heads against the
+// page's 16 tokens (global_page_scores), then, with the head block's partial
+// scores added, the online-softmax update and the PV product into the wave's
+// output-dim slice (global_page_update).  pg: the page in LDS; tok_page0:
+// the position of the page's first token; p: the row's position (tokens past
+// it are masked, and their V zeroed, so unwritten slots never reach the
+// output).
+// The wave's share of S^T = K . Q^T: the 4 HB 32-dim steps ks0 .. (the
+// waves of a head block split the 512 dims between them; their partial
+// sums are added through LDS).  The K fragments are read first (their LDS
+// latencies overlap), then two accumulation chains; lane holds head l16,
+// tokens 4g .. 4g+3.  e4m3 fragments (8 bytes) widen exactly to bf16 just
+// before their product.
+template <bool COMPRESSED, int HB, bool FP8 = false>
+__device__ __forceinline__ f32x4 global_page_scores(const uint8_t* pg, const bf16x8 (&qf)[4 * HB], int ks0, int g,
+                                                    int l16) {
+  using PG = GlobalPage<COMPRESSED, FP8>;
+  constexpr int kKs = 4 * HB;
   f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  if constexpr (FP8) {
+    uint2 kr[kKs];
 #pragma unroll
-  for (int ks = 0; ks < 16; ks += 2) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
+    for (int k = 0; k < kKs; ++k) kr[k] = *reinterpret_cast<const uint2*>(pg + PG::k_off(4 * (ks0 + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);
+    auto widen = [](uint2 r) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, uint4{e4m3x2_to_bf16x2<false>(r.x), e4m3x2_to_bf16x2<true>(r.x),
+                                              e4m3x2_to_bf16x2<false>(r.y), e4m3x2_to_bf16x2<true>(r.y)});
+    };
+#pragma unroll
+    for (int k = 0; k < kKs; k += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(kr[k]), qf[k], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(kr[k + 1]), qf[k + 1], s1, 0, 0, 0);
+    }
+  } else {
+    bf16x8 kf[kKs];
+#pragma unroll
+    for (int k = 0; k < kKs; ++k) kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (ks0 + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+#pragma unroll
+    for (int k = 0; k < kKs; k += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k + 1], qf[k + 1], s1, 0, 0, 0);
+    }
   }
-  const f32x4 sacc = s0 + s1;
+  return s0 + s1;
+}
 
+// The rest of a page for one wave, given the page's full scores sacc: the
+// online-softmax update and the PV product into the wave's output-dim slice.
+template <bool COMPRESSED, int HB, bool FP8 = false>
+__device__ __forceinline__ void global_page_update(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
+                                                   const uint8_t* pg, const f32x4 sacc, int tok_page0, int p, int g,
+                                                   int l16, int v_lane_off, float scale_log2) {
+  constexpr int kBlocks = 8 * HB;
   // ---- online softmax for head l16 over the page's 16 tokens
   const int tok0 = tok_page0 + 4 * g;
   float z[4];
@@ -123,26 +164,56 @@ __device__ __forceinline__ void global_page_step(f32x4 (&acc)[8 * HB], float& m_
     vm0 = (tok0 + 0 <= p ? 0x0000ffffu : 0u) | (tok0 + 1 <= p ? 0xffff0000u : 0u);
     vm1 = (tok0 + 2 <= p ? 0x0000ffffu : 0u) | (tok0 + 3 <= p ? 0xffff0000u : 0u);
   }
-  lds_u8* vrow = (lds_u8*)pg + v_lane_off;
-  uint2 vf[kBlocks];
+  if constexpr (FP8) {
+    // lane (g, 4a + c) reads dims 16b + 4a .. +3 of token 4g + c (4 bytes);
+    // a byte transpose inside each quad of lanes (two DPP exchanges) leaves
+    // lane c with dim 16b + 4a + c of tokens 4g .. 4g+3, which widen to bf16
+    uint32_t vr[kBlocks];
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b)
-    vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
-  __builtin_amdgcn_sched_barrier(0);
+    for (int b = 0; b < kBlocks; ++b) vr[b] = *reinterpret_cast<const uint32_t*>(pg + v_lane_off + 256 * b);
+    __builtin_amdgcn_sched_barrier(0);
+    // byte selectors of v_perm_b32 (bytes 0-3: own word, 4-7: partner's):
+    // step 1 with the xor-1 partner keeps bytes 0, 2 (even lane) or 1, 3
+    // (odd lane) of both; step 2 with the xor-2 partner keeps the low
+    // (lanes 0, 1) or high (lanes 2, 3) halves of both
+    const int c = l16 & 3;
+    const uint32_t sel1 = (c & 1) ? 0x03070105u : 0x06020400u;
+    const uint32_t sel2 = (c & 2) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    uint2 vv = vf[b];
-    vv.x &= vm0;
-    vv.y &= vm1;
-    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+    for (int b = 0; b < kBlocks; ++b) {
+      const uint32_t x = vr[b];
+      const uint32_t xp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kQuadSwap1, 0xf, 0xf, false);
+      const uint32_t y = __builtin_amdgcn_perm(xp, x, sel1);
+      const uint32_t yp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, kQuadSwap2, 0xf, 0xf, false);
+      const uint32_t z = __builtin_amdgcn_perm(yp, y, sel2);
+      const uint2 vv = uint2{e4m3x2_to_bf16x2<false>(z) & vm0, e4m3x2_to_bf16x2<true>(z) & vm1};
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+    }
+  } else {
+    lds_u8* vrow = (lds_u8*)pg + v_lane_off;
+    uint2 vf[kBlocks];
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b)
+      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+      uint2 vv = vf[b];
+      vv.x &= vm0;
+      vv.y &= vm1;
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
+    }
   }
 }
 
 // Byte offset, inside a page, of what lane (g, l16) names in the transposing
 // read of V for dims d_lo .. (lane (g, e, q) names token 4g + e, dims
 // d_lo + 4q .. +3, and receives dim d_lo + l16 of tokens 4g .. 4g+3).
-template <bool COMPRESSED>
+// e4m3 (FP8): lane (g, 4a + c) reads dims d_lo + 4a .. +3 of token 4g + c.
+template <bool COMPRESSED, bool FP8 = false>
 __device__ __forceinline__ int global_v_lane_off(int d_lo, int g, int l16) {
+  if constexpr (FP8)
+    return GlobalPage<COMPRESSED, FP8>::kVOff + ((d_lo >> 4) * 16 + 4 * g + (l16 & 3)) * 16 + 4 * (l16 >> 2);
   const int t_rd = 4 * g + (l16 >> 2);
   const int dd = d_lo + 4 * (l16 & 3);
   return GlobalPage<COMPRESSED>::kVOff + ((dd >> 3) * 16 + t_rd) * 16 + (dd & 7) * 2;
@@ -154,14 +225,23 @@ __device__ __forceinline__ int global_v_lane_off(int d_lo, int g, int l16) {
 // one overlap the other's), each with its own online-softmax state; the two
 // states merge once at the end, group 1 into group 0, in that order.
 // NP: page pairs in the LDS ring (NP - 1 pairs in flight while one is read).
-template <bool COMPRESSED, int HB, int NP>
+// FP8: e4m3 pages, widened to bf16 as they are read from LDS; q then has an
+// LDS region of its own after the ring, and a 10 KiB compressed page moves
+// as 3 + 3 + 2 + 2 units (waves 0, 1 take one unit of the last two each).
+template <bool COMPRESSED, int HB, int NP, bool FP8 = false>
 __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a) {
-  using PG = GlobalPage<COMPRESSED>;
+  using PG = GlobalPage<COMPRESSED, FP8>;
   constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
-  constexpr int kPerWave = kUnits / 4;        // units per wave per pair
+  constexpr int kPerWave = (kUnits + 3) / 4;  // most units a wave moves per page
+  constexpr int kExtra = kUnits - 4 * (kUnits / 4);   // waves below kExtra move one more
   constexpr int kBlocks = 8 * HB;             // 16-dim output blocks per wave
+  constexpr int kRingBytes = NP * 2 * PG::kBytes;
   static_assert(NP >= 2 && kPerWave * (NP - 2) < 64 && NP - 2 <= 4, "ring depth");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NP][2][PG::kBytes];
+  static_assert(kRingBytes >= 4 * kBlocks * 64 * 16 + 4 * 64 * 8, "the ring holds the group merge");
+  static_assert(FP8 || 2 * PG::kBytes >= 32 * 1024, "a ring slot holds q");
+  constexpr int kXsOff = kRingBytes + (FP8 ? 32 * 1024 : 0);   // partial scores, [wave][lane] f32x4
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + 8 * 64 * 16];
+  uint8_t(*ring)[2][PG::kBytes] = reinterpret_cast<uint8_t(*)[2][PG::kBytes]>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform_i32(tid >> 6);
@@ -247,15 +327,15 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
     rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
   asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
   if (append_here && wv == 0)
-    put_global_record<COMPRESSED>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
-                                  p & 15, lane);
+    put_global_record_as<COMPRESSED, FP8>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
+                                          p & 15, lane);
 
   // ---- q into LDS by direct transfers, ahead of the pages, in ring slot
   // NP - 1 (free until the loop's first transfer): 1 KiB per head, the
   // row's 16-byte chunk c of head h stored at chunk c ^ (h % 8), so that the
   // Q^T operand reads below hit distinct banks.  Wave wv moves heads
   // 2 HB wv .. +2 HB - 1; lane i fetches the chunk that lands at position i.
-  uint8_t* qs = &ring[NP - 1][0][0];
+  uint8_t* qs = FP8 ? smem + kRingBytes : &ring[NP - 1][0][0];
   {
     const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
@@ -272,48 +352,73 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   // its last page as the second one; that copy is never computed on.  The
   // loop's waits count transfers only; the appending wave's pool stores and
   // the q transfers are older than all of them, so they are covered too.
-  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) +
-                             (uint32_t)(grp * PG::kBytes + 1024 * kPerWave * w);
+  // wave w moves units kUnits/4 * w + u, and, below kExtra, unit 4 (kUnits/4) + w
+  constexpr int kEven = kUnits / 4;
+  const int my_units = kEven + (w < kExtra ? 1 : 0);
+  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) + (uint32_t)(grp * PG::kBytes);
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
     const int i = min(2 * j + grp, n - 1);
-    const uint8_t* src = a.pool + (int64_t)phys(i) * a.page_bytes + 1024 * kPerWave * w + 16 * lane;
+    const uint8_t* src = a.pool + (int64_t)phys(i) * a.page_bytes + 16 * lane;
     const uint32_t dst = ring_base + (uint32_t)((j % NP) * 2 * PG::kBytes);
 #pragma unroll
-    for (int u = 0; u < kPerWave; ++u) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+    for (int u = 0; u < kEven; ++u) dma16_to_lds(src + 1024 * (kEven * w + u), dst + 1024 * (kEven * w + u));
+    if (kExtra > 0 && w < kExtra) dma16_to_lds(src + 1024 * (4 * kEven + w), dst + 1024 * (4 * kEven + w));
+  };
+  // at most k pairs' transfers of this wave left in flight
+  auto wait_pairs_after = [&](int k) __attribute__((always_inline)) {
+    if (kExtra > 0 && my_units == kEven) wait_groups_after<(kExtra > 0 ? kEven : kPerWave)>(k);
+    else wait_groups_after<kPerWave>(k);
   };
 #pragma unroll
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
 
-  // Q^T operand: head 16hb + l16, dims 32ks + 8g .. +7 (16-byte chunk 4ks + g),
-  // once every wave's q transfers (older than its page transfers) are in
-  wait_groups_after<kPerWave>(min(NP - 1, n_pairs));
+  // Q^T operand for the wave's part of the score dims (part `part` of the
+  // 4 / HB waves of its head block): head 16hb + l16, dims 32ks + 8g .. +7
+  // (16-byte chunk 4ks + g), once every wave's q transfers (older than its
+  // page transfers) are in
+  constexpr int kKs = 4 * HB;
+  const int part = HB == 2 ? (w >> 1) : w;
+  wait_pairs_after(min(NP - 1, n_pairs));
   lds_barrier();
-  bf16x8 qf[16];
+  bf16x8 qf[kKs];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + (((4 * ks + g) ^ (head & 7)) * 16));
+  for (int k = 0; k < kKs; ++k) {
+    const int ks = part * kKs + k;
+    qf[k] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + (((4 * ks + g) ^ (head & 7)) * 16));
+  }
+  f32x4* xs = reinterpret_cast<f32x4*>(smem + kXsOff);
 
   f32x4 acc[kBlocks];
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const int v_lane_off = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
+  const int v_lane_off = global_v_lane_off<COMPRESSED, FP8>(d_lo, g, l16);
 
   for (int j = 0; j < n_pairs; ++j) {
-    wait_groups_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
+    wait_pairs_after(min(NP - 2, n_pairs - 1 - j));
     lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
     if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
     if (append_here && j == ((n - 1) >> 1)) {
-      if (wv == 0) put_global_record<COMPRESSED>(&ring[j % NP][(n - 1) & 1][0], rec, p & 15, lane);
+      if (wv == 0) put_global_record_as<COMPRESSED, FP8>(&ring[j % NP][(n - 1) & 1][0], rec, p & 15, lane);
       lds_barrier();
     }
+    // both groups pass the exchange barrier, also a group with no page in
+    // the split's last pair
     const int i = 2 * j + grp;
-    if (i >= n) continue;
+    const bool live = i < n;
     const uint8_t* pg = ring[j % NP][grp];
-
-    global_page_step<COMPRESSED, HB>(acc, m_run, l_run, ring[j % NP][grp], qf, (pg0 + i) * 16, p, g, l16,
-                                     v_lane_off, a.scale_log2);
+    if (live) xs[wv * 64 + lane] = global_page_scores<COMPRESSED, HB, FP8>(pg, qf, part * kKs, g, l16);
+    lds_barrier();
+    if (live) {
+      // the head block's partial scores, added in part order by every wave
+      const f32x4* xh = xs + (4 * grp + hb) * 64 + lane;
+      f32x4 sacc;
+      if constexpr (HB == 2) sacc = xh[0] + xh[2 * 64];
+      else sacc = (xh[0] + xh[64]) + (xh[2 * 64] + xh[3 * 64]);
+      global_page_update<COMPRESSED, HB, FP8>(acc, m_run, l_run, pg, sacc, (pg0 + i) * 16, p, g, l16, v_lane_off,
+                                              a.scale_log2);
+    }
   }
 
   // ---- merge group 1 into group 0 through LDS (the ring is free now):
@@ -663,11 +768,19 @@ hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream) {
+hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool fp8, hipStream_t stream) {
   dim3 grid(a.max_splits * a.num_seqs), block(512);
   const bool h32 = a.num_q_heads == 32;
-  constexpr int kNc = GW_GLOBAL_NP_C, kNf = GW_GLOBAL_NP_F;
-  if (compressed) {
+  constexpr int kNc = GW_GLOBAL_NP_C, kNf = GW_GLOBAL_NP_F, kNc8 = GW_GLOBAL_NP_C8, kNf8 = GW_GLOBAL_NP_F8;
+  if (fp8) {
+    if (compressed) {
+      if (h32) hipLaunchKernelGGL((global_decode_kernel<true, 2, kNc8, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((global_decode_kernel<true, 1, kNc8, true>), grid, block, 0, stream, a);
+    } else {
+      if (h32) hipLaunchKernelGGL((global_decode_kernel<false, 2, kNf8, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((global_decode_kernel<false, 1, kNf8, true>), grid, block, 0, stream, a);
+    }
+  } else if (compressed) {
     if (h32) hipLaunchKernelGGL((global_decode_kernel<true, 2, kNc>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((global_decode_kernel<true, 1, kNc>), grid, block, 0, stream, a);
   } else {

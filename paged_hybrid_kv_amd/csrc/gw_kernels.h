@@ -95,7 +95,7 @@ struct AppendArgs {
 // Each launcher enqueues its kernel(s) on `stream` and returns the
 // hipGetLastError() status of the launch.
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream);
-hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, hipStream_t stream);
+hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool fp8, hipStream_t stream);
 hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int max_q_len,
                                 hipStream_t stream);
 hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream);
@@ -104,7 +104,7 @@ hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStre
 // Rows mode (seq_lens set): one workgroup per (sequence, page of its rows).
 hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream);
 hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream);
-hipError_t launch_append_global(const AppendArgs& a, bool compressed, hipStream_t stream);
+hipError_t launch_append_global(const AppendArgs& a, bool compressed, bool fp8, hipStream_t stream);
 hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int rot_dim,
                              int head_dim, double theta, hipStream_t stream);
 

@@ -136,7 +136,7 @@ def upload_global(case: GlobalCase, compressed: bool = True, device="cuda",
     given, replaces the case's queries (the caller's own q for that K)."""
     require_gpu()
     fam = gw.GW_FAMILY_GLOBAL_COMPRESSED if compressed else gw.GW_FAMILY_GLOBAL_FULL
-    pool = Pool(fam, gw.GW_KV_BF16, case.seqs.num_pages, 1, 128, device, fill_byte)
+    pool = Pool(fam, gw.GW_KV_E4M3 if case.fp8 else gw.GW_KV_BF16, case.seqs.num_pages, 1, 128, device, fill_byte)
     pt = i32_dev(case.seqs.page_table, device)
     stride = case.seqs.page_table.shape[1]
     max_len = int(case.seqs.lens.max())

@@ -121,6 +121,7 @@ class GlobalCase:
     # K's per-dim norm weight [512] (K = V * w_k before rotation), None when K = V;
     # every value is 1 + k/64, |k| <= 32, so exact in bf16
     w_k: np.ndarray | None = None
+    fp8: bool = False           # e4m3 pool (codes of the bf16 record)
 
     @property
     def q_indptr(self) -> np.ndarray:
@@ -180,7 +181,7 @@ def local_case(name, seed, lens, window, num_q_heads, num_kv_heads, q_len=None,
 
 def global_case(name, seed, lens, num_q_heads=32, q_len=None, q_scale=1.0,
                 v_scale=1.0, rope=True, head_dim=512, rot_dim=128,
-                extra_pages=0, k_norm=False) -> GlobalCase:
+                extra_pages=0, k_norm=False, fp8=False) -> GlobalCase:
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens(rng) if callable(lens) else lens, dtype=np.int64)
     S = lens.shape[0]
@@ -193,7 +194,8 @@ def global_case(name, seed, lens, num_q_heads=32, q_len=None, q_scale=1.0,
         if k_norm else None
     return GlobalCase(name=name, seqs=seqs, num_q_heads=num_q_heads, head_dim=head_dim,
                       rot_dim=rot_dim, q_len=q_len, q=q, v=v, tok_seq=tok_seq,
-                      tok_pos=tok_pos, rope=rope, scale=float(1.0 / np.sqrt(head_dim)), w_k=w_k)
+                      tok_pos=tok_pos, rope=rope, scale=float(1.0 / np.sqrt(head_dim)), w_k=w_k,
+                      fp8=fp8)
 
 
 # ----------------------------------------------------------------------------

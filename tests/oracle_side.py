@@ -54,6 +54,10 @@ def global_seq(case, s):
         k_pre = OC.bf16_round(v * case.w_k.astype(np.float64))
         k = OA.global_k(k_pre, pos if case.rope else np.zeros_like(pos))
         k[:, :128] = OC.bf16_round(k[:, :128])
+    if case.fp8:
+        # e4m3 pool: every stored element is the e4m3 code of its bf16 value
+        k = OC.e4m3_decode(OC.e4m3_encode(k))
+        v = OC.e4m3_decode(OC.e4m3_encode(v))
     L = int(case.seqs.lens[s])
     K = np.full((L, 512), np.nan)
     V = np.full((L, 512), np.nan)

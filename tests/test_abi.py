@@ -54,6 +54,9 @@ def test_page_bytes():
     comp = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_COMPRESSED))
     full = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_FULL))
     assert (comp, full) == (20480, 32768) and comp / full == 0.625
+    comp8 = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3))
+    full8 = gw.gw_pool_page_bytes(desc(gw.GW_FAMILY_GLOBAL_FULL, dt=gw.GW_KV_E4M3))
+    assert (comp8, full8) == (10240, 16384)
 
 
 @pytest.mark.parametrize("kw,code,frag", [
@@ -64,8 +67,6 @@ def test_page_bytes():
     (dict(dim=128), gw.GW_ERR_GEOMETRY, "head_dim"),
     (dict(rot=64), gw.GW_ERR_GEOMETRY, "rot_dim"),
     (dict(heads=0), gw.GW_ERR_GEOMETRY, "num_kv_heads"),
-    (dict(family=gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), gw.GW_ERR_UNSUPPORTED,
-     "e4m3 supports only the local family"),
     (dict(family=gw.GW_FAMILY_GLOBAL_FULL, heads=2), gw.GW_ERR_GEOMETRY, "num_kv_heads"),
     (dict(family=gw.GW_FAMILY_GLOBAL_FULL, rot=512), gw.GW_ERR_GEOMETRY, "rot_dim"),
 ])
@@ -82,8 +83,6 @@ def append(d, k=FAKE, v=FAKE, n=4, stride=8, cos=FAKE, sin=FAKE):
 
 
 @pytest.mark.parametrize("call,code,frag", [
-    (lambda: append(desc(family=gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), k=None),
-     gw.GW_ERR_UNSUPPORTED, "gw_kv_append: e4m3 supports only the local family"),
     (lambda: append(desc(base=None)), gw.GW_ERR_INVALID_ARG, "base is null"),
     (lambda: append(desc(pages=0)), gw.GW_ERR_INVALID_ARG, "num_pages"),
     (lambda: append(desc(), n=-1), gw.GW_ERR_INVALID_ARG, "n_tok"),
@@ -153,8 +152,8 @@ def test_local_rejects(call, code, frag):
 @pytest.mark.parametrize("call,code,frag", [
     (lambda: glob(hq=8), gw.GW_ERR_UNSUPPORTED, "num_q_heads"),
     (lambda: glob(d=desc()), gw.GW_ERR_INVALID_ARG, "not a global family"),
-    (lambda: glob(d=desc(gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3)), gw.GW_ERR_UNSUPPORTED,
-     "e4m3 supports only the local family"),
+    (lambda: glob(d=desc(gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), mql=2, indptr=FAKE),
+     gw.GW_ERR_UNSUPPORTED, "decode rows only"),
     (lambda: glob(wsb=0), gw.GW_ERR_WORKSPACE, "workspace"),
     (lambda: glob(msl=0), gw.GW_ERR_INVALID_ARG, "max_seq_len"),
     (lambda: glob(vn=FAKE), gw.GW_ERR_INVALID_ARG, "rotary tables"),

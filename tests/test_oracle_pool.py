@@ -41,6 +41,11 @@ def test_page_bytes():
     assert pool.local_page_bytes(8, 256, 1) == 65536
     assert pool.global_page_bytes(512, 128, True) == 20480
     assert pool.global_page_bytes(512, 128, False) == 32768
+    assert pool.global_page_bytes(512, 128, True, 1) == 10240
+    assert pool.global_page_bytes(512, 128, False, 1) == 16384
+    # the e4m3 compressed record keeps the pages' 0.625x of the full one
+    assert pool.global_page_bytes(512, 128, True, 1) / pool.global_page_bytes(512, 128, False, 1) == \
+        GOLD["global_compressed_ratio"]["value"]
 
 
 def test_layer_pattern_12b():
@@ -63,10 +68,40 @@ def test_local_layouts_are_bijections(eb):
         assert np.array_equal(np.sort(idx.ravel()), np.arange(16 * 256))
 
 
-def test_chunk_layout_is_bijection():
+@pytest.mark.parametrize("eb", [1, 2])
+def test_chunk_layout_is_bijection(eb):
     for w in (128, 512):
-        idx = pool.chunk_index(w)
+        idx = pool.chunk_index(w, eb)
         assert np.array_equal(np.sort(idx.ravel()), np.arange(16 * w))
+        # a chunk is 16 bytes of one token: consecutive dims, one token
+        e = 16 // eb
+        assert np.array_equal(idx[5, :e], idx[5, 0] + np.arange(e))
+        assert idx[5, e] == idx[5, 0] + 16 * e
+
+
+@pytest.mark.parametrize("eb", [1, 2])
+@pytest.mark.parametrize("compressed", [True, False])
+def test_global_decoder_roundtrip(eb, compressed):
+    """Pages written element by element from the layout's formula read back
+    in token order, through a shuffled page table."""
+    rng = np.random.default_rng(10 + eb)
+    dt = np.uint16 if eb == 2 else np.uint8
+    e = 16 // eb
+    wa, wb = (512, 128) if compressed else (512, 512)
+    L, npages = 37, 6
+    A = rng.integers(0, 2 ** (8 * eb) - 1, (48, wa)).astype(dt)
+    B = rng.integers(0, 2 ** (8 * eb) - 1, (48, wb)).astype(dt)
+    table = np.array([4, 1, 5], dtype=np.int32)
+    per_page = 16 * (wa + wb)
+    elems = np.zeros(npages * per_page, dtype=dt)
+    for lp, pp in enumerate(table):
+        for t in range(16):
+            for d in range(wa):
+                elems[pp * per_page + ((d // e) * 16 + t) * e + d % e] = A[lp * 16 + t, d]
+            for d in range(wb):
+                elems[pp * per_page + 16 * wa + ((d // e) * 16 + t) * e + d % e] = B[lp * 16 + t, d]
+    Ad, Bd = pool.global_codes(elems.view(np.uint8), table, L, compressed, eb)
+    assert np.array_equal(Ad, A[:L]) and np.array_equal(Bd, B[:L])
 
 
 @pytest.mark.parametrize("eb", [1, 2])
