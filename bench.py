@@ -181,7 +181,8 @@ def config_throughput(iters=30):
     seeded generator): local bf16 (16 slots, contexts U[1024, 8192], window
     1024, 16 q / 8 KV heads), global tied (8 slots x 131072 tokens, 32 q / 1
     KV head, compressed and full records, in bf16 and in e4m3 pools) and
-    local e4m3 (64 slots x 8192).
+    local e4m3 (64 slots x 8192); and the page copy of the prefix cache
+    (4096 local bf16 pages, read and written once).
     Calls run back to back over pool replicas whose total exceeds the 256 MB
     last-level cache; returns {name: {us, GB_s, pct_of_peak, tok_s, bytes}}."""
     import numpy as np
@@ -255,6 +256,20 @@ def config_throughput(iters=30):
                 [dc], 8 * 131072 * (640 if compressed else 1024) * (1 if fp8 else 2), 8)
             del dc
             torch.cuda.empty_cache()
+    # prefix-cache page copies: 4096 local bf16 pages (512 MiB) from a cache
+    # pool into a live pool, in a shuffled order; bytes counted once each way
+    src = RT.Pool(gw.GW_FAMILY_LOCAL, gw.GW_KV_BF16, 4096, 8, 256, dev, fill_byte=1)
+    dst = RT.Pool(gw.GW_FAMILY_LOCAL, gw.GW_KV_BF16, 4096, 8, 256, dev, fill_byte=0)
+    perm = np.random.default_rng(6).permutation(4096).astype(np.int32)
+    ids_s, ids_d = RT.i32_dev(np.arange(4096, dtype=np.int32)), RT.i32_dev(perm)
+    gw.gw_copy_pages(dst.desc, src.desc, ids_d, ids_s, 4096)
+    ms = time_events(lambda: gw.gw_copy_pages(dst.desc, src.desc, ids_d, ids_s, 4096), iters)
+    nbytes = 2 * 4096 * src.page_bytes
+    res["copy_pages"] = {"us": round(ms * 1e3, 2), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "pct_of_peak": round(nbytes / (ms * 1e-3) / PEAK_HBM * 100, 2),
+                         "tok_s": round(4096 * 16 / (ms * 1e-3), 1), "bytes": nbytes}
+    del src, dst
+    torch.cuda.empty_cache()
     c4 = [local_pool([8192] * 64, True, 4, r) for r in range(2)]
     res["local_fp8"] = timed(c4, 64 * 1024 * 8 * 256 * 2, 64)
     del c4

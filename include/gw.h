@@ -49,7 +49,8 @@ typedef enum gw_status {
   GW_ERR_UNSUPPORTED = -2, /* valid but not served (e.g. group size > 8)     */
   GW_ERR_GEOMETRY = -3,    /* shape does not match the family's layout      */
   GW_ERR_WORKSPACE = -4,   /* workspace smaller than gw_attn_workspace_bytes */
-  GW_ERR_HIP = -5          /* a HIP launch failed; message has the reason   */
+  GW_ERR_HIP = -5,         /* a HIP launch failed; message has the reason   */
+  GW_ERR_REFUSED = -6      /* admission refused: the request can never run  */
 } gw_status;
 
 /* --------------------------------------------------------------- enums -- */
@@ -245,6 +246,64 @@ int gw_decode_attn_global(const gw_pool_desc* pool /* host */, const void* q,
                           int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
                           int32_t max_seq_len, float scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------- pool lifecycle -- */
+/*
+ * Host page allocator of the two families (pegainfer "Gemma 4" page,
+ * Scheduling): one object owns the page ids of one local and one global
+ * pool (the same ids serve every layer of a family) and the decode slots.
+ *   - Admission: a request of total_tokens (prompt + max_tokens) that will
+ *     have at most max_step_rows query rows in one step is admitted into a
+ *     free slot when both families' budgets hold its worst case: global,
+ *     ceil(total / 16) pages (global pages are never freed while it runs);
+ *     local, min(ceil(total / 16), (max_step_rows + window + 13) / 16 + 1)
+ *     pages (the pages one step's rows and their windows can span).
+ *     Otherwise it waits (*slot = -1, GW_OK) -- or, when no request is
+ *     active and so nothing can free up, or total_tokens exceeds the
+ *     ceiling max_context, it is refused (GW_ERR_REFUSED).
+ *   - gw_alloc_extend: the slot's sequence now has new_len tokens and its
+ *     earliest row still to be queried is at first_query_pos (new_len - 1
+ *     for a decode step; non-decreasing; new_len - first_query_pos <=
+ *     max_step_rows).  Pages are assigned to every logical page up to
+ *     (new_len - 1) / 16 in both families; local pages wholly before
+ *     first_query_pos - window + 1 go back to the free list, their table
+ *     entries -1 (the attention kernels never read them).
+ *   - gw_alloc_release: every page of the slot back, the slot free.
+ *   - Free page ids are handed out lowest first, so the tables depend only
+ *     on the sequence of calls.
+ * All pointers here are host pointers; nothing touches the GPU.  One
+ * allocator must not be called from two threads at once.
+ */
+typedef struct gw_page_alloc gw_page_alloc;
+
+int gw_alloc_create(int32_t slots, int32_t max_context, int32_t window, int32_t local_pages,
+                    int32_t global_pages, gw_page_alloc** out /* host */);
+int gw_alloc_destroy(gw_page_alloc* a);
+int gw_alloc_admit(gw_page_alloc* a, int32_t total_tokens, int32_t max_step_rows,
+                   int32_t* slot /* host */);
+int gw_alloc_extend(gw_page_alloc* a, int32_t slot, int32_t new_len, int32_t first_query_pos);
+int gw_alloc_release(gw_page_alloc* a, int32_t slot);
+/* Page tables as the attention calls take them (host int32, copied out):
+ * local_pt [slots][local_stride], global_pt [slots][global_stride], both
+ * strides >= ceil(max_context / 16), -1 where no page is held; seq_lens
+ * [slots] (0 for a free slot) may be NULL. */
+int gw_alloc_tables(const gw_page_alloc* a, int32_t* local_pt, int32_t local_stride, int32_t* global_pt,
+                    int32_t global_stride, int32_t* seq_lens);
+/* stats[6] (host): free local pages, free global pages, reserved local,
+ * reserved global, active requests, slots. */
+int gw_alloc_stats(const gw_page_alloc* a, int32_t* stats);
+
+/*
+ * Copy whole pages between two pools of the same family, dtype and
+ * geometry: page dst_pages[i] of dst <- page src_pages[i] of src, i < n
+ * (device int32 arrays).  This is the copy of the conversation prefix cache
+ * (pegainfer "Gemma 4" page, Conversation prefix cache: finished prompt
+ * states kept in pages of their own and copied back on a hit).  A pair with
+ * an id outside its pool's [0, num_pages) is skipped.  Pairs must not write
+ * the same destination page, nor read a page another pair writes.
+ */
+int gw_copy_pages(const gw_pool_desc* dst /* host */, const gw_pool_desc* src /* host */,
+                  const int32_t* dst_pages, const int32_t* src_pages, int32_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "gw.h"
+#include "gw_alloc.h"
 #include "gw_kernels.h"
 #include "gw_plan.h"
 
@@ -418,6 +421,128 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   }
   if (max_q_len > 1) {
     e = gw::launch_global_prefill(a, compressed, max_q_len, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+// ------------------------------------------------------ pool lifecycle --
+struct gw_page_alloc {
+  gw::Allocator impl;
+};
+
+int gw_alloc_create(int32_t slots, int32_t max_context, int32_t window, int32_t local_pages,
+                    int32_t global_pages, gw_page_alloc** out) {
+  const char* fn = "gw_alloc_create";
+  if (!out) return fail(GW_ERR_INVALID_ARG, fn, "out is null");
+  *out = nullptr;
+  if (slots < 1 || slots > (1 << 20)) return fail(GW_ERR_INVALID_ARG, fn, "slots %d", slots);
+  if (max_context < 1 || max_context > (1 << 24)) return fail(GW_ERR_INVALID_ARG, fn, "max_context %d", max_context);
+  if (window < 1) return fail(GW_ERR_INVALID_ARG, fn, "window %d", window);
+  if (local_pages < 0 || global_pages < 0)
+    return fail(GW_ERR_INVALID_ARG, fn, "page counts %d, %d", local_pages, global_pages);
+  if ((int64_t)slots * ((max_context + 15) / 16) > (1LL << 28))
+    return fail(GW_ERR_INVALID_ARG, fn, "slots x pages per slot too large");
+  try {
+    *out = new gw_page_alloc{gw::Allocator(slots, max_context, window, local_pages, global_pages)};
+  } catch (...) {
+    return fail(GW_ERR_INVALID_ARG, fn, "out of host memory");
+  }
+  return ok();
+}
+
+int gw_alloc_destroy(gw_page_alloc* a) {
+  delete a;
+  return ok();
+}
+
+int gw_alloc_admit(gw_page_alloc* a, int32_t total_tokens, int32_t max_step_rows, int32_t* slot) {
+  const char* fn = "gw_alloc_admit";
+  if (!a || !slot) return fail(GW_ERR_INVALID_ARG, fn, "null allocator or slot");
+  *slot = -1;
+  gw::Allocator& A = a->impl;
+  if (total_tokens < 1) return fail(GW_ERR_INVALID_ARG, fn, "total_tokens %d", total_tokens);
+  if (max_step_rows < 1 || max_step_rows > total_tokens)
+    return fail(GW_ERR_INVALID_ARG, fn, "max_step_rows %d (1 .. total_tokens)", max_step_rows);
+  if (total_tokens > A.max_context)
+    return fail(GW_ERR_REFUSED, fn, "total_tokens %d exceeds the ceiling %d", total_tokens, A.max_context);
+  const int r = A.admit(total_tokens, max_step_rows, slot);
+  if (r < 0) return fail(GW_ERR_REFUSED, fn, "the pools cannot hold the request and nothing else runs");
+  return ok();
+}
+
+int gw_alloc_extend(gw_page_alloc* a, int32_t slot, int32_t new_len, int32_t first_query_pos) {
+  const char* fn = "gw_alloc_extend";
+  if (!a) return fail(GW_ERR_INVALID_ARG, fn, "allocator is null");
+  gw::Allocator& A = a->impl;
+  if (slot < 0 || slot >= A.slots || !A.seq[slot].used) return fail(GW_ERR_INVALID_ARG, fn, "slot %d is not active", slot);
+  const auto& q = A.seq[slot];
+  if (new_len < std::max(1, q.len) || new_len > q.total)
+    return fail(GW_ERR_INVALID_ARG, fn, "new_len %d (%d .. %d)", new_len, std::max(1, q.len), q.total);
+  if (first_query_pos < q.first_query || first_query_pos > new_len - 1)
+    return fail(GW_ERR_INVALID_ARG, fn, "first_query_pos %d (%d .. %d)", first_query_pos, q.first_query, new_len - 1);
+  if (new_len - first_query_pos > q.rows)
+    return fail(GW_ERR_INVALID_ARG, fn, "%d rows in one step > max_step_rows %d", new_len - first_query_pos, q.rows);
+  A.extend(slot, new_len, first_query_pos);
+  return ok();
+}
+
+int gw_alloc_release(gw_page_alloc* a, int32_t slot) {
+  const char* fn = "gw_alloc_release";
+  if (!a) return fail(GW_ERR_INVALID_ARG, fn, "allocator is null");
+  if (slot < 0 || slot >= a->impl.slots || !a->impl.seq[slot].used)
+    return fail(GW_ERR_INVALID_ARG, fn, "slot %d is not active", slot);
+  a->impl.release(slot);
+  return ok();
+}
+
+int gw_alloc_tables(const gw_page_alloc* a, int32_t* local_pt, int32_t local_stride, int32_t* global_pt,
+                    int32_t global_stride, int32_t* seq_lens) {
+  const char* fn = "gw_alloc_tables";
+  if (!a || !local_pt || !global_pt) return fail(GW_ERR_INVALID_ARG, fn, "null allocator or table");
+  const gw::Allocator& A = a->impl;
+  const int np = (A.max_context + 15) / 16;
+  if (local_stride < np || global_stride < np)
+    return fail(GW_ERR_INVALID_ARG, fn, "strides %d, %d < %d pages", local_stride, global_stride, np);
+  for (int s = 0; s < A.slots; ++s) {
+    const auto& q = A.seq[s];
+    for (int i = 0; i < local_stride; ++i) local_pt[(int64_t)s * local_stride + i] = i < np ? q.lpt[i] : -1;
+    for (int i = 0; i < global_stride; ++i) global_pt[(int64_t)s * global_stride + i] = i < np ? q.gpt[i] : -1;
+    if (seq_lens) seq_lens[s] = q.used ? q.len : 0;
+  }
+  return ok();
+}
+
+int gw_alloc_stats(const gw_page_alloc* a, int32_t* stats) {
+  if (!a || !stats) return fail(GW_ERR_INVALID_ARG, "gw_alloc_stats", "null allocator or stats");
+  const gw::Allocator& A = a->impl;
+  stats[0] = (int32_t)A.free_local.size();
+  stats[1] = (int32_t)A.free_global.size();
+  stats[2] = A.reserved_l;
+  stats[3] = A.reserved_g;
+  stats[4] = A.active();
+  stats[5] = A.slots;
+  return ok();
+}
+
+int gw_copy_pages(const gw_pool_desc* dst, const gw_pool_desc* src, const int32_t* dst_pages,
+                  const int32_t* src_pages, int32_t n, void* stream) {
+  const char* fn = "gw_copy_pages";
+  int rc = check_pool(dst, fn);
+  if (rc != GW_OK) return rc;
+  rc = check_pool(src, fn);
+  if (rc != GW_OK) return rc;
+  if (dst->family != src->family || dst->kv_dtype != src->kv_dtype || page_bytes_of(dst) != page_bytes_of(src))
+    return fail(GW_ERR_GEOMETRY, fn, "the two pools differ in family, dtype or page size");
+  if (n < 0) return fail(GW_ERR_INVALID_ARG, fn, "n %d", n);
+  if (n == 0) return ok();
+  if (!dst_pages || !src_pages) return fail(GW_ERR_INVALID_ARG, fn, "null page list");
+  (void)hipGetLastError();
+  for (int32_t c = 0; c < n; c += 65535) {
+    const int m = std::min(65535, n - c);
+    hipError_t e = gw::launch_copy_pages(static_cast<uint8_t*>(dst->base), static_cast<const uint8_t*>(src->base),
+                                         dst_pages + c, src_pages + c, m, page_bytes_of(dst), dst->num_pages,
+                                         src->num_pages, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ok();

@@ -20,6 +20,7 @@ GW_ERR_UNSUPPORTED = -2
 GW_ERR_GEOMETRY = -3
 GW_ERR_WORKSPACE = -4
 GW_ERR_HIP = -5
+GW_ERR_REFUSED = -6
 
 GW_FAMILY_LOCAL = 1
 GW_FAMILY_GLOBAL_COMPRESSED = 2
@@ -29,7 +30,9 @@ GW_KV_BF16 = 1
 GW_KV_E4M3 = 2
 
 EXPORTS = ("gw_version", "gw_last_error", "gw_pool_page_bytes", "gw_rope_table", "gw_kv_append",
-           "gw_attn_workspace_bytes", "gw_decode_attn_local", "gw_decode_attn_global")
+           "gw_attn_workspace_bytes", "gw_decode_attn_local", "gw_decode_attn_global",
+           "gw_alloc_create", "gw_alloc_destroy", "gw_alloc_admit", "gw_alloc_extend", "gw_alloc_release",
+           "gw_alloc_tables", "gw_alloc_stats", "gw_copy_pages")
 
 
 class GwError(RuntimeError):
@@ -84,6 +87,22 @@ def lib():
         L.gw_decode_attn_global.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P, _P,
                                             _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                             _P]
+        L.gw_alloc_create.restype = ctypes.c_int
+        L.gw_alloc_create.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_void_p)]
+        L.gw_alloc_destroy.restype = ctypes.c_int
+        L.gw_alloc_destroy.argtypes = [_P]
+        L.gw_alloc_admit.restype = ctypes.c_int
+        L.gw_alloc_admit.argtypes = [_P, _I, _I, ctypes.POINTER(ctypes.c_int32)]
+        L.gw_alloc_extend.restype = ctypes.c_int
+        L.gw_alloc_extend.argtypes = [_P, _I, _I, _I]
+        L.gw_alloc_release.restype = ctypes.c_int
+        L.gw_alloc_release.argtypes = [_P, _I]
+        L.gw_alloc_tables.restype = ctypes.c_int
+        L.gw_alloc_tables.argtypes = [_P, _P, _I, _P, _I, _P]
+        L.gw_alloc_stats.restype = ctypes.c_int
+        L.gw_alloc_stats.argtypes = [_P, _P]
+        L.gw_copy_pages.restype = ctypes.c_int
+        L.gw_copy_pages.argtypes = [ctypes.POINTER(gw_pool_desc), ctypes.POINTER(gw_pool_desc), _P, _P, _I, _P]
         _lib = L
     return _lib
 
@@ -164,3 +183,56 @@ def gw_decode_attn_global(desc: gw_pool_desc, q, num_q_heads, v_new, rope_cos, r
                                        _ptr(seq_lens), _ptr(page_table), pt_stride, num_seqs,
                                        num_rows, max_q_len, max_seq_len, scale, _ptr(out),
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------- pool lifecycle --
+class PageAllocator:
+    """gw_alloc_*: the two families' page ids and the decode slots (host
+    only).  Tables come back as numpy int32 arrays."""
+
+    def __init__(self, slots, max_context, window, local_pages, global_pages):
+        h = ctypes.c_void_p()
+        _check(lib().gw_alloc_create(slots, max_context, window, local_pages, global_pages, ctypes.byref(h)))
+        self.h = h.value
+        self.slots, self.max_context = slots, max_context
+        self.pages_per_slot = (max_context + 15) // 16
+
+    def close(self):
+        if self.h:
+            lib().gw_alloc_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+    def admit(self, total_tokens, max_step_rows):
+        """Slot index, or -1 to wait; raises GwError(GW_ERR_REFUSED) when refused."""
+        slot = ctypes.c_int32(-1)
+        _check(lib().gw_alloc_admit(self.h, total_tokens, max_step_rows, ctypes.byref(slot)))
+        return slot.value
+
+    def extend(self, slot, new_len, first_query_pos):
+        _check(lib().gw_alloc_extend(self.h, slot, new_len, first_query_pos))
+
+    def release(self, slot):
+        _check(lib().gw_alloc_release(self.h, slot))
+
+    def tables(self):
+        import numpy as np
+        n = self.pages_per_slot
+        lpt = np.empty((self.slots, n), dtype=np.int32)
+        gpt = np.empty((self.slots, n), dtype=np.int32)
+        lens = np.empty(self.slots, dtype=np.int32)
+        _check(lib().gw_alloc_tables(self.h, lpt.ctypes.data, n, gpt.ctypes.data, n, lens.ctypes.data))
+        return lpt, gpt, lens
+
+    def stats(self):
+        """(free local, free global, reserved local, reserved global, active, slots)"""
+        import numpy as np
+        st = np.empty(6, dtype=np.int32)
+        _check(lib().gw_alloc_stats(self.h, st.ctypes.data))
+        return tuple(int(x) for x in st)
+
+
+def gw_copy_pages(dst: gw_pool_desc, src: gw_pool_desc, dst_pages, src_pages, n, stream=None):
+    _check(lib().gw_copy_pages(ctypes.byref(dst), ctypes.byref(src), _ptr(dst_pages), _ptr(src_pages), n,
+                               _stream(stream)))

@@ -205,3 +205,14 @@ def test_error_message_is_thread_local_and_cleared():
     assert gw.gw_last_error().startswith("gw_decode_attn_local")
     assert gw.gw_pool_page_bytes(desc()) > 0
     assert gw.gw_last_error() == ""
+
+
+def test_copy_pages_rejects():
+    a, b = desc(), desc(gw.GW_FAMILY_GLOBAL_FULL)
+    for d, sd, n, code, frag in ((a, b, 1, gw.GW_ERR_GEOMETRY, "differ"),
+                                 (a, desc(dt=gw.GW_KV_E4M3), 1, gw.GW_ERR_GEOMETRY, "differ"),
+                                 (a, a, -1, gw.GW_ERR_INVALID_ARG, "n -1")):
+        with pytest.raises(gw.GwError) as e:
+            gw.gw_copy_pages(d, sd, FAKE, FAKE, n)
+        assert e.value.code == code and frag in e.value.message
+    gw.gw_copy_pages(a, a, FAKE, FAKE, 0)      # n == 0: no-op, no GPU call
