@@ -24,7 +24,7 @@ struct Allocator {
   int local_reserve(int total, int rows) const;
   int active() const;
   int admit(int total, int rows, int* slot);
-  void extend(int slot, int new_len, int first_query);
+  int extend(int slot, int new_len, int first_query);
   void release(int slot);
   static int take(std::vector<int>& fl);
   static void give(std::vector<int>& fl, int id);

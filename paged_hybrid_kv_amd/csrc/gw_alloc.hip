@@ -38,6 +38,7 @@ int Allocator::local_reserve(int total, int rows) const {
 }
 
 int Allocator::take(std::vector<int>& fl) {
+  if (fl.empty()) return -1;
   const int id = fl.back();
   fl.pop_back();
   return id;
@@ -91,13 +92,23 @@ int Allocator::admit(int total, int rows, int* slot) {
   return active() == 0 ? -1 : 0;
 }
 
-void Allocator::extend(int slot, int new_len, int first_query) {
+// 0, or -1 (nothing changed) when a free list cannot supply the pages: the
+// admission reservations make that impossible, so it means a broken
+// invariant, reported rather than acted on.
+int Allocator::extend(int slot, int new_len, int first_query) {
   Seq& q = seq[slot];
   const int last_page = (new_len - 1) / kPage;
+  const int lo_page = std::max(0, first_query - window + 1) / kPage;
+  int need_g = 0, need_l = 0, freed_l = 0;
+  for (int i = 0; i <= last_page; ++i) {
+    need_g += q.gpt[i] < 0;
+    need_l += i >= lo_page && q.lpt[i] < 0;
+    freed_l += i < lo_page && q.lpt[i] >= 0;
+  }
+  if (need_g > (int)free_global.size() || need_l > (int)free_local.size() + freed_l) return -1;
   for (int i = 0; i <= last_page; ++i) {
     if (q.gpt[i] < 0) q.gpt[i] = take(free_global);
   }
-  const int lo_page = std::max(0, first_query - window + 1) / kPage;
   for (int i = 0; i < lo_page; ++i)
     if (q.lpt[i] >= 0) {
       give(free_local, q.lpt[i]);
@@ -107,6 +118,7 @@ void Allocator::extend(int slot, int new_len, int first_query) {
     if (q.lpt[i] < 0) q.lpt[i] = take(free_local);
   q.len = new_len;
   q.first_query = first_query;
+  return 0;
 }
 
 void Allocator::release(int slot) {

@@ -36,6 +36,8 @@ constexpr size_t kAlign = 256;
 // Longest sequence served (tokens): keeps every page count and split bound
 // of the plans well inside 32-bit arithmetic.
 constexpr int kMaxSeqLen = 1 << 24;
+// Most workgroups of one (1-D) launch.
+constexpr long long kMaxGrid = 0x7fffffff;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool is_local(int f) { return f == GW_FAMILY_LOCAL; }
@@ -271,6 +273,17 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
     return fail(GW_ERR_INVALID_ARG, fn, "rot_dim 0 takes no rotary tables");
   const WsPlan w = plan_workspace(GW_FAMILY_LOCAL, num_seqs, pool->num_kv_heads, num_q_heads, 256,
                                   max_seq_len, window, group);
+  // grids: (split, KV head, sequence) for the decode rows, (row block, KV
+  // head) for the prompt rows
+  const long long dec_wgs = (long long)std::max(w.max_splits, 1) * pool->num_kv_heads * num_seqs;
+  if (dec_wgs > kMaxGrid)
+    return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups (served: up to %lld)", dec_wgs, kMaxGrid);
+  if (max_q_len > 1) {
+    const long long pre_wgs =
+        gw::prefill_items(num_rows, num_seqs, max_q_len, gw::local_prefill_rows(group)) * pool->num_kv_heads;
+    if (pre_wgs > kMaxGrid)
+      return fail(GW_ERR_UNSUPPORTED, fn, "%lld prompt-row workgroups (served: up to %lld)", pre_wgs, kMaxGrid);
+  }
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
@@ -360,6 +373,11 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
   const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0, 1);
+  if (max_q_len > 1) {
+    const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads));
+    if (pre_wgs > kMaxGrid)
+      return fail(GW_ERR_UNSUPPORTED, fn, "%lld prompt-row workgroups (served: up to %lld)", pre_wgs, kMaxGrid);
+  }
   if (workspace_bytes < w.total)
     return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
@@ -483,7 +501,8 @@ int gw_alloc_extend(gw_page_alloc* a, int32_t slot, int32_t new_len, int32_t fir
     return fail(GW_ERR_INVALID_ARG, fn, "first_query_pos %d (%d .. %d)", first_query_pos, q.first_query, new_len - 1);
   if (new_len - first_query_pos > q.rows)
     return fail(GW_ERR_INVALID_ARG, fn, "%d rows in one step > max_step_rows %d", new_len - first_query_pos, q.rows);
-  A.extend(slot, new_len, first_query_pos);
+  if (A.extend(slot, new_len, first_query_pos) != 0)
+    return fail(GW_ERR_REFUSED, fn, "a free list cannot supply the pages (the reservations do not cover them)");
   return ok();
 }
 

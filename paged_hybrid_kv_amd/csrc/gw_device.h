@@ -313,12 +313,4 @@ __device__ __forceinline__ void put_global_record_as(uint8_t* pb, const GlobalRe
   else put_global_record<COMPRESSED>(pb, r, slot, l);
 }
 
-// Balanced split of n units into k parts: part i is [lo(i), lo(i+1)).
-// With n <= 2^20 pages (the entry points cap sequences at 2^24 tokens) and
-// i <= k <= n / 256 + 64, n * i stays below 2^32, so a 32-bit unsigned
-// division is exact -- and far shorter than the 64-bit sequence.
-__device__ __forceinline__ int split_lo(int n, int k, int i) {
-  return (int)((unsigned)(n * i) / (unsigned)k);
-}
-
 }  // namespace gw

@@ -569,6 +569,7 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   constexpr int kPerWave = kUnits / kW;       // units per wave per page ...
   constexpr int kPerWaveTail = kUnits % kW;   // ... the first kUnits % kW waves one more
   constexpr int kRows = kW * NR / HB;         // rows per workgroup
+  static_assert(NR != 1 || kRows == global_prefill_rows(16 * HB), "the host's item count");
   static_assert(NS >= 2 && NS - 2 <= 4 && (kPerWave + 1) * (NS - 2) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
 
@@ -791,14 +792,10 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool f
 }
 
 hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
-  // items: (prompt sequence, group of 8 / HB rows); at most
-  // (rows + sequences * (group - 1)) / group, and at most
-  // sequences * ceil(max_q_len / group)
+  // one workgroup per (prompt sequence, group of 8 / HB rows); the entry
+  // point has checked that the count fits a grid
   const bool h32 = a.num_q_heads == 32;
-  const int rows = h32 ? 4 : 8;
-  const int64_t by_rows = ((int64_t)a.num_rows + (int64_t)a.num_seqs * (rows - 1)) / rows;
-  const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + rows - 1) / rows);
-  const int64_t items = by_rows < by_len ? by_rows : by_len;
+  const long long items = prefill_items(a.num_rows, a.num_seqs, max_q_len, global_prefill_rows(a.num_q_heads));
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)items), block(512);

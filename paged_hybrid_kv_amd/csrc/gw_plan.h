@@ -42,6 +42,35 @@ __host__ __device__ inline int global_nsplit(int n_pages) {
   return k < k_min ? k_min : k;
 }
 
+// Balanced split of n units into k parts: part i is [split_lo(n, k, i),
+// split_lo(n, k, i + 1)), i.e. floor(n i / k).  Written as
+// (n / k) i + ((n % k) i) / k, which is the same integer (n = (n / k) k +
+// n % k, and (n / k) i is whole) but never forms the product n i: the first
+// term is at most n and the second's product is below k^2, so every value
+// stays in 32 bits for any n < 2^31 and k <= kMaxSplitsAny.  (n i itself
+// would pass 2^32 for the longest rows served, 2^20 pages split 4096 ways.)
+constexpr int kMaxSplitsAny = 46340;   // k^2 < 2^31
+__host__ __device__ inline int split_lo(int n, int k, int i) {
+  const int q = n / k, r = n - q * k;
+  return q * i + (r * i) / k;
+}
+
+// Prompt rows (sequences with more than one query row in a call).  A local
+// prompt-row workgroup takes kLocalPrefillVectors query vectors (a row and
+// one q head of its group): 128 / G consecutive rows of one (sequence, KV
+// head).  A global one takes 8 / HB rows (HB = q heads / 16).  Upper bound
+// on a call's (prompt sequence, row block) items: every sequence's rows in
+// blocks of `rows`, at most (rows of the call + sequences (rows - 1)) / rows
+// and at most sequences x ceil(max_q_len / rows).
+constexpr int kLocalPrefillVectors = 128;
+__host__ __device__ constexpr int local_prefill_rows(int group) { return kLocalPrefillVectors / group; }
+__host__ __device__ constexpr int global_prefill_rows(int num_q_heads) { return num_q_heads == 32 ? 4 : 8; }
+inline long long prefill_items(long long num_rows, long long num_seqs, long long max_q_len, long long rows) {
+  const long long by_rows = (num_rows + num_seqs * (rows - 1)) / rows;
+  const long long by_len = num_seqs * ((max_q_len + rows - 1) / rows);
+  return by_rows < by_len ? by_rows : by_len;
+}
+
 // Pages touched by the window of a query at position p: [p_lo/16, p/16].
 __host__ __device__ inline int local_range_pages(int p, int window) {
   int lo = p - window + 1;

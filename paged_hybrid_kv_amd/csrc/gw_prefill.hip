@@ -2,8 +2,8 @@
 // row in the call): sliding window, head dim 256, grouped query heads, bf16
 // or e4m3 pool.
 //
-// What is computed (pegainfer "Gemma 4" page, Scheduling: a new prompt's rows
-// are computed in the same step as the live streams' next token; intro and
+// What is computed (pegainfer "Gemma 4" page, Scheduling: prompt rows share
+// the step with the decode rows; intro and
 // Architecture notes for the window and the grouped heads): row r of
 // sequence s sits at position p_r = seq_len - q_len + r; each q head h of
 // KV head g = h / G attends the keys j in [max(0, p_r - W + 1), p_r].
@@ -128,11 +128,6 @@ constexpr float kLazyMax = 8.f;
 #endif
 constexpr int kPrefillQB = GW_PREFILL_QB;
 
-// Rows of prompt per workgroup: 128 query vectors.
-template <int G>
-constexpr int prefill_rows_per_wg() {
-  return 128 / G;
-}
 
 template <int G, bool FP8, int NS, int QB>
 __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAttnArgs a) {
@@ -141,21 +136,22 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   constexpr int kWaves = 8 / QB;               // waves per workgroup, QB query blocks each
   constexpr int kPerWavePage = kUnits / kWaves;   // units a wave moves of each page
   constexpr int kPerStep = 2 * kPerWavePage;   // transfers per wave per two-page step
-  constexpr int kRows = prefill_rows_per_wg<G>();
+  constexpr int kRows = local_prefill_rows(G);
   static_assert(NS >= 3 && NS - 2 <= 4 && kPerStep * (NS - 2) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][2][LH::kBytes];
 
-  const int gk = blockIdx.x;
+  // workgroup b: KV head b % Hkv of item b / Hkv (the head fastest)
+  const int gk = (int)blockIdx.x % a.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
   const int gq = lane >> 4, l16 = lane & 15;
 
   // ---- work item: the call's (prompt sequence, row block) items, numbered
   // sequence by sequence, the blocks of a sequence from its last (longest
-  // range) to its first; item blockIdx.y, for KV head blockIdx.x
+  // range) to its first
   int s = -1, rb = 0, row0 = 0, q_len = 0, L = 0;
   {
-    const int item = blockIdx.y;
+    const int item = (int)blockIdx.x / a.num_kv_heads;
     int base = 0;
     for (int c = 0; c < a.num_seqs; c += 64) {
       const int sl = c + lane;
@@ -417,19 +413,15 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
 
 hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int max_q_len,
                                 hipStream_t stream) {
-  // items: (prompt sequence, row block); sum over sequences of
-  // ceil(q_len / rows) is at most (rows + sequences * (rows - 1)) / rows
-  auto items = [&](int rows) {
-    const int64_t by_rows = ((int64_t)a.num_rows + (int64_t)a.num_seqs * (rows - 1)) / rows;
-    const int64_t by_len = (int64_t)a.num_seqs * ((max_q_len + rows - 1) / rows);
-    return (unsigned)(by_rows < by_len ? by_rows : by_len);
-  };
+  // one workgroup per (item, KV head); the entry point has checked that the
+  // count fits a grid
+  const long long n = prefill_items(a.num_rows, a.num_seqs, max_q_len, local_prefill_rows(group)) * a.num_kv_heads;
+  if (n == 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n), block(64 * (8 / kPrefillQB));
 #define GW_PREFILL_CASE(G_, F_)                                                                     \
   if (group == G_ && fp8 == F_) {                                                                   \
-    const unsigned n = items(prefill_rows_per_wg<G_>());                                            \
-    if (n == 0) return hipSuccess;                                                                  \
-    if (n > 65535) return hipErrorInvalidConfiguration;                                             \
-    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 4, kPrefillQB>), dim3(a.num_kv_heads, n), dim3(64 * (8 / kPrefillQB)), 0, stream, a); \
+    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 4, kPrefillQB>), grid, block, 0, stream, a);   \
     return hipGetLastError();                                                                       \
   }
   GW_PREFILL_CASE(1, false) GW_PREFILL_CASE(2, false) GW_PREFILL_CASE(4, false)

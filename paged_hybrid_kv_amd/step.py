@@ -2,8 +2,8 @@
 step's new K/V into its family's pool and attends with that family's page
 table (pegainfer "Gemma 4" page, intro: five local layers per global one,
 the last layer global; Scheduling: one pool and one page budget per family,
-local pages before the window freed, global pages kept; a new prompt's rows
-computed in the same step as the live streams' next token).
+local pages before the window freed, global pages kept; prompt rows share
+the step with the decode rows).
 
 Each layer owns its pool; all layers of a family share one page table.
 The step is plain C-ABI calls on one stream, so it can be captured once as a

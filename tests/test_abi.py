@@ -140,6 +140,14 @@ def glob(d=None, q=FAKE, hq=32, vn=None, cos=None, sin=None, indptr=None, lens=F
     (lambda: local(kn=FAKE, vn=FAKE, cos=FAKE), gw.GW_ERR_INVALID_ARG, "both"),
     (lambda: local(d=desc(rot=0), kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE), gw.GW_ERR_INVALID_ARG,
      "takes no rotary tables"),
+    # grids past 2^31 - 1 workgroups are refused before any launch: the
+    # decode rows' (split, KV head, sequence) grid, and the prompt rows'
+    # (row block, KV head) grid
+    (lambda: local(d=desc(heads=65535), hq=65535, S=65535, rows=65535, stride=512, wsb=1 << 62),
+     gw.GW_ERR_UNSUPPORTED, "decode workgroups"),
+    (lambda: local(d=desc(heads=32768), hq=32768, S=65535, rows=2 ** 31 - 1, indptr=FAKE, mql=8192, win=1,
+                   ws=None, wsb=0),
+     gw.GW_ERR_UNSUPPORTED, "prompt-row workgroups"),
 ])
 def test_local_rejects(call, code, frag):
     with pytest.raises(gw.GwError) as e:

@@ -38,8 +38,9 @@ def test_global_pool_is_slots_times_ceiling():
     """At the defaults (16 slots, 8192-token ceiling) the global pool that
     admits every slot at the ceiling is 16 x 512 pages; one page fewer and
     the sixteenth request waits."""
-    slots = GOLD["decode_slots"]["value"] if "decode_slots" in GOLD else 16
-    ceiling = GOLD["max_context"]["value"] if "max_context" in GOLD else 8192
+    slots = GOLD["decode_slots"]["value"]
+    ceiling = GOLD["max_context"]["value"]
+    assert GOLD["global_pool_rule"]["value"] == "slots x ceiling"
     need = slots * OA.pages_for(ceiling)
     assert need == 8192
     for pages, last in ((need, "admit"), (need - 1, "wait")):

@@ -4,8 +4,8 @@ appending its rows' own tokens first), checked on sampled rows against the
 CPU oracle.
 
 Workload: 16 decode slots with seeded contexts in [2048, 8192] plus 4 new
-512-token prompts (pegainfer "Gemma 4" page, Scheduling: a new prompt's rows
-are computed in the same step as the live streams' next token), and the same
+512-token prompts (pegainfer "Gemma 4" page, Scheduling: prompt rows share
+the step with the decode rows), and the same
 step with the prompt rows as a 512-token chunk after a cached 3584-token
 prefix (chunked prefill against cached context).  The oracle
 sees only the seeded draws of the layer (q, the step's new K/V and the prior
