@@ -60,8 +60,6 @@ class HybridStep:
             self.layers.append(self._make_layer(l, fill_context))
 
         D_l, D_g = sh.local_head_dim, sh.global_head_dim
-        self.out_local = torch.empty((self.rows, sh.local_q_heads, D_l), dtype=torch.float32, device=device)
-        self.out_global = torch.empty((self.rows, sh.global_q_heads, D_g), dtype=torch.float32, device=device)
         self.ws_local = Workspace(device)
         self.ws_global = Workspace(device)
         self.ws_bytes = {
@@ -94,8 +92,11 @@ class HybridStep:
             if len(ps):
                 gw.gw_kv_append(pool.desc, d.k_prior, d.v_prior, i32_dev(ps, self.device),
                                 i32_dev(pp, self.device), len(ps), pt, stride, cos, sin)
-        return dict(local=local, pool=pool, q=d.q, k_new=d.k_new, v_new=d.v_new, pt=pt,
-                    stride=stride, cos=cos, sin=sin)
+        # each layer writes its own output (the next layer's projection would read it)
+        Hq, D = (sh.local_q_heads, sh.local_head_dim) if local else (sh.global_q_heads, sh.global_head_dim)
+        out = torch.empty((self.rows, Hq, D), dtype=torch.float32, device=self.device)
+        return dict(index=l, local=local, pool=pool, q=d.q, k_new=d.k_new, v_new=d.v_new, pt=pt,
+                    stride=stride, cos=cos, sin=sin, out=out)
 
     # -------------------------------------------------------------- the step
     def append(self, L):
@@ -116,15 +117,19 @@ class HybridStep:
                                     self.q_indptr, self.seq_lens,
                                     L["pt"], L["stride"], self.S, self.rows, self.max_q_len, self.max_len,
                                     sh.window, 1.0 / np.sqrt(sh.local_head_dim),
-                                    self.out_local if out is None else out,
+                                    L["out"] if out is None else out,
                                     self.ws_ptr[fam], self.ws_bytes[fam])
         else:
             vn, cs, sn = (L["v_new"], L["cos"], L["sin"]) if append else (None,) * 3
             gw.gw_decode_attn_global(L["pool"].desc, L["q"], sh.global_q_heads, vn, cs, sn,
                                      self.q_indptr, self.seq_lens, L["pt"], L["stride"], self.S, self.rows,
                                      self.max_q_len, self.max_len, 1.0 / np.sqrt(sh.global_head_dim),
-                                     self.out_global if out is None else out,
+                                     L["out"] if out is None else out,
                                      self.ws_ptr[fam], self.ws_bytes[fam])
+
+    def layer_out(self, layer: int):
+        """fp32 [rows][Hq][D]: layer `layer`'s attention output of the last step."""
+        return self.layers[layer]["out"]
 
     def run(self):
         """One step, eagerly: every layer's attention call appends the step's
