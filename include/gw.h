@@ -21,6 +21,8 @@
  *   - The caller owns all memory: the library never allocates or frees
  *     device memory and never synchronizes.  Work is enqueued on `stream`
  *     (a hipStream_t passed as void*; NULL = the legacy default stream).
+ *     (One exception: gw_decode_attn_local_noalloc keeps its workspace in a
+ *     static device array of the library's own.)
  *   - Every host-checkable argument is validated before any HIP call; a
  *     rejected call returns a negative gw_status and launches nothing.
  *   - gw_last_error() then holds a message that starts with the name of the
@@ -30,7 +32,8 @@
  *     checked: seq_lens[s] >= 1; every page a call touches has a valid
  *     page-table entry in [0, num_pages); no two tokens of one append call
  *     write the same slot; positions < the rotary table length.
- *   - Reentrant; no mutable global state beyond the thread-local message.
+ *   - Reentrant; no mutable global state beyond the thread-local message
+ *     (and the per-device address of gw_decode_attn_local_noalloc's array).
  */
 #ifndef GW_H
 #define GW_H
@@ -232,6 +235,27 @@ int gw_decode_attn_local(const gw_pool_desc* pool /* host */, const void* q,
                          int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
                          int32_t max_seq_len, int32_t window, float scale, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* gw_decode_attn_local without a workspace argument, for callers that
+ * cannot allocate device memory around the call (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, arithmetic, kernels and results as gw_decode_attn_local; the
+ * split partials, counters and call epochs live instead in a scratch array
+ * of the library's own, 32 MiB per GPU (static device memory, held until the
+ * process ends).  A call whose plan needs more (gw_attn_workspace_bytes of
+ * its shape above 32 MiB) returns GW_ERR_WORKSPACE before any HIP call.
+ * Each call first clears the region it uses, so calls of any shape may
+ * follow one another.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (concurrent streams or threads) race and
+ * must be serialised by the caller.  The library allocates nothing here; the
+ * array's device address is looked up once per device on the first call. */
+int gw_decode_attn_local_noalloc(const gw_pool_desc* pool /* host */, const void* q,
+                                 int32_t num_q_heads, const void* k_new, const void* v_new,
+                                 const float* rope_cos, const float* rope_sin, const int32_t* q_indptr,
+                                 const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
+                                 int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                                 int32_t max_seq_len, int32_t window, float scale, float* out,
+                                 void* stream);
 
 /* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16
  * or e4m3).  num_q_heads 16 or 32.  The two layouts give bit-identical

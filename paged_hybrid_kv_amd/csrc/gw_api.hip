@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gw.h"
 #include "gw_alloc.h"
@@ -242,13 +243,52 @@ size_t gw_attn_workspace_bytes(int32_t family, int32_t num_seqs, int32_t num_row
   return plan_workspace(family, num_seqs, num_q_heads, num_q_heads, head_dim, max_seq_len, window, 4).total;
 }
 
-int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
-                         const void* k_new, const void* v_new, const float* rope_cos,
-                         const float* rope_sin, const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
-                         int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
-                         int32_t max_seq_len, int32_t window, float scale, float* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  const char* fn = "gw_decode_attn_local";
+}  // extern "C"
+
+namespace {
+
+// The allocation-free local entry point's workspace: one array per GPU, in
+// the library's own device memory, held until the process ends.  Host code
+// uses it only through the device address hipGetSymbolAddress returns for
+// the current device (kept per device); the array's name is a host-side
+// stand-in, not that address.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array of the current device (its address resolved on the
+// first call on that device), or an error status.
+int scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(GW_ERR_UNSUPPORTED, fn, "device %d (served: 0 .. %d)", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!ptr) return fail(GW_ERR_HIP, fn, "no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GW_OK;
+}
+
+// Zero n bytes (a multiple of 16) at p: a plain fill kernel rather than a
+// memset node, so that the call can be captured in a graph.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+               const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
+               const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
+               int32_t num_seqs, int32_t num_rows, int32_t max_q_len, int32_t max_seq_len, int32_t window,
+               float scale, float* out, void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   int rc = check_pool(pool, fn);
   if (rc != GW_OK) return rc;
   if (!is_local(pool->family))
@@ -284,12 +324,32 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
     if (pre_wgs > kMaxGrid)
       return fail(GW_ERR_UNSUPPORTED, fn, "%lld prompt-row workgroups (served: up to %lld)", pre_wgs, kMaxGrid);
   }
-  if (workspace_bytes < w.total)
-    return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
-  if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
-  if (w.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
-    return fail(GW_ERR_INVALID_ARG, fn, "workspace is not 256-byte aligned");
+  if (noalloc) {
+    if (w.total > kScratchBytes)
+      return fail(GW_ERR_WORKSPACE, fn, "the call needs %zu bytes of scratch; this entry point holds %zu",
+                  w.total, kScratchBytes);
+  } else {
+    if (workspace_bytes < w.total)
+      return fail(GW_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+    if (w.total > 0 && !workspace) return fail(GW_ERR_INVALID_ARG, fn, "workspace is null");
+    if (w.total > 0 && ((uintptr_t)workspace % kAlign) != 0)
+      return fail(GW_ERR_INVALID_ARG, fn, "workspace is not 256-byte aligned");
+  }
   if (num_seqs == 0 || num_rows == 0) return ok();
+  if (noalloc && w.total > 0) {
+    // every call starts from a zeroed region: the split counters and call
+    // epochs of the previous call (of any shape) sit elsewhere, and its
+    // tagged partials must not pass for this call's
+    rc = scratch_for_current_device(fn, &workspace);
+    if (rc != GW_OK) return rc;
+    (void)hipGetLastError();
+    const size_t n16 = w.total / 16;   // the plan's regions are 256-byte multiples
+    const unsigned blocks = (unsigned)std::min<size_t>((n16 + 255) / 256, 2048);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<uint4*>(workspace), n16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
 
   gw::LocalAttnArgs a{};
   a.pool = static_cast<const uint8_t*>(pool->base);
@@ -348,6 +408,32 @@ int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gw_decode_attn_local(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+                         const void* k_new, const void* v_new, const float* rope_cos,
+                         const float* rope_sin, const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
+                         int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
+                         int32_t max_seq_len, int32_t window, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attn_local("gw_decode_attn_local", pool, q, num_q_heads, k_new, v_new, rope_cos, rope_sin, q_indptr,
+                    seq_lens, page_table, pt_stride, num_seqs, num_rows, max_q_len, max_seq_len, window, scale,
+                    out, workspace, workspace_bytes, false, stream);
+}
+
+int gw_decode_attn_local_noalloc(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
+                                 const void* k_new, const void* v_new, const float* rope_cos,
+                                 const float* rope_sin, const int32_t* q_indptr, const int32_t* seq_lens,
+                                 const int32_t* page_table, int32_t pt_stride, int32_t num_seqs,
+                                 int32_t num_rows, int32_t max_q_len, int32_t max_seq_len, int32_t window,
+                                 float scale, float* out, void* stream) {
+  return attn_local("gw_decode_attn_local_noalloc", pool, q, num_q_heads, k_new, v_new, rope_cos, rope_sin,
+                    q_indptr, seq_lens, page_table, pt_stride, num_seqs, num_rows, max_q_len, max_seq_len, window,
+                    scale, out, nullptr, 0, true, stream);
 }
 
 int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,

@@ -30,7 +30,8 @@ GW_KV_BF16 = 1
 GW_KV_E4M3 = 2
 
 EXPORTS = ("gw_version", "gw_last_error", "gw_pool_page_bytes", "gw_rope_table", "gw_kv_append",
-           "gw_attn_workspace_bytes", "gw_decode_attn_local", "gw_decode_attn_global",
+           "gw_attn_workspace_bytes", "gw_decode_attn_local", "gw_decode_attn_local_noalloc",
+           "gw_decode_attn_global",
            "gw_alloc_create", "gw_alloc_destroy", "gw_alloc_admit", "gw_alloc_extend", "gw_alloc_release",
            "gw_alloc_tables", "gw_alloc_stats", "gw_copy_pages")
 
@@ -83,6 +84,9 @@ def lib():
         L.gw_decode_attn_local.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P, _P,
                                            _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
                                            ctypes.c_size_t, _P]
+        L.gw_decode_attn_local_noalloc.restype = ctypes.c_int
+        L.gw_decode_attn_local_noalloc.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P,
+                                                   _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P]
         L.gw_decode_attn_global.restype = ctypes.c_int
         L.gw_decode_attn_global.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P, _P,
                                             _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t,
@@ -173,6 +177,16 @@ def gw_decode_attn_local(desc: gw_pool_desc, q, num_q_heads, k_new, v_new, rope_
                                       _ptr(seq_lens), _ptr(page_table), pt_stride, num_seqs,
                                       num_rows, max_q_len, max_seq_len, window, scale, _ptr(out),
                                       _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gw_decode_attn_local_noalloc(desc: gw_pool_desc, q, num_q_heads, k_new, v_new, rope_cos, rope_sin,
+                                 q_indptr, seq_lens, page_table, pt_stride, num_seqs, num_rows, max_q_len,
+                                 max_seq_len, window, scale, out, stream=None):
+    _check(lib().gw_decode_attn_local_noalloc(ctypes.byref(desc), _ptr(q), num_q_heads, _ptr(k_new),
+                                              _ptr(v_new), _ptr(rope_cos), _ptr(rope_sin), _ptr(q_indptr),
+                                              _ptr(seq_lens), _ptr(page_table), pt_stride, num_seqs,
+                                              num_rows, max_q_len, max_seq_len, window, scale, _ptr(out),
+                                              _stream(stream)))
 
 
 def gw_decode_attn_global(desc: gw_pool_desc, q, num_q_heads, v_new, rope_cos, rope_sin, q_indptr,

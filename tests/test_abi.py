@@ -174,6 +174,28 @@ def test_global_rejects(call, code, frag):
     assert frag in e.value.message
 
 
+def test_local_noalloc_rejects():
+    # the same host checks as the workspace entry point, named after the
+    # entry point that ran, and a plan too large for the library's scratch
+    # array refused before any HIP call
+    def noalloc(**kw):
+        a = dict(d=desc(), q=FAKE, hq=16, lens=FAKE, pt=FAKE, stride=512, S=4, rows=4, mql=1, msl=8192,
+                 win=1024, scale=0.0625, out=FAKE)
+        a.update(kw)
+        gw.gw_decode_attn_local_noalloc(a["d"], a["q"], a["hq"], None, None, None, None, None, a["lens"],
+                                        a["pt"], a["stride"], a["S"], a["rows"], a["mql"], a["msl"], a["win"],
+                                        a["scale"], a["out"])
+    for kw, code, frag in ((dict(win=0), gw.GW_ERR_INVALID_ARG, "window"),
+                           (dict(hq=64), gw.GW_ERR_UNSUPPORTED, "group size 8"),
+                           (dict(S=65535, rows=65535), gw.GW_ERR_WORKSPACE, "scratch")):
+        with pytest.raises(gw.GwError) as e:
+            noalloc(**kw)
+        assert e.value.code == code
+        assert e.value.message.startswith("gw_decode_attn_local_noalloc: ")
+        assert frag in e.value.message
+    noalloc(S=0, rows=0)   # empty batch: no-op, no GPU call
+
+
 def test_empty_batches_are_noops():
     local(S=0, rows=0, ws=None, wsb=0)
     glob(S=0, rows=0, ws=None, wsb=0)
