@@ -268,12 +268,15 @@ __device__ __forceinline__ void put_global_record(uint8_t* pb, const GlobalRecor
   uint8_t* vblock = COMPRESSED ? pb : pb + 16384;
   uint8_t* kblock = COMPRESSED ? pb + 16384 : pb;
   *reinterpret_cast<uint4*>(vblock + (l * 16 + slot) * 16) = r.v;
-  if (l < 8) {
-    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 16) = r.ka;
-    *reinterpret_cast<uint4*>(kblock + ((l + 8) * 16 + slot) * 16) = r.kb;
-  } else if (!COMPRESSED && l >= 16) {
-    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 16) = r.v;   // K dims >= 128 are V's
+  // K chunk l: the rotated chunk (l < 8) or, in the full record, V's (K dims
+  // >= 128 are V's); the value is selected, not the source, so the record
+  // stays in registers
+  const bool rot = l < 8;
+  if (rot || (!COMPRESSED && l >= 16)) {
+    const uint4 k = {rot ? r.ka.x : r.v.x, rot ? r.ka.y : r.v.y, rot ? r.ka.z : r.v.z, rot ? r.ka.w : r.v.w};
+    *reinterpret_cast<uint4*>(kblock + (l * 16 + slot) * 16) = k;
   }
+  if (rot) *reinterpret_cast<uint4*>(kblock + ((l + 8) * 16 + slot) * 16) = r.kb;
 }
 
 // Eight bf16 (a 16-byte chunk) -> their eight e4m3 codes, in order.
@@ -299,12 +302,13 @@ __device__ __forceinline__ void put_global_record_e4m3(uint8_t* pb, const Global
   auto at = [&](uint8_t* blk, int c8) { return blk + ((c8 >> 1) * 16 + slot) * 16 + 8 * (c8 & 1); };
   const uint2 v8 = e4m3x8_of_bf16x8(r.v);
   *reinterpret_cast<uint2*>(at(vblock, l)) = v8;
-  if (l < 8) {
-    *reinterpret_cast<uint2*>(at(kblock, l)) = e4m3x8_of_bf16x8(r.ka);
-    *reinterpret_cast<uint2*>(at(kblock, l + 8)) = e4m3x8_of_bf16x8(r.kb);
-  } else if (!COMPRESSED && l >= 16) {
-    *reinterpret_cast<uint2*>(at(kblock, l)) = v8;   // K dims >= 128 are V's
+  const bool rot = l < 8;   // as in put_global_record: select the value, not the source
+  if (rot || (!COMPRESSED && l >= 16)) {
+    const uint2 ka8 = e4m3x8_of_bf16x8(r.ka);
+    const uint2 k = {rot ? ka8.x : v8.x, rot ? ka8.y : v8.y};
+    *reinterpret_cast<uint2*>(at(kblock, l)) = k;
   }
+  if (rot) *reinterpret_cast<uint2*>(at(kblock, l + 8)) = e4m3x8_of_bf16x8(r.kb);
 }
 
 template <bool COMPRESSED, bool FP8>

@@ -9,35 +9,37 @@
 // Both records take the same arithmetic, so their results are bit-identical.
 //
 // With every q head on one KV head the score and value steps are dense
-// contractions (heads x 16 tokens x 512 dims per page), so both run on MFMA
-// with fp32 accumulation, in 16 x 16 blocks:
+// contractions, so both run on MFMA (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation), in 16 x 16 blocks over a pair of pages (32 tokens):
 //   S^T (16 tokens x 16 heads) = K (16 x 512) . Q^T (512 x 16 heads)
-//                                  -- v_mfma_f32_16x16x32_bf16, 16 steps
-//   O^T (16 dims x 16 heads)  += V^T (16 x 16 tokens) . P^T (16 x 16 heads)
-//                                  -- v_mfma_f32_16x16x16_bf16, per dim block
-// The S^T result already sits in the lanes as the P^T operand wants it (lane
-// l: head l % 16, tokens 4(l/16) .. +3), so the softmax of a page stays in
-// the wave.
+//                                  -- per page of the pair
+//   O^T (16 dims x 16 heads)  += V^T (16 dims x 32 tokens) . P^T (32 x 16)
+//                                  -- per 16-dim block, both pages at once
+// The S^T results already sit in the lanes as the P^T operand wants them
+// (lane l: head l % 16, tokens 4(l/16) .. +3 of each page; those eight
+// tokens are the lane's k slots of the PV product), so the softmax of a pair
+// stays in the wave, and the V^T operand holds the same eight tokens: the
+// gfx950 transposing LDS reads give a lane one dim of four (bf16,
+// ds_read_b64_tr_b16, once per page) or eight (e4m3, ds_read_b64_tr_b8, both
+// pages in one read) tokens.
 //
 // Work split: one workgroup per (sequence, split) item, numbered compactly
 // (workgroup b takes item b); a split is a balanced run of the row's pages
-// (gw_plan.h).  A workgroup is two groups of four waves that take alternate
-// pages of the split, each with its own online-softmax state, merged at the
-// end.  Inside a group, wave w takes head block w % 2 (16 heads; with 16 q
-// heads, the only block) and a slice of the output dims (256 dims per wave
-// with 32 heads, 128 with 16); the waves of a head block split the score
-// contraction's 512 dims the same way and add their partial scores through
-// LDS, in a fixed order, so each score is computed once.  Pages stream
-// straight from HBM into a ring of LDS page pairs (global_load_lds_dwordx4,
-// each wave moving a quarter of its group's page), NP - 1 pairs in flight
-// while one is read; after an LDS-only barrier each wave reads K (as stored)
-// and V^T (through the gfx950 transposing LDS read ds_read_b64_tr_b16, or
-// for an e4m3 page plain reads and a byte transpose across lanes) from its
-// group's page.  On the
-// row's last page, V of tokens past the row's position is zeroed in the
-// operand registers and their scores are masked, so unwritten slots (possibly
-// NaN) never reach the output.  P is rounded to bf16 for PV and the sum l
-// adds exactly those rounded values.
+// (gw_plan.h).  The split's pages go by in pairs, and all eight waves work on
+// every pair: wave w takes head block hb (16 heads: w % 2 with 32 q heads,
+// the only block with 16), 128 of the score contraction's 512 dims (part w / 2,
+// or w % 4 with 16 heads) and a slice of the output dims (128 dims with 32
+// heads, 64 with 16).  The waves of a head block add their partial scores
+// through LDS in a fixed part order, so every wave of the block holds the same
+// full scores and the same online-softmax state.  The running max moves only
+// when a score passes it by more than 2^8 (so the accumulators are rarely
+// rescaled; the unnormalised weights stay below 2^8).  Pages stream straight
+// from HBM into a ring of LDS pair slots (global_load_lds_dwordx4, every wave
+// moving its share of every pair), NP - 1 pairs in flight while one is read.
+// On the split's last pair, tokens past the row's position (and the missing
+// second page of an odd split) get masked scores and zeroed V operands, so
+// unwritten slots (possibly NaN) never reach the output.  P is rounded to
+// bf16 for PV and the sum l adds exactly those rounded values.
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -48,26 +50,30 @@ namespace {
 
 constexpr int kGD = 512;
 
-// LDS ring depth in page pairs, compressed / full record (3 x 40 KiB and
-// 2 x 64 KiB: one workgroup per CU either way).
+// LDS ring depth in page pairs: bf16 compressed / full record (3 x 40 KiB,
+// 2 x 64 KiB), e4m3 compressed / full (5 x 20 KiB, 3 x 32 KiB, q in a 32
+// KiB region of its own); with the 16 KiB score exchange, one workgroup per CU.
 #ifndef GW_GLOBAL_NP_C
 #define GW_GLOBAL_NP_C 3
 #endif
 #ifndef GW_GLOBAL_NP_F
 #define GW_GLOBAL_NP_F 2
 #endif
-// e4m3 pages (10 and 16 KiB): 6 x 20 KiB and 3 x 32 KiB, q in a 32 KiB
-// region of its own
 #ifndef GW_GLOBAL_NP_C8
-#define GW_GLOBAL_NP_C8 6
+#define GW_GLOBAL_NP_C8 5
 #endif
 #ifndef GW_GLOBAL_NP_F8
 #define GW_GLOBAL_NP_F8 3
 #endif
 
+// The reference max moves only when a score (base 2) passes it by more than this.
+constexpr float kLazyMaxG = 8.f;
+
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // FP8: the e4m3 page, its blocks in 16-dim chunks (16 bytes of a token).
@@ -84,170 +90,111 @@ struct GlobalPage {
   }
 };
 
-// A page for one wave: its share of the scores of its 16 heads against the
-// page's 16 tokens (global_page_scores), then, with the head block's partial
-// scores added, the online-softmax update and the PV product into the wave's
-// output-dim slice (global_page_update).  pg: the page in LDS; tok_page0:
-// the position of the page's first token; p: the row's position (tokens past
-// it are masked, and their V zeroed, so unwritten slots never reach the
-// output).
-// The wave's share of S^T = K . Q^T: the 4 HB 32-dim steps ks0 .. (the
-// waves of a head block split the 512 dims between them; their partial
-// sums are added through LDS).  The K fragments are read first (their LDS
-// latencies overlap), then two accumulation chains; lane holds head l16,
-// tokens 4g .. 4g+3.  e4m3 fragments (8 bytes) widen exactly to bf16 just
-// before their product.
-template <bool COMPRESSED, int HB, bool FP8 = false>
-__device__ __forceinline__ f32x4 global_page_scores(const uint8_t* pg, const bf16x8 (&qf)[4 * HB], int ks0, int g,
-                                                    int l16) {
-  using PG = GlobalPage<COMPRESSED, FP8>;
-  constexpr int kKs = 4 * HB;
-  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-  if constexpr (FP8) {
-    uint2 kr[kKs];
-#pragma unroll
-    for (int k = 0; k < kKs; ++k) kr[k] = *reinterpret_cast<const uint2*>(pg + PG::k_off(4 * (ks0 + k) + g, l16));
-    __builtin_amdgcn_sched_barrier(0);
-    auto widen = [](uint2 r) __attribute__((always_inline)) {
-      return __builtin_bit_cast(bf16x8, uint4{e4m3x2_to_bf16x2<false>(r.x), e4m3x2_to_bf16x2<true>(r.x),
-                                              e4m3x2_to_bf16x2<false>(r.y), e4m3x2_to_bf16x2<true>(r.y)});
-    };
-#pragma unroll
-    for (int k = 0; k < kKs; k += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(kr[k]), qf[k], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(kr[k + 1]), qf[k + 1], s1, 0, 0, 0);
-    }
-  } else {
-    bf16x8 kf[kKs];
-#pragma unroll
-    for (int k = 0; k < kKs; ++k) kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (ks0 + k) + g, l16));
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
-#pragma unroll
-    for (int k = 0; k < kKs; k += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k + 1], qf[k + 1], s1, 0, 0, 0);
-    }
-  }
-  return s0 + s1;
-}
-
-// The rest of a page for one wave, given the page's full scores sacc: the
-// online-softmax update and the PV product into the wave's output-dim slice.
-template <bool COMPRESSED, int HB, bool FP8 = false>
-__device__ __forceinline__ void global_page_update(f32x4 (&acc)[8 * HB], float& m_run, float& l_run,
-                                                   const uint8_t* pg, const f32x4 sacc, int tok_page0, int p, int g,
-                                                   int l16, int v_lane_off, float scale_log2) {
-  constexpr int kBlocks = 8 * HB;
-  // ---- online softmax for head l16 over the page's 16 tokens
-  const int tok0 = tok_page0 + 4 * g;
-  float z[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) z[r] = (tok0 + r <= p) ? sacc[r] * scale_log2 : -INFINITY;
-  const float mx = max_lanes_xor16_32(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-  const float mnew = fmaxf(m_run, mx);
-  if (__any(mnew > m_run)) {
-    const float alpha = mnew > m_run ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
-    l_run *= alpha;
-  }
-  m_run = mnew;
-  const uint32_t p01 = pack_bf16(__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run));
-  const uint32_t p23 = pack_bf16(__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run));
-  l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-  const s16x4 pb = __builtin_bit_cast(s16x4, uint2{p01, p23});
-
-  // ---- O^T += V^T . P^T.  On the row's last page, V of tokens past p
-  // (unwritten slots, possibly NaN) is zeroed in the operand registers.
-  uint32_t vm0 = 0xffffffffu, vm1 = 0xffffffffu;
-  if (tok_page0 + 15 > p) {
-    vm0 = (tok0 + 0 <= p ? 0x0000ffffu : 0u) | (tok0 + 1 <= p ? 0xffff0000u : 0u);
-    vm1 = (tok0 + 2 <= p ? 0x0000ffffu : 0u) | (tok0 + 3 <= p ? 0xffff0000u : 0u);
-  }
-  if constexpr (FP8) {
-    // lane (g, 4a + c) reads dims 16b + 4a .. +3 of token 4g + c (4 bytes);
-    // a byte transpose inside each quad of lanes (two DPP exchanges) leaves
-    // lane c with dim 16b + 4a + c of tokens 4g .. 4g+3, which widen to bf16
-    uint32_t vr[kBlocks];
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) vr[b] = *reinterpret_cast<const uint32_t*>(pg + v_lane_off + 256 * b);
-    __builtin_amdgcn_sched_barrier(0);
-    // byte selectors of v_perm_b32 (bytes 0-3: own word, 4-7: partner's):
-    // step 1 with the xor-1 partner keeps bytes 0, 2 (even lane) or 1, 3
-    // (odd lane) of both; step 2 with the xor-2 partner keeps the low
-    // (lanes 0, 1) or high (lanes 2, 3) halves of both
-    const int c = l16 & 3;
-    const uint32_t sel1 = (c & 1) ? 0x03070105u : 0x06020400u;
-    const uint32_t sel2 = (c & 2) ? 0x03020706u : 0x05040100u;
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) {
-      const uint32_t x = vr[b];
-      const uint32_t xp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kQuadSwap1, 0xf, 0xf, false);
-      const uint32_t y = __builtin_amdgcn_perm(xp, x, sel1);
-      const uint32_t yp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, kQuadSwap2, 0xf, 0xf, false);
-      const uint32_t z = __builtin_amdgcn_perm(yp, y, sel2);
-      const uint2 vv = uint2{e4m3x2_to_bf16x2<false>(z) & vm0, e4m3x2_to_bf16x2<true>(z) & vm1};
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
-    }
-  } else {
-    lds_u8* vrow = (lds_u8*)pg + v_lane_off;
-    uint2 vf[kBlocks];
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
-      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * b)));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) {
-      uint2 vv = vf[b];
-      vv.x &= vm0;
-      vv.y &= vm1;
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb, acc[b], 0, 0, 0);
-    }
-  }
-}
-
 // Byte offset, inside a page, of what lane (g, l16) names in the transposing
-// read of V for dims d_lo .. (lane (g, e, q) names token 4g + e, dims
+// read of bf16 V for dims d_lo .. (lane (g, e, q) names token 4g + e, dims
 // d_lo + 4q .. +3, and receives dim d_lo + l16 of tokens 4g .. 4g+3).
-// e4m3 (FP8): lane (g, 4a + c) reads dims d_lo + 4a .. +3 of token 4g + c.
-template <bool COMPRESSED, bool FP8 = false>
+template <bool COMPRESSED>
 __device__ __forceinline__ int global_v_lane_off(int d_lo, int g, int l16) {
-  if constexpr (FP8)
-    return GlobalPage<COMPRESSED, FP8>::kVOff + ((d_lo >> 4) * 16 + 4 * g + (l16 & 3)) * 16 + 4 * (l16 >> 2);
   const int t_rd = 4 * g + (l16 >> 2);
   const int dd = d_lo + 4 * (l16 & 3);
   return GlobalPage<COMPRESSED>::kVOff + ((dd >> 3) * 16 + t_rd) * 16 + (dd & 7) * 2;
 }
 
-// One workgroup = two groups of four waves.  Group q (0, 1) takes the pages
-// 2j + q of the split: in every step j the two groups work on the two pages
-// of pair j side by side (one wave of each group per SIMD, so the phases of
-// one overlap the other's), each with its own online-softmax state; the two
-// states merge once at the end, group 1 into group 0, in that order.
-// NP: page pairs in the LDS ring (NP - 1 pairs in flight while one is read).
-// FP8: e4m3 pages, widened to bf16 as they are read from LDS; q then has an
-// LDS region of its own after the ring, and a 10 KiB compressed page moves
-// as 3 + 3 + 2 + 2 units (waves 0, 1 take one unit of the last two each).
+// 8 e4m3 codes -> 8 bf16 (exact), in order.
+__device__ __forceinline__ bf16x8 widen_e4m3x8(uint32_t w0, uint32_t w1) {
+  return __builtin_bit_cast(bf16x8, uint4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                          e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
+}
+
+// A pair of pages in LDS (page a at pa, page b at pa + kBytes), for one wave:
+//
+// global_pair_scores: the wave's share of S^T = K . Q^T for both pages, over
+// the four 32-dim steps 4 sp .. 4 sp + 3 of its score part (the waves of a
+// head block add their shares through LDS); lane holds head l16, tokens
+// 4g .. 4g+3 of each page.  All eight K fragments are read before the
+// products.  e4m3 fragments (8 bytes) widen exactly to bf16 just before
+// their product.
+template <bool COMPRESSED, bool FP8>
+__device__ __forceinline__ void global_pair_scores(f32x4 (&s)[2], const lds_u8* pa, const bf16x8 (&qf)[4], int sp,
+                                                   int g, int l16) {
+  using PG = GlobalPage<COMPRESSED, FP8>;
+  if constexpr (FP8) {
+    i32x2 kr[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        kr[t][k] = *reinterpret_cast<const lds_i32x2*>(pa + t * PG::kBytes + PG::k_off(4 * (4 * sp + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_e4m3x8((uint32_t)kr[t][k][0], (uint32_t)kr[t][k][1]),
+                                                       qf[k], s[t], 0, 0, 0);
+    }
+  } else {
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        kf[t][k] = *reinterpret_cast<const lds_bf16x8*>(pa + t * PG::kBytes + PG::k_off(4 * (4 * sp + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][k], qf[k], s[t], 0, 0, 0);
+    }
+  }
+}
+
+// The V^T operand of output block b (16 dims) for the pair: lane (g, l16)
+// gets dim (its block's first dim + l16) of tokens 4g .. 4g+3 of page a,
+// then of page b, as 8 bf16.  vo: the lane's byte offset for block 0 (bf16:
+// global_v_lane_off in page a; e4m3: the tr8 row it names, in page a or b).
+template <bool COMPRESSED, bool FP8>
+__device__ __forceinline__ uint4 global_pair_vt(const lds_u8* pa, int vo, int b) {
+  if constexpr (FP8) {
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(pa + vo + 256 * b));
+    return __builtin_bit_cast(uint4, widen_e4m3x8((uint32_t)r[0], (uint32_t)r[1]));
+  } else {
+    constexpr int kB = GlobalPage<COMPRESSED>::kBytes;
+    const uint2 va = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + vo + 512 * b)));
+    const uint2 vb =
+        __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + kB + vo + 512 * b)));
+    return uint4{va.x, va.y, vb.x, vb.y};
+  }
+}
+
+// One workgroup = eight waves on one (sequence, split) item; see the header
+// for the work split.  NP: page pairs in the LDS ring (NP - 1 pairs in
+// flight while one is read).  FP8: e4m3 pages, widened to bf16 as they are
+// read from LDS; q then has an LDS region of its own after the ring.
 template <bool COMPRESSED, int HB, int NP, bool FP8 = false>
 __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a) {
   using PG = GlobalPage<COMPRESSED, FP8>;
-  constexpr int kUnits = PG::kBytes / 1024;   // 1 KiB transfer units per page
-  constexpr int kPerWave = (kUnits + 3) / 4;  // most units a wave moves per page
-  constexpr int kExtra = kUnits - 4 * (kUnits / 4);   // waves below kExtra move one more
-  constexpr int kBlocks = 8 * HB;             // 16-dim output blocks per wave
-  constexpr int kRingBytes = NP * 2 * PG::kBytes;
+  constexpr int kPair = 2 * PG::kBytes;
+  constexpr int kUnits = kPair / 1024;        // 1 KiB transfer units per pair
+  constexpr int kEven = kUnits / 8;           // units every wave moves ...
+  constexpr int kExtra = kUnits % 8;          // ... and one more for waves below kExtra
+  constexpr int kPerWave = kEven + (kExtra > 0 ? 1 : 0);
+  constexpr int kBlocks = HB == 2 ? 8 : 4;    // 16-dim output blocks per wave
+  constexpr int kRingBytes = NP * kPair;
+  constexpr int kXsOff = kRingBytes;          // score exchange: [wave][lane][page] f32x4
+  constexpr int kQOff = kXsOff + 8 * 64 * 32; // e4m3: q
   static_assert(NP >= 2 && kPerWave * (NP - 2) < 64 && NP - 2 <= 4, "ring depth");
-  static_assert(kRingBytes >= 4 * kBlocks * 64 * 16 + 4 * 64 * 8, "the ring holds the group merge");
-  static_assert(FP8 || 2 * PG::kBytes >= 32 * 1024, "a ring slot holds q");
-  constexpr int kXsOff = kRingBytes + (FP8 ? 32 * 1024 : 0);   // partial scores, [wave][lane] f32x4
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + 8 * 64 * 16];
-  uint8_t(*ring)[2][PG::kBytes] = reinterpret_cast<uint8_t(*)[2][PG::kBytes]>(smem);
+  static_assert(FP8 || kPair >= 32 * 1024, "a ring slot holds q");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQOff + (FP8 ? 32 * 1024 : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = uniform_i32(tid >> 6);
-  const int grp = wv >> 2, w = wv & 3;
+  const int w = uniform_i32(tid >> 6);
   const int hb = HB == 2 ? (w & 1) : 0;
-  const int d_lo = HB == 2 ? 256 * (w >> 1) : 128 * w;
+  const int sp = HB == 2 ? (w >> 1) : (w & 3);          // score part: dims 128 sp ..
+  const int d_lo = HB == 2 ? 128 * (w >> 1) : 64 * w;   // output dims d_lo .. + 16 kBlocks
   const int g = lane >> 4, l16 = lane & 15;
 
   // ---- work item of this workgroup: the call's (sequence, split) items are
@@ -323,46 +270,51 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   // page once the page has landed
   const bool append_here = a.v_new != nullptr && split == nsplit - 1;
   GlobalRecordLane rec{};
-  if (append_here && wv == 0)
+  if (append_here && w == 0)
     rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
   asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
-  if (append_here && wv == 0)
+  if (append_here && w == 0)
     put_global_record_as<COMPRESSED, FP8>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
                                           p & 15, lane);
 
-  // ---- q into LDS by direct transfers, ahead of the pages, in ring slot
-  // NP - 1 (free until the loop's first transfer): 1 KiB per head, the
+  // ---- q into LDS by direct transfers, ahead of the pages (bf16: in ring
+  // slot NP - 1, free until the loop's first transfer): 1 KiB per head, the
   // row's 16-byte chunk c of head h stored at chunk c ^ (h % 8), so that the
-  // Q^T operand reads below hit distinct banks.  Wave wv moves heads
-  // 2 HB wv .. +2 HB - 1; lane i fetches the chunk that lands at position i.
-  uint8_t* qs = FP8 ? smem + kRingBytes : &ring[NP - 1][0][0];
+  // Q^T operand reads below hit distinct banks.  Wave w moves heads
+  // 2 HB w .. +2 HB - 1; lane i fetches the chunk that lands at position i.
+  uint8_t* qs = FP8 ? smem + kQOff : smem + (NP - 1) * kPair;
   {
     const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
     for (int i = 0; i < 2 * HB; ++i) {
-      const int h = 2 * HB * wv + i;
+      const int h = 2 * HB * w + i;
       dma16_to_lds(a.q + ((int64_t)row * a.num_q_heads + h) * kGD + 8 * (lane ^ (h & 7)),
                    qs_lds + (uint32_t)(h * 1024));
     }
   }
 
-  // ---- transfers: group q moves page 2j + q of pair j, wave w of the group
-  // the units [kPerWave w, kPerWave (w + 1)) of the page (1 KiB each), so
-  // the LDS copy has the pool's layout.  An odd split's last pair repeats
-  // its last page as the second one; that copy is never computed on.  The
-  // loop's waits count transfers only; the appending wave's pool stores and
-  // the q transfers are older than all of them, so they are covered too.
-  // wave w moves units kUnits/4 * w + u, and, below kExtra, unit 4 (kUnits/4) + w
-  constexpr int kEven = kUnits / 4;
+  // ---- transfers: unit u (1 KiB) of pair j is unit u % (kUnits / 2) of
+  // page 2j (u < kUnits / 2) or page 2j + 1, landing at unit u of the pair's
+  // ring slot, so the LDS copy has the pool's layout.  Wave w moves units
+  // kEven w .. + kEven - 1 and, below kExtra, unit 8 kEven + w.  An odd
+  // split's last pair repeats its last page as the second; that copy's
+  // scores are masked and its V zeroed.  The loop's waits count transfers
+  // only; the appending wave's pool stores and the q transfers are older
+  // than all of them, so they are covered too.
   const int my_units = kEven + (w < kExtra ? 1 : 0);
-  const uint32_t ring_base = uniform_i32((int)lds_address(&ring[0][0][0])) + (uint32_t)(grp * PG::kBytes);
+  const uint32_t ring_base = uniform_i32((int)lds_address(smem));
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
-    const int i = min(2 * j + grp, n - 1);
-    const uint8_t* src = a.pool + (int64_t)phys(i) * a.page_bytes + 16 * lane;
-    const uint32_t dst = ring_base + (uint32_t)((j % NP) * 2 * PG::kBytes);
+    const uint8_t* src0 = a.pool + (int64_t)phys(2 * j) * a.page_bytes + 16 * lane;
+    const uint8_t* src1 = a.pool + (int64_t)phys(min(2 * j + 1, n - 1)) * a.page_bytes + 16 * lane;
+    const uint32_t dst = ring_base + (uint32_t)((j % NP) * kPair);
+    auto unit = [&](int u) __attribute__((always_inline)) {
+      constexpr int kHalf = kUnits / 2;
+      const uint8_t* src = u < kHalf ? src0 + 1024 * u : src1 + 1024 * (u - kHalf);
+      dma16_to_lds(src, dst + 1024 * u);
+    };
 #pragma unroll
-    for (int u = 0; u < kEven; ++u) dma16_to_lds(src + 1024 * (kEven * w + u), dst + 1024 * (kEven * w + u));
-    if (kExtra > 0 && w < kExtra) dma16_to_lds(src + 1024 * (4 * kEven + w), dst + 1024 * (4 * kEven + w));
+    for (int u = 0; u < kEven; ++u) unit(kEven * w + u);
+    if (kExtra > 0 && w < kExtra) unit(8 * kEven + w);
   };
   // at most k pairs' transfers of this wave left in flight
   auto wait_pairs_after = [&](int k) __attribute__((always_inline)) {
@@ -373,18 +325,15 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
 
-  // Q^T operand for the wave's part of the score dims (part `part` of the
-  // 4 / HB waves of its head block): head 16hb + l16, dims 32ks + 8g .. +7
-  // (16-byte chunk 4ks + g), once every wave's q transfers (older than its
-  // page transfers) are in
-  constexpr int kKs = 4 * HB;
-  const int part = HB == 2 ? (w >> 1) : w;
+  // Q^T operand for the wave's score part: head 16hb + l16, dims
+  // 32 ks + 8g .. +7 (16-byte chunk 4ks + g), ks = 4 sp + k, once every
+  // wave's q transfers (older than its page transfers) are in
   wait_pairs_after(min(NP - 1, n_pairs));
   lds_barrier();
-  bf16x8 qf[kKs];
+  bf16x8 qf[4];
 #pragma unroll
-  for (int k = 0; k < kKs; ++k) {
-    const int ks = part * kKs + k;
+  for (int k = 0; k < 4; ++k) {
+    const int ks = 4 * sp + k;
     qf[k] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + (((4 * ks + g) ^ (head & 7)) * 16));
   }
   f32x4* xs = reinterpret_cast<f32x4*>(smem + kXsOff);
@@ -393,56 +342,108 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const int v_lane_off = global_v_lane_off<COMPRESSED, FP8>(d_lo, g, l16);
+  // V^T read offsets: bf16, the tr16 lane offset inside page a (page b at
+  // + kBytes); e4m3, the tr8 row r = l16 / 2 of the lane's group names token
+  // 4g + r % 4 of page a (r < 4) or b, half l16 % 2 of the block's 16 dims
+  int vo;
+  if constexpr (FP8) {
+    const int r = l16 >> 1;
+    vo = (r < 4 ? 0 : PG::kBytes) + PG::kVOff + (((d_lo >> 4) * 16 + 4 * g + (r & 3)) * 16) + 8 * (l16 & 1);
+  } else {
+    vo = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
+  }
+  const uint32_t ring_lds = uniform_i32((int)lds_address(smem));
 
   for (int j = 0; j < n_pairs; ++j) {
     wait_pairs_after(min(NP - 2, n_pairs - 1 - j));
     lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
     if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
+    const uint32_t slot = ring_lds + (uint32_t)((j % NP) * kPair);
+    const lds_u8* pa = (const lds_u8*)(uintptr_t)slot;
     if (append_here && j == ((n - 1) >> 1)) {
-      if (wv == 0) put_global_record_as<COMPRESSED, FP8>(&ring[j % NP][(n - 1) & 1][0], rec, p & 15, lane);
+      if (w == 0) put_global_record_as<COMPRESSED, FP8>(smem + (j % NP) * kPair + ((n - 1) & 1) * PG::kBytes, rec,
+                                                        p & 15, lane);
       lds_barrier();
     }
-    // both groups pass the exchange barrier, also a group with no page in
-    // the split's last pair
-    const int i = 2 * j + grp;
-    const bool live = i < n;
-    const uint8_t* pg = ring[j % NP][grp];
-    if (live) xs[wv * 64 + lane] = global_page_scores<COMPRESSED, HB, FP8>(pg, qf, part * kKs, g, l16);
-    lds_barrier();
-    if (live) {
-      // the head block's partial scores, added in part order by every wave
-      const f32x4* xh = xs + (4 * grp + hb) * 64 + lane;
-      f32x4 sacc;
-      if constexpr (HB == 2) sacc = xh[0] + xh[2 * 64];
-      else sacc = (xh[0] + xh[64]) + (xh[2 * 64] + xh[3 * 64]);
-      global_page_update<COMPRESSED, HB, FP8>(acc, m_run, l_run, pg, sacc, (pg0 + i) * 16, p, g, l16, v_lane_off,
-                                              a.scale_log2);
+    // ---- scores: the wave's part, then the head block's four parts added
+    // in part order
+    f32x4 sc[2];
+    global_pair_scores<COMPRESSED, FP8>(sc, pa, qf, sp, g, l16);
+    if (HB == 2 || w < 4) {
+      xs[(w * 64 + lane) * 2 + 0] = sc[0];
+      xs[(w * 64 + lane) * 2 + 1] = sc[1];
     }
-  }
+    lds_barrier();
+    const int w0 = HB == 2 ? hb : 0, ws = HB == 2 ? 2 : 1;   // wave of part q: w0 + ws q
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 x0 = xs[((w0 + 0 * ws) * 64 + lane) * 2 + t], x1 = xs[((w0 + 1 * ws) * 64 + lane) * 2 + t];
+      const f32x4 x2 = xs[((w0 + 2 * ws) * 64 + lane) * 2 + t], x3 = xs[((w0 + 3 * ws) * 64 + lane) * 2 + t];
+      sc[t] = (x0 + x1) + (x2 + x3);
+    }
 
-  // ---- merge group 1 into group 0 through LDS (the ring is free now):
-  // M = max(m0, m1), acc = acc0 2^(m0 - M) + acc1 2^(m1 - M), same for l
-  lds_barrier();
-  float* xa = reinterpret_cast<float*>(&ring[0][0][0]) + (w * kBlocks * 64 + lane) * 4;
-  float* xm = reinterpret_cast<float*>(&ring[0][0][0]) + 4 * kBlocks * 64 * 4 + (w * 64 + lane) * 2;
-  if (grp == 1) {
+    // ---- online softmax for head l16 over the pair's 32 tokens; on the
+    // split's last pair, tokens past p and a missing second page are masked
+    const int tok_a = (pg0 + 2 * j) * 16 + 4 * g;   // the lane's first token of page a; page b: + 16
+    const bool last = j == n_pairs - 1;             // uniform
+    float z[2][4];
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(xa + b * 256) = acc[b];
-    xm[0] = m_run;
-    xm[1] = l_run;
-  }
-  lds_barrier();
-  if (grp == 1) return;
-  {
-    const float m1 = xm[0], l1 = xm[1];
-    const float M = fmaxf(m_run, m1);
-    const float s0 = __builtin_amdgcn_exp2f(m_run - M);
-    const float s1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) acc[b] = acc[b] * s0 + *reinterpret_cast<const f32x4*>(xa + b * 256) * s1;
-    l_run = l_run * s0 + l1 * s1;
-    m_run = M;
+      for (int r = 0; r < 4; ++r) z[t][r] = sc[t][r] * a.scale_log2;
+    uint32_t vm[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    if (last) {
+      const bool b_ok = 2 * j + 1 < n;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = tok_a + 16 * t + r <= p && (t == 0 || b_ok);
+          z[t][r] = ok ? z[t][r] : -INFINITY;
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          vm[2 * t + h] = (z[t][2 * h] != -INFINITY ? 0x0000ffffu : 0u) | (z[t][2 * h + 1] != -INFINITY ? 0xffff0000u : 0u);
+    }
+    const float mx = max_lanes_xor16_32(fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                                              fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3]))));
+    if (__any(mx > m_run + kLazyMaxG)) {
+      const bool up = mx > m_run + kLazyMaxG;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) acc[b] *= alpha;
+      l_run *= alpha;
+      m_run = up ? mx : m_run;
+    }
+    uint32_t pp[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pp[2 * t + h] = pack_bf16(__builtin_amdgcn_exp2f(z[t][2 * h] - m_run), __builtin_amdgcn_exp2f(z[t][2 * h + 1] - m_run));
+    l_run += ((bf16_lo(pp[0]) + bf16_hi(pp[0])) + (bf16_lo(pp[1]) + bf16_hi(pp[1]))) +
+             ((bf16_lo(pp[2]) + bf16_hi(pp[2])) + (bf16_lo(pp[3]) + bf16_hi(pp[3])));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pp[0], pp[1], pp[2], pp[3]});
+
+    // ---- O^T += V^T . P^T over the pair's 32 tokens, per 16-dim block
+    uint4 vf[kBlocks];
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) vf[b] = global_pair_vt<COMPRESSED, FP8>(pa, vo, b);
+    __builtin_amdgcn_sched_barrier(0);
+    if (last) {
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) {
+        vf[b].x &= vm[0];
+        vf[b].y &= vm[1];
+        vf[b].z &= vm[2];
+        vf[b].w &= vm[3];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b)
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[b]), pb, acc[b], 0, 0, 0);
   }
 
   // ---- write: lane holds head 16hb + l16, dims d_lo + 16b + 4g .. +3
