@@ -174,7 +174,7 @@ def cpu_baseline(step):
                       f"{nbytes} algorithmic KV bytes; os.cpu_count()={os.cpu_count()}"}
 
 
-def config_throughput(iters=30):
+def config_throughput(iters=30, oracle=True):
     """Decode-attention throughput of the three single-family workloads at
     their full sizes (the parity tests' cases; the page tables come from the
     same seeded recipes, the pools are filled on the device with torch's
@@ -233,10 +233,12 @@ def config_throughput(iters=30):
         q = torch.randn(8, 32, 512, device=dev, generator=g).to(torch.bfloat16)
         return RT.DeviceCase(pool, q, None, RT.i32_dev(lens), pt, stride, 8, 8, 1, 131072, 32, 512 ** -0.5, None)
 
-    def timed(dcs, nbytes, slots):
+    def timed(dcs, nbytes, slots, keep=None):
         ws = RT.Workspace()
         outs = [RT.attend(dc, ws=ws) for dc in dcs]
         torch.cuda.synchronize()
+        if keep is not None:
+            keep.append(outs[0].clone())
         ms = time_events(lambda: [RT.attend(dc, out=o, ws=ws) for dc, o in zip(dcs, outs)], iters) / len(dcs)
         return {"us": round(ms * 1e3, 2), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "pct_of_peak": round(nbytes / (ms * 1e-3) / PEAK_HBM * 100, 2),
@@ -250,12 +252,16 @@ def config_throughput(iters=30):
     del c2
     torch.cuda.empty_cache()
     for fp8 in (False, True):
+        kept = []
         for compressed in (True, False):
             dc = global_pool(compressed, fp8)
             res["global_" + ("compressed" if compressed else "full") + ("_e4m3" if fp8 else "")] = timed(
-                [dc], 8 * 131072 * (640 if compressed else 1024) * (1 if fp8 else 2), 8)
+                [dc], 8 * 131072 * (640 if compressed else 1024) * (1 if fp8 else 2), 8, kept)
             del dc
             torch.cuda.empty_cache()
+        # the two records of the same draws give bit-identical outputs
+        res["global_compressed" + ("_e4m3" if fp8 else "")]["compressed_equals_full"] = bool(torch.equal(kept[0], kept[1]))
+        del kept
     # prefix-cache page copies: 4096 local bf16 pages (512 MiB) from a cache
     # pool into a live pool, in a shuffled order; bytes counted once each way
     src = RT.Pool(gw.GW_FAMILY_LOCAL, gw.GW_KV_BF16, 4096, 8, 256, dev, fill_byte=1)
@@ -274,9 +280,83 @@ def config_throughput(iters=30):
     res["local_fp8"] = timed(c4, 64 * 1024 * 8 * 256 * 2, 64)
     del c4
     torch.cuda.empty_cache()
+    if oracle:
+        for k, o in config_oracle().items():
+            res[k]["cpu_baseline"] = o
     for k, v in res.items():
-        log(f"{k}: {v['us']} us/call, {v['GB_s']} GB/s ({v['pct_of_peak']}% of peak), {v['tok_s']} tok/s")
+        log(f"{k}: {v['us']} us/call, {v['GB_s']} GB/s ({v['pct_of_peak']}% of peak), {v['tok_s']} tok/s"
+            + (f"; oracle {v['cpu_baseline']['value']} GB/s" if "cpu_baseline" in v else ""))
     return res
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def config_oracle():
+    """The oracle as it stands on a bounded sample of each single-family
+    workload (same shapes, value distributions and rotation as the timed
+    calls; the sample's K/V come from the seeded recipes of the parity
+    tests): the local bf16 workload's first 4 slots, one 131072-token slot of
+    the global tied workload (compressed record, K rebuilt from V and the
+    rotated quarter), and 4 of the 64 local e4m3 slots.  Returns
+    {name: cpu_baseline}, GB/s of the same algorithmic bytes."""
+    import numpy as np
+    from oracle import attention as OA, codecs as OC, rope as OR
+    from paged_hybrid_kv_amd import synth as SY
+
+    def timed_oracle(case, seqs, per_seq_bytes, label):
+        # timed: the oracle's own rounding, rotation, e4m3 decode and attention
+        t0 = time.perf_counter()
+        nbytes = 0
+        for s in seqs:
+            L = int(case.seqs.lens[s])
+            sel = case.tok_seq == s
+            pos = case.tok_pos[sel]
+            q = OC.bf16_round(case.q[s:s + 1].astype(np.float64))
+            if hasattr(case, "window"):
+                k = OC.bf16_round(case.k[sel].astype(np.float64))
+                v = OC.bf16_round(case.v[sel].astype(np.float64))
+                k = OC.bf16_round(OR.rotate_local(k, pos[:, None]))
+                if case.fp8:
+                    k = OC.e4m3_decode(OC.e4m3_encode(k))
+                    v = OC.e4m3_decode(OC.e4m3_encode(v))
+                K = np.full((L,) + k.shape[1:], np.nan)
+                V = np.full((L,) + v.shape[1:], np.nan)
+                K[pos], V[pos] = k, v
+                OA.attend_sequence(q, K, V, case.scale, case.window)
+            else:
+                v = OC.bf16_round(case.v[sel].astype(np.float64))
+                k_rot = OC.bf16_round(OR.rotate_global(v, pos)[:, :128])
+                K = OA.k_from_compressed(v, k_rot)[:, None, :]
+                OA.attend_sequence(q, K, v[:, None, :], case.scale, None)
+            nbytes += per_seq_bytes(L)
+        dt = time.perf_counter() - t0
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+                "seconds": round(dt, 2), "sample": f"{label}; {nbytes} algorithmic KV bytes; "
+                                                   f"os.cpu_count()={os.cpu_count()}"}
+
+    out = {}
+    lens2 = np.random.default_rng(2).integers(1024, 8192, size=16, endpoint=True)[:4]
+    c2 = SY.local_case("oracle sample", 2, lens2, window=1024, num_q_heads=16, num_kv_heads=8, q_scale=0.5,
+                       kv_scale=0.5, rope=True, fill_window_only=True)
+    out["local_bf16"] = timed_oracle(c2, range(4), lambda L: min(L, 1024) * 8 * 256 * 2 * 2,
+                                     "4 of the 16 local bf16 slots (window 1024, 16 q / 8 KV heads), fp64 rotation "
+                                     "and naive masked softmax")
+    c3 = SY.global_case("oracle sample", 3, [131072], num_q_heads=32, rope=True)
+    out["global_compressed"] = timed_oracle(c3, range(1), lambda L: L * 1280,
+                                            "1 of the 8 global slots (131072 tokens, 32 q heads, K rebuilt from "
+                                            "V and the rotated quarter)")
+    c4 = SY.local_case("oracle sample", 4, [8192] * 4, window=1024, num_q_heads=16, num_kv_heads=8, q_scale=0.5,
+                       kv_scale=0.5, rope=True, fp8=True, fill_window_only=True)
+    out["local_fp8"] = timed_oracle(c4, range(4), lambda L: min(L, 1024) * 8 * 256 * 2,
+                                    "4 of the 64 local e4m3 slots (8192 tokens, window 1024), e4m3 decode of the "
+                                    "stored codes")
+    return out
 
 
 def main():
@@ -288,8 +368,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-rounds", type=int, default=10)
     ap.add_argument("--no-mixed", action="store_true", help="skip the step with prompt rows")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time the local bf16, global tied and local e4m3 workloads at full size")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the local bf16, global tied and local e4m3 workloads at full size")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -366,7 +446,7 @@ def main():
     if args.copy_calib:
         copy_calibration()
 
-    configs = config_throughput() if args.configs else None
+    configs = None if args.no_configs else config_throughput(oracle=not args.no_cpu_baseline)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(step)
     if cpu:
@@ -382,8 +462,10 @@ def main():
         "decode_tok_s": round(sh.decode_slots / (ms * 1e-3), 1),
         "decode_kv_bytes_per_step": dec_bytes,
         "config": {"workload": "gemma4 hybrid decode step: 60 layers (50 local hd256 16q/8kv window 1024 "
-                               "bf16 pool, 10 global hd512 32q/1kv tied compressed pool), 16 slots, "
-                               "contexts U[2048,8192] seed 5, 16-token pages",
+                               "bf16 pool, 10 global hd512 32q/1kv tied compressed pool), 16 decode slots, "
+                               "contexts U[2048,8192] seed 5, 16-token pages; decode rows only (0 prompt rows: "
+                               "the same step with 4 x 512 prompt rows is mixed_step)",
+                   "prompt_rows": 0,
                    "layers": sh.num_layers, "slots": sh.decode_slots,
                    "contexts": [int(x) for x in sh.decode_lens], "graph": not args.no_graph},
         "roofline": roof,
