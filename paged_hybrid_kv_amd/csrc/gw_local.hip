@@ -215,10 +215,19 @@ __device__ __forceinline__ void put_new_token(PageRegs<FP8>& r, uint8_t* b, cons
   }
 }
 
+// The group's q in LDS: head h's 16-byte chunk j (dims 8j .. 8j + 7, bf16
+// pairs) at chunk h * 32 + (j ^ ((j / 8) % 8)); the four quarters a lane
+// reads together (chunks 8c + k, c = 0..3) sit in distinct banks, and every
+// lane of a quad reads the same chunk.
+typedef __attribute__((address_space(3))) const u32x4 lds_q4;
+
 // One virtual page: b as in load_vpage, mask = its slots inside the row's
 // range (bit t for slot t; 0xffff for every page but the range's edges).
+// q: bf16 pages take it from registers (qr, the lane's quarter of each head),
+// e4m3 pages from LDS (qh: the K codes widen once for every head of the
+// group, and the registers q would take are left to the page buffers).
 template <int G, bool FP8>
-__device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&qr)[G][32],
+__device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&qr)[G][32], lds_q4* qh,
                                              uint32_t mask, int b, float scale_log2, int lane,
                                              float (&m_run)[G], float (&l_run)[G],
                                              float (&acc)[G][4]) {
@@ -237,31 +246,52 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
       }
     }
   }
-  // ---- scores: lane (t, c) dots its quarter of K_t with q, then quad sum
-  float z[G];
+  // ---- scores: lane (t, c) dots its quarter of K_t with q, then quad sum;
+  // per head the products go into two chains in the order k, m
+  float s0[G], s1[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float s0 = 0.f, s1 = 0.f;
-    if constexpr (!FP8) {
+  for (int h = 0; h < G; ++h) s0[h] = s1[h] = 0.f;
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        float& s = (k & 1) ? s1 : s0;
+        float& s = (k & 1) ? s1[h] : s0[h];
 #pragma unroll
         for (int m = 0; m < 4; ++m) s = dot2_bf16(u4_get(r.k[k], m), qr[h][4 * k + m], s);
       }
-    } else {
+    }
+  } else {
+    const int c = lane & 3;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float& s = (k & 1) ? s1 : s0;
+    for (int k = 0; k < 4; ++k) {
+      // the K codes widen to bf16 once, for every head of the group
+      uint32_t lo[4], hi[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t w = u4_get(r.k[k], m);
-          s = dot2_bf16(e4m3x2_to_bf16x2<false>(w), qr[h][8 * k + 2 * m], s);
-          s = dot2_bf16(e4m3x2_to_bf16x2<true>(w), qr[h][8 * k + 2 * m + 1], s);
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w = u4_get(r.k[k], m);
+        lo[m] = e4m3x2_to_bf16x2<false>(w);
+        hi[m] = e4m3x2_to_bf16x2<true>(w);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float& s = (k & 1) ? s1[h] : s0[h];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int j = 8 * c + 2 * k + half;
+          const u32x4 qv = qh[h * 32 + (j ^ ((j >> 3) & 7))];
+          s = dot2_bf16(lo[2 * half], qv[0], s);
+          s = dot2_bf16(hi[2 * half], qv[1], s);
+          s = dot2_bf16(lo[2 * half + 1], qv[2], s);
+          s = dot2_bf16(hi[2 * half + 1], qv[3], s);
         }
       }
     }
-    float s = s0 + s1;
+  }
+  float z[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float s = s0[h] + s1[h];
     s += dpp_f32<kQuadSwap1>(s);
     s += dpp_f32<kQuadSwap2>(s);
     z[h] = s;
@@ -511,11 +541,13 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   }
   __syncthreads();
 
-  // q of the group, this lane's quarter of the dims, as bf16 pairs
+  // q of the group, this lane's quarter of the dims, as bf16 pairs (bf16
+  // pages; e4m3 pages read it from LDS)
   const int c = lane & 3;
   uint32_t qr[G][32];
+  lds_q4* qh = (lds_q4*)&sm_q[0][0];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < (FP8 ? 0 : G); ++h) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int j = 8 * c + k;
@@ -599,14 +631,14 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   for (int i = 0; i < nw; i += 2) {
     if (i + 1 < nw) load_vpage<FP8>(B, dB.r0, dB.r1, dB.b, lane);
     const VPage dA2 = i + 2 < nw ? vpage(k_of(i + 2)) : dA;
-    process_page<G, FP8>(A, qr, dA.mask, dA.b, a.scale_log2, lane, m_run, l_run, acc);
+    process_page<G, FP8>(A, qr, qh, dA.mask, dA.b, a.scale_log2, lane, m_run, l_run, acc);
     if (i + 1 >= nw) break;
     if (i + 2 < nw) {
       dA = dA2;
       load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
     }
     const VPage dB2 = i + 3 < nw ? vpage(k_of(i + 3)) : dB;
-    process_page<G, FP8>(B, qr, dB.mask, dB.b, a.scale_log2, lane, m_run, l_run, acc);
+    process_page<G, FP8>(B, qr, qh, dB.mask, dB.b, a.scale_log2, lane, m_run, l_run, acc);
     dB = dB2;
   }
 
