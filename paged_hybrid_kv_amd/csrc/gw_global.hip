@@ -25,21 +25,28 @@
 //
 // Work split: one workgroup per (sequence, split) item, numbered compactly
 // (workgroup b takes item b); a split is a balanced run of the row's pages
-// (gw_plan.h).  The split's pages go by in pairs, and all eight waves work on
-// every pair: wave w takes head block hb (16 heads: w % 2 with 32 q heads,
-// the only block with 16), 128 of the score contraction's 512 dims (part w / 2,
-// or w % 4 with 16 heads) and a slice of the output dims (128 dims with 32
-// heads, 64 with 16).  The waves of a head block add their partial scores
-// through LDS in a fixed part order, so every wave of the block holds the same
-// full scores and the same online-softmax state.  The running max moves only
-// when a score passes it by more than 2^8 (so the accumulators are rarely
-// rescaled; the unnormalised weights stay below 2^8).  Pages stream straight
-// from HBM into a ring of LDS pair slots (global_load_lds_dwordx4, every wave
-// moving its share of every pair), NP - 1 pairs in flight while one is read.
-// On the split's last pair, tokens past the row's position (and the missing
-// second page of an odd split) get masked scores and zeroed V operands, so
-// unwritten slots (possibly NaN) never reach the output.  P is rounded to
-// bf16 for PV and the sum l adds exactly those rounded values.
+// (gw_plan.h), streamed in pairs straight from HBM into an LDS ring
+// (global_load_lds_dwordx4, every wave moving its share of every pair).
+// The score and value steps of a pair are split between waves and
+// pipelined a pair apart (global_decode_ws_kernel: four score waves, each
+// taking one page and half the score contraction's dims for every head, so
+// each K fragment is read from LDS once, and four value waves, each taking
+// 128 output dims of every head, so each V fragment is read once); the full
+// bf16 record, whose 64 KiB pairs leave room for a ring of two only, runs
+// both steps on all eight waves in turn (global_decode_full_kernel).  The
+// partial scores of a page are added through LDS in a fixed order, scaled
+// into the base-2 domain by the wave that computed them, and every wave that
+// runs the softmax of a head holds the same scores and the same state, so
+// all records take the same arithmetic and give bit-identical results.
+// The running max moves only when a score passes it by more than 2^8 (the
+// accumulators are rarely rescaled; the unnormalised weights stay below
+// 2^8).  On the split's last pair, tokens past the row's position (and the
+// missing second page of an odd split) get masked scores and zeroed V
+// operands, so unwritten slots (possibly NaN) never reach the output.  P is
+// rounded to bf16 for PV and the sum l adds exactly those rounded values
+// (v_dot2_f32_bf16 against ones).  A row with several splits leaves each
+// split's (acc, m, l) in the workspace, in MFMA fragment order, for
+// global_split_reduce_kernel.
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -50,24 +57,27 @@ namespace {
 
 constexpr int kGD = 512;
 
-// LDS ring depth in page pairs: bf16 compressed / full record (3 x 40 KiB,
-// 2 x 64 KiB), e4m3 compressed / full (5 x 20 KiB, 3 x 32 KiB, q in a 32
-// KiB region of its own); with the 16 KiB score exchange, one workgroup per CU.
-#ifndef GW_GLOBAL_NP_C
-#define GW_GLOBAL_NP_C 3
+// LDS ring depth: page slots of the wave-specialised kernel for the bf16
+// compressed record (7 x 20 KiB), e4m3 compressed (14 x 10 KiB) and e4m3
+// full (8 x 16 KiB), and pair slots of the full bf16 record's kernel
+// (2 x 64 KiB); with the score exchange, one workgroup per CU.
+#ifndef GW_GLOBAL_NS_C
+#define GW_GLOBAL_NS_C 7
 #endif
 #ifndef GW_GLOBAL_NP_F
 #define GW_GLOBAL_NP_F 2
 #endif
-#ifndef GW_GLOBAL_NP_C8
-#define GW_GLOBAL_NP_C8 5
+#ifndef GW_GLOBAL_NS_C8
+#define GW_GLOBAL_NS_C8 14
 #endif
-#ifndef GW_GLOBAL_NP_F8
-#define GW_GLOBAL_NP_F8 3
+#ifndef GW_GLOBAL_NS_F8
+#define GW_GLOBAL_NS_F8 8
 #endif
 
 // The reference max moves only when a score (base 2) passes it by more than this.
 constexpr float kLazyMaxG = 8.f;
+// bf16 1.0 in both halves: dot2_bf16(p, kBf16Ones, l) adds a pair of weights to l.
+constexpr uint32_t kBf16Ones = 0x3f803f80u;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -106,183 +116,500 @@ __device__ __forceinline__ bf16x8 widen_e4m3x8(uint32_t w0, uint32_t w1) {
                                           e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
 }
 
-// A pair of pages in LDS (page a at pa, page b at pa + kBytes), for one wave:
-//
-// global_pair_scores: the wave's share of S^T = K . Q^T for both pages, over
-// the four 32-dim steps 4 sp .. 4 sp + 3 of its score part (the waves of a
-// head block add their shares through LDS); lane holds head l16, tokens
-// 4g .. 4g+3 of each page.  All eight K fragments are read before the
-// products.  e4m3 fragments (8 bytes) widen exactly to bf16 just before
-// their product.
+// The V^T operand of output block b (16 dims) for a pair of pages in LDS
+// (page a at pa, page b at pb; an e4m3 pair must have pb = pa + kBytes, as
+// one transposing read spans both pages): lane (g, l16) gets dim (its
+// block's first dim + l16) of tokens 4g .. 4g+3 of page a, then of page b,
+// as 8 bf16.  vo: the lane's byte offset for block 0 (bf16:
+// global_v_lane_off in a page; e4m3: the tr8 row it names, in page a or b).
 template <bool COMPRESSED, bool FP8>
-__device__ __forceinline__ void global_pair_scores(f32x4 (&s)[2], const lds_u8* pa, const bf16x8 (&qf)[4], int sp,
-                                                   int g, int l16) {
-  using PG = GlobalPage<COMPRESSED, FP8>;
-  if constexpr (FP8) {
-    i32x2 kr[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        kr[t][k] = *reinterpret_cast<const lds_i32x2*>(pa + t * PG::kBytes + PG::k_off(4 * (4 * sp + k) + g, l16));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_e4m3x8((uint32_t)kr[t][k][0], (uint32_t)kr[t][k][1]),
-                                                       qf[k], s[t], 0, 0, 0);
-    }
-  } else {
-    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        kf[t][k] = *reinterpret_cast<const lds_bf16x8*>(pa + t * PG::kBytes + PG::k_off(4 * (4 * sp + k) + g, l16));
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][k], qf[k], s[t], 0, 0, 0);
-    }
-  }
-}
-
-// The V^T operand of output block b (16 dims) for the pair: lane (g, l16)
-// gets dim (its block's first dim + l16) of tokens 4g .. 4g+3 of page a,
-// then of page b, as 8 bf16.  vo: the lane's byte offset for block 0 (bf16:
-// global_v_lane_off in page a; e4m3: the tr8 row it names, in page a or b).
-template <bool COMPRESSED, bool FP8>
-__device__ __forceinline__ uint4 global_pair_vt(const lds_u8* pa, int vo, int b) {
+__device__ __forceinline__ uint4 global_pair_vt(const lds_u8* pa, const lds_u8* pb, int vo, int b) {
   if constexpr (FP8) {
     const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(pa + vo + 256 * b));
     return __builtin_bit_cast(uint4, widen_e4m3x8((uint32_t)r[0], (uint32_t)r[1]));
   } else {
-    constexpr int kB = GlobalPage<COMPRESSED>::kBytes;
     const uint2 va = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + vo + 512 * b)));
-    const uint2 vb =
-        __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa + kB + vo + 512 * b)));
+    const uint2 vb = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pb + vo + 512 * b)));
     return uint4{va.x, va.y, vb.x, vb.y};
   }
 }
 
-// One workgroup = eight waves on one (sequence, split) item; see the header
-// for the work split.  NP: page pairs in the LDS ring (NP - 1 pairs in
-// flight while one is read).  FP8: e4m3 pages, widened to bf16 as they are
-// read from LDS; q then has an LDS region of its own after the ring.
-template <bool COMPRESSED, int HB, int NP, bool FP8 = false>
-__global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a) {
+// s_waitcnt vmcnt(n) for a run-time n in 0 .. 31 (larger n waits for 31).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+#define GW_VMCNT_CASE(N) \
+  case N: wait_vmcnt<N>(); break;
+    GW_VMCNT_CASE(0) GW_VMCNT_CASE(1) GW_VMCNT_CASE(2) GW_VMCNT_CASE(3) GW_VMCNT_CASE(4) GW_VMCNT_CASE(5)
+    GW_VMCNT_CASE(6) GW_VMCNT_CASE(7) GW_VMCNT_CASE(8) GW_VMCNT_CASE(9) GW_VMCNT_CASE(10) GW_VMCNT_CASE(11)
+    GW_VMCNT_CASE(12) GW_VMCNT_CASE(13) GW_VMCNT_CASE(14) GW_VMCNT_CASE(15) GW_VMCNT_CASE(16) GW_VMCNT_CASE(17)
+    GW_VMCNT_CASE(18) GW_VMCNT_CASE(19) GW_VMCNT_CASE(20) GW_VMCNT_CASE(21) GW_VMCNT_CASE(22) GW_VMCNT_CASE(23)
+    GW_VMCNT_CASE(24) GW_VMCNT_CASE(25) GW_VMCNT_CASE(26) GW_VMCNT_CASE(27) GW_VMCNT_CASE(28) GW_VMCNT_CASE(29)
+    GW_VMCNT_CASE(30)
+#undef GW_VMCNT_CASE
+    default: wait_vmcnt<31>(); break;
+  }
+}
+
+// The (sequence, split) item of workgroup b: the call's items are numbered
+// sequence by sequence (a decode row's splits in order), and workgroup b
+// takes item b, so the active workgroups are 0 .. items-1 and spread evenly
+// over the XCDs.  False past the last item.  Every value is wave-uniform.
+struct GlobalItem {
+  int s, split, nsplit, row, p;
+};
+__device__ __forceinline__ bool global_item(const GlobalAttnArgs& a, int b, int lane, GlobalItem& it) {
+  int base = 0;
+  for (int c = 0; c < a.num_seqs; c += 64) {
+    const int sl = c + lane;
+    int cnt = 0, len = 1, r0 = sl;
+    if (sl < a.num_seqs) {
+      len = a.seq_lens[sl];
+      if (a.q_indptr) r0 = a.q_indptr[sl];
+      if (!a.q_indptr || a.q_indptr[sl + 1] - r0 == 1) cnt = global_nsplit(((len - 1) >> 4) + 1);
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d, 64);
+      incl += lane >= d ? up : 0;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (b < base + total) {
+      const uint64_t hit = __ballot(base + incl > b);
+      const int ls = __builtin_ctzll(hit);
+      it.s = uniform_i32(c + ls);
+      it.nsplit = uniform_i32(__builtin_amdgcn_readlane(cnt, ls));
+      it.p = uniform_i32(__builtin_amdgcn_readlane(len, ls)) - 1;
+      it.row = uniform_i32(__builtin_amdgcn_readlane(r0, ls));
+      it.split = uniform_i32(b - (base + __builtin_amdgcn_readlane(incl, ls) - it.nsplit));
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// A split's physical page ids (at most 256), 64 per register, read back
+// with readlane so that the page loop issues no vector memory operation the
+// compiler would wait on.
+struct SplitPages {
+  int v0, v1, v2, v3;
+  __device__ __forceinline__ void load(const int32_t* pt, int n, int lane) {
+    v0 = lane < n ? pt[lane] : 0;
+    v1 = n > 64 && 64 + lane < n ? pt[64 + lane] : 0;
+    v2 = n > 128 && 128 + lane < n ? pt[128 + lane] : 0;
+    v3 = n > 192 && 192 + lane < n ? pt[192 + lane] : 0;
+  }
+  __device__ __forceinline__ int operator()(int i) const {
+    const int l = i & 63;
+    return i < 64 ? __builtin_amdgcn_readlane(v0, l)
+         : i < 128 ? __builtin_amdgcn_readlane(v1, l)
+         : i < 192 ? __builtin_amdgcn_readlane(v2, l)
+                   : __builtin_amdgcn_readlane(v3, l);
+  }
+};
+
+
+// ---------------------------------------------------------------------------
+// Wave-specialised decode, for rings of three pairs or more (the compressed
+// record and both e4m3 records): the score and the value steps of the pages
+// run on separate waves and overlap, a pair apart.
+//
+//   score waves 0..3: wave w takes page w % 2 of the pair and dims
+//     256 (w / 2) .. +255 of the score contraction, for every q head (its Q^T
+//     operands stay in registers), so each K fragment is read from LDS once
+//     and feeds the products of all head blocks; it leaves its partial
+//     S^T blocks in an exchange buffer.
+//   value waves 4..7: wave 4 + v adds the two partial sums of each score (in
+//     a fixed order), runs the online softmax of every head (each value wave
+//     holds the same full scores and keeps the same softmax state) and
+//     accumulates O^T for dims 128 v .. +127 of every head, so each V
+//     fragment is read once and feeds all head blocks.
+//
+// Step i of the loop: the score waves take pair i, the value waves pair
+// i - 1 (exchange buffers alternate between steps), one barrier between
+// steps.  The LDS ring holds NS pages (not pairs, so an odd count uses the
+// space a pair ring would leave): the pages that slots freed by pair i - 2
+// take are issued at step i, so NS - 4 pages are in flight while pairs i
+// and i - 1 are read; q waits in the ring's last slots until the score
+// waves have read it.
+template <bool COMPRESSED, bool FP8, int HB>
+__device__ __forceinline__ void global_tile_scores(f32x4 (&s)[HB], const lds_u8* pg, const bf16x8 (&qf)[HB][8],
+                                                   int dh, int g, int l16) {
   using PG = GlobalPage<COMPRESSED, FP8>;
-  constexpr int kPair = 2 * PG::kBytes;
-  constexpr int kUnits = kPair / 1024;        // 1 KiB transfer units per pair
-  constexpr int kEven = kUnits / 8;           // units every wave moves ...
-  constexpr int kExtra = kUnits % 8;          // ... and one more for waves below kExtra
-  constexpr int kPerWave = kEven + (kExtra > 0 ? 1 : 0);
-  constexpr int kBlocks = HB == 2 ? 8 : 4;    // 16-dim output blocks per wave
-  constexpr int kRingBytes = NP * kPair;
-  constexpr int kXsOff = kRingBytes;          // score exchange: [wave][lane][page] f32x4
-  constexpr int kQOff = kXsOff + 8 * 64 * 32; // e4m3: q
-  static_assert(NP >= 2 && kPerWave * (NP - 2) < 64 && NP - 2 <= 4, "ring depth");
-  static_assert(FP8 || kPair >= 32 * 1024, "a ring slot holds q");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kQOff + (FP8 ? 32 * 1024 : 0)];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) s[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (FP8) {
+    i32x2 kr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kr[k] = *reinterpret_cast<const lds_i32x2*>(pg + PG::k_off(4 * (8 * dh + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bf16x8 kf = widen_e4m3x8((uint32_t)kr[k][0], (uint32_t)kr[k][1]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hb][k], s[hb], 0, 0, 0);
+    }
+  } else {
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    bf16x8 kf[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kf[k] = *reinterpret_cast<const lds_bf16x8*>(pg + PG::k_off(4 * (8 * dh + k) + g, l16));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[hb][k], s[hb], 0, 0, 0);
+  }
+}
+
+template <bool COMPRESSED, int HB, int NS, bool FP8>
+__global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs a) {
+  using PG = GlobalPage<COMPRESSED, FP8>;
+  constexpr int kU = PG::kBytes / 1024;       // 1 KiB transfer units per page
+  constexpr int kQPages = (HB * 16 * 1024 + PG::kBytes - 1) / PG::kBytes;   // page slots q holds at first
+  constexpr int kXsBytes = HB * 4 * 1024;     // one pair's partial scores: [page][dim half][hb][lane] f32x4
+  constexpr int kXsOff = NS * PG::kBytes;
+  // pages issued before the loop: every slot q does not hold, at most 10
+  // (so that no wait below counts more than 31 transfers)
+  constexpr int kPro = NS - kQPages < 10 ? NS - kQPages : 10;
+  static_assert(NS >= 6 && kPro >= 2 && (NS - 4) * ((kU + 7) / 8) <= 31 && kPro * ((kU + 7) / 8) <= 31, "ring depth");
+  static_assert(!FP8 || NS % 2 == 0, "an e4m3 pair's pages sit side by side");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + 2 * kXsBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
-  const int hb = HB == 2 ? (w & 1) : 0;
-  const int sp = HB == 2 ? (w >> 1) : (w & 3);          // score part: dims 128 sp ..
-  const int d_lo = HB == 2 ? 128 * (w >> 1) : 64 * w;   // output dims d_lo .. + 16 kBlocks
+  const bool scorer = w < 4;
   const int g = lane >> 4, l16 = lane & 15;
 
-  // ---- work item of this workgroup: the call's (sequence, split) items are
-  // numbered sequence by sequence, and workgroup b takes item b, so the
-  // active workgroups are 0 .. items-1 and spread evenly over the XCDs
-  int s = -1, split = 0, nsplit = 1, L = 1, row = 0;
+  GlobalItem it;
+  if (!global_item(a, blockIdx.x, lane, it)) return;
+  const int s = it.s, split = it.split, nsplit = it.nsplit, row = it.row, p = it.p;
+  const int n_pages = (p >> 4) + 1;
+  const int pg0 = split_lo(n_pages, nsplit, split);
+  const int n = split_lo(n_pages, nsplit, split + 1) - pg0;
+  const int n_pairs = (n + 1) >> 1;
+
+  // ---- the split's page ids, waited for here: the compiler does not see
+  // the direct-to-LDS transfers below, and a wait of its own placed after
+  // them would hold for them too
+  SplitPages phys;
+  phys.load(a.page_table + (int64_t)s * a.pt_stride + pg0, n, lane);
+  asm volatile("" ::"v"(phys.v0), "v"(phys.v1), "v"(phys.v2), "v"(phys.v3));
+  // the decode row's own token, when the call carries it: on the workgroup
+  // of the row's last split, value wave 7 (idle while the score waves take
+  // pair 0) rotates it, stores it into the pool (as gw_kv_append does) and,
+  // before that page's scores, into the page's LDS copy
+  const bool append_here = a.v_new != nullptr && split == nsplit - 1;
+  constexpr int kAppendWave = 7;
+  GlobalRecordLane rec{};
+
+  // ---- q into the ring's last kQPages slots (1 KiB per head, chunk c of
+  // head h at chunk c ^ (h % 8), so the operand reads hit distinct banks),
+  // ahead of the pages; wave w moves heads 2 HB w .. +2 HB - 1
+  uint8_t* qs = smem + (NS - kQPages) * PG::kBytes;
   {
-    const int b = blockIdx.x;
-    int base = 0;
-    for (int c = 0; c < a.num_seqs; c += 64) {
-      const int sl = c + lane;
-      int cnt = 0, len = 1, r0 = sl;
-      if (sl < a.num_seqs) {
-        len = a.seq_lens[sl];
-        if (a.q_indptr) r0 = a.q_indptr[sl];
-        if (!a.q_indptr || a.q_indptr[sl + 1] - r0 == 1) cnt = global_nsplit(((len - 1) >> 4) + 1);
-      }
-      int incl = cnt;
+    const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int up = __shfl_up(incl, d, 64);
-        incl += lane >= d ? up : 0;
-      }
-      const int total = __builtin_amdgcn_readlane(incl, 63);
-      if (b < base + total) {
-        const uint64_t hit = __ballot(base + incl > b);
-        const int ls = __builtin_ctzll(hit);
-        s = c + ls;
-        nsplit = __builtin_amdgcn_readlane(cnt, ls);
-        L = __builtin_amdgcn_readlane(len, ls);
-        row = __builtin_amdgcn_readlane(r0, ls);
-        split = b - (base + __builtin_amdgcn_readlane(incl, ls) - nsplit);
-        break;
-      }
-      base += total;
+    for (int i = 0; i < 2 * HB; ++i) {
+      const int h = 2 * HB * w + i;
+      dma16_to_lds(a.q + ((int64_t)row * a.num_q_heads + h) * kGD + 8 * (lane ^ (h & 7)),
+                   qs_lds + (uint32_t)(h * 1024));
     }
   }
-  if (s < 0) return;
-  s = uniform_i32(s);
-  split = uniform_i32(split);
-  nsplit = uniform_i32(nsplit);
-  L = uniform_i32(L);
-  row = uniform_i32(row);
-  const int p = L - 1;
+
+  // ---- transfers: page q of the split (pages 2j, 2j + 1 make pair j; an
+  // odd split's last pair repeats its last page as the second, whose scores
+  // are masked and V zeroed) lands in page slot q % NS, in the pool's
+  // layout; its 1 KiB unit u is moved by wave (kU q + u) % 8, so each wave
+  // moves its share of every pair.  The waits count transfers only: q's
+  // transfers are older than all of them, and the appending wave's loads and
+  // pool stores come after the first pages' transfers (the compiler waits for
+  // those loads, and with them for everything older) and before every later
+  // transfer, so a later wait covers the stores too.
+  const uint32_t ring_lds = uniform_i32((int)lds_address(smem));
+  const int n_pg = 2 * n_pairs;
+  auto first_unit = [&](int q) __attribute__((always_inline)) { return (w - kU * q) & 7; };
+  auto units_of = [&](int q) __attribute__((always_inline)) {
+    const int u0 = first_unit(q);
+    return u0 < kU ? (kU - 1 - u0) / 8 + 1 : 0;
+  };
+  auto issue_page = [&](int q) __attribute__((always_inline)) {
+    const uint8_t* src = a.pool + (int64_t)phys(min(q, n - 1)) * a.page_bytes + 16 * lane;
+    const uint32_t dst = ring_lds + (uint32_t)((q % NS) * PG::kBytes);
+    const int u0 = first_unit(q);
+#pragma unroll
+    for (int k = 0; k < (kU + 7) / 8; ++k) {
+      const int u = u0 + 8 * k;
+      if (u < kU) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
+    }
+  };
+  // pages 0 .. last landed: this wave's transfers of the later pages issued
+  // so far may stay in flight
+  int issued = min(kPro, n_pg);   // pages issued so far (uniform)
+  auto wait_through = [&](int last) __attribute__((always_inline)) {
+    int after = 0;
+    for (int q = last + 1; q < issued; ++q) after += units_of(q);
+    wait_vmcnt_upto(after);
+  };
+  for (int q = 0; q < issued; ++q) issue_page(q);
+  auto page_lds = [&](int q) __attribute__((always_inline)) {
+    return (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((q % NS) * PG::kBytes));
+  };
+
+  // ---- the loop's synchronisation, the same on both roles: step i > 0
+  // opens with pair i in LDS (this wave's transfers, then the barrier), pair
+  // i - 1's partial scores in, pair i - 2 done, and issues the pages whose
+  // slots that freed; the appending workgroup patches the split's last page
+  // before its scores
+  f32x4* xs = reinterpret_cast<f32x4*>(smem + kXsOff);
+  auto step_open = [&](int i) __attribute__((always_inline)) {
+    if (i > 0) {
+      if (i < n_pairs) wait_through(2 * i + 1);
+      lds_barrier();
+      const int lim = min(2 * i - 3 + NS, n_pg - 1);
+      while (issued <= lim) issue_page(issued++);
+    }
+    if (append_here && i == n_pairs - 1) {
+      if (w == kAppendWave)
+        put_global_record_as<COMPRESSED, FP8>(smem + ((n - 1) % NS) * PG::kBytes, rec, p & 15, lane);
+      lds_barrier();
+    }
+  };
+  // pair 0 and q in LDS for every wave
+  wait_through(1);
+  lds_barrier();
+
+  if (scorer) {
+    // ---- score waves: Q^T operands (head 16 hb + l16, dims 256 dh + 32 k +
+    // 8g .. +7) from LDS once, then per step the page's partial S^T blocks
+    const int t_sc = w & 1, dh = w >> 1;
+    bf16x8 qf[HB][8];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int h = 16 * hb + l16, c = 4 * (8 * dh + k) + g;
+        qf[hb][k] = *reinterpret_cast<const bf16x8*>(qs + h * 1024 + ((c ^ (h & 7)) * 16));
+      }
+    for (int i = 0; i <= n_pairs; ++i) {
+      step_open(i);
+      if (i < n_pairs) {
+        f32x4 sc[HB];
+        global_tile_scores<COMPRESSED, FP8, HB>(
+            sc, page_lds(2 * i + t_sc), qf, dh, g, l16);
+        f32x4* xb = xs + (i & 1) * (kXsBytes / 16);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) xb[((2 * t_sc + dh) * HB + hb) * 64 + lane] = sc[hb] * a.scale_log2;
+      }
+    }
+    return;
+  }
+
+  // ---- value waves: output dims v_lo .. +127 of every head
+  if (append_here && w == kAppendWave) {
+    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+    put_global_record_as<COMPRESSED, FP8>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
+                                          p & 15, lane);
+  }
+  const int v_lo = 128 * (w - 4);
+  f32x4 acc[HB][8];
+  float m_run[HB], l_run[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    m_run[hb] = -INFINITY;
+    l_run[hb] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[hb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // V^T read offset of block 0 (bf16: the tr16 lane offset inside page a,
+  // page b at + kBytes; e4m3: the tr8 row r = l16 / 2 names token 4g + r % 4
+  // of page a (r < 4) or b, half l16 % 2 of the block's 16 dims)
+  int vo;
+  if constexpr (FP8) {
+    const int r = l16 >> 1;
+    vo = (r < 4 ? 0 : PG::kBytes) + PG::kVOff + (((v_lo >> 4) * 16 + 4 * g + (r & 3)) * 16) + 8 * (l16 & 1);
+  } else {
+    vo = global_v_lane_off<COMPRESSED>(v_lo, g, l16);
+  }
+  for (int i = 0; i <= n_pairs; ++i) {
+    step_open(i);
+    if (i == 0) continue;
+    {
+      const int j = i - 1;
+      const lds_u8* pa = page_lds(2 * j);
+      const lds_u8* pbp = page_lds(2 * j + 1);
+      uint4 vf[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) vf[b] = global_pair_vt<COMPRESSED, FP8>(pa, pbp, vo, b);
+      const f32x4* xb = xs + (j & 1) * (kXsBytes / 16);
+      // lane: head 16 hb + l16, tokens 4g .. 4g+3 of page a (t = 0) and b
+      float z[HB][2][4];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 sc = xb[((2 * t + 0) * HB + hb) * 64 + lane] + xb[((2 * t + 1) * HB + hb) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[hb][t][r] = sc[r];
+        }
+      // the split's last pair: tokens past p and a missing second page masked
+      const bool last = j == n_pairs - 1;   // uniform
+      uint32_t vm[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+      if (last) {
+        const int tok_a = (pg0 + 2 * j) * 16 + 4 * g;
+        const bool b_ok = 2 * j + 1 < n;
+        bool ok[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ok[t][r] = tok_a + 16 * t + r <= p && (t == 0 || b_ok);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[hb][t][r] = ok[t][r] ? z[hb][t][r] : -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            vm[2 * t + h] = (ok[t][2 * h] ? 0x0000ffffu : 0u) | (ok[t][2 * h + 1] ? 0xffff0000u : 0u);
+      }
+      float mx[HB];
+      bool grow = false;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        mx[hb] = max_lanes_xor16_32(fmaxf(fmaxf(fmaxf(z[hb][0][0], z[hb][0][1]), fmaxf(z[hb][0][2], z[hb][0][3])),
+                                          fmaxf(fmaxf(z[hb][1][0], z[hb][1][1]), fmaxf(z[hb][1][2], z[hb][1][3]))));
+        grow = grow || mx[hb] > m_run[hb] + kLazyMaxG;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const bool up = mx[hb] > m_run[hb] + kLazyMaxG;
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_run[hb] - mx[hb]) : 1.f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) acc[hb][b] *= alpha;
+          l_run[hb] *= alpha;
+          m_run[hb] = up ? mx[hb] : m_run[hb];
+        }
+      }
+      bf16x8 pb[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        uint32_t pp[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            pp[2 * t + h] = pack_bf16(__builtin_amdgcn_exp2f(z[hb][t][2 * h] - m_run[hb]),
+                                      __builtin_amdgcn_exp2f(z[hb][t][2 * h + 1] - m_run[hb]));
+        l_run[hb] = dot2_bf16(pp[3], kBf16Ones, dot2_bf16(pp[2], kBf16Ones,
+                              dot2_bf16(pp[1], kBf16Ones, dot2_bf16(pp[0], kBf16Ones, l_run[hb]))));
+        pb[hb] = __builtin_bit_cast(bf16x8, uint4{pp[0], pp[1], pp[2], pp[3]});
+      }
+      if (last) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          vf[b].x &= vm[0];
+          vf[b].y &= vm[1];
+          vf[b].z &= vm[2];
+          vf[b].w &= vm[3];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          acc[hb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[b]), pb[hb], acc[hb][b], 0,
+                                                               0, 0);
+    }
+  }
+
+  // ---- write: lane holds head 16 hb + l16, dims v_lo + 16b + 4g .. +3
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 16 * hb + l16;
+    const float l_tot = sum_lanes_xor16_32(l_run[hb]);
+    if (nsplit == 1) {
+      float* op = a.out + ((int64_t)row * a.num_q_heads + head) * kGD + v_lo + 4 * g;
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[hb][b] * inv;
+    } else {
+      const int64_t item = (int64_t)s * a.max_splits + split;
+      f32x4* op = reinterpret_cast<f32x4*>(a.part_acc) + ((item * HB + hb) * 32 + (v_lo >> 4)) * 64 + lane;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) op[64 * b] = acc[hb][b];
+      if (v_lo == 0 && g == 0) {
+        a.part_ml[(item * a.num_q_heads + head) * 2 + 0] = m_run[hb];
+        a.part_ml[(item * a.num_q_heads + head) * 2 + 1] = l_tot;
+      }
+    }
+  }
+}
+
+// The full bf16 record (64 KiB pairs, a ring of two): all eight waves on
+// every pair, scores first, then softmax and PV.  The arithmetic is that of
+// global_decode_ws_kernel step for step, so both records give bit-identical
+// results: wave w computes the S^T block of page (w / 2) % 2, dim half w / 4
+// and head block w % 2 (with 16 heads: page w % 2, half w / 2, waves 0..3),
+// the partial sums are added in the same order, and wave w then takes head
+// block w % 2 and output dims 128 (w / 2) .. +127 (16 heads: dims 64 w ..
+// +63) of the softmax and PV steps.
+template <int HB, int NP>
+__global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnArgs a) {
+  using PG = GlobalPage<false>;
+  constexpr int kPair = 2 * PG::kBytes;
+  constexpr int kUnits = kPair / 1024;        // 1 KiB transfer units per pair (8 per wave)
+  constexpr int kPerWave = kUnits / 8;
+  constexpr int kBlocks = HB == 2 ? 8 : 4;    // 16-dim output blocks per wave
+  constexpr int kXsOff = NP * kPair;          // partial scores: [page][dim half][hb][lane] f32x4
+  static_assert(kUnits % 8 == 0 && NP >= 2 && kPerWave * (NP - 2) < 64 && NP - 2 <= 4, "ring depth");
+  static_assert(kPair >= HB * 16 * 1024, "a ring slot holds q");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + HB * 4 * 1024];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform_i32(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const bool scorer = HB == 2 || w < 4;
+  const int t_sc = HB == 2 ? (w >> 1) & 1 : w & 1;     // score block: page,
+  const int dh = HB == 2 ? w >> 2 : (w >> 1) & 1;      // dim half,
+  const int hb = HB == 2 ? w & 1 : 0;                   // head block (also of the PV step)
+  const int d_lo = HB == 2 ? 128 * (w >> 1) : 64 * w;   // output dims d_lo .. + 16 kBlocks
+
+  GlobalItem it;
+  if (!global_item(a, blockIdx.x, lane, it)) return;
+  const int s = it.s, split = it.split, nsplit = it.nsplit, row = it.row, p = it.p;
   const int n_pages = (p >> 4) + 1;
   const int pg0 = split_lo(n_pages, nsplit, split);
   const int n = split_lo(n_pages, nsplit, split + 1) - pg0;
   const int n_pairs = (n + 1) >> 1;
   const int head = 16 * hb + l16;
 
-  // ---- the split's physical page ids (one per lane and register, read
-  // back with readlane; a split has at most 256 pages) and, on the wave that
-  // appends a decode row's own token, that token's inputs go out first, in
-  // one round trip, and are waited for before anything else is issued: the
-  // compiler does not see the direct-to-LDS transfers below, and a wait of
-  // its own placed after them would hold for them too.
-  const int32_t* pt = a.page_table + (int64_t)s * a.pt_stride + pg0;
-  auto pt_at = [&](int idx) __attribute__((always_inline)) { return idx < n ? pt[idx] : 0; };
-  const int ptv0 = pt_at(lane);
-  const int ptv1 = n > 64 ? pt_at(64 + lane) : 0;
-  const int ptv2 = n > 128 ? pt_at(128 + lane) : 0;
-  const int ptv3 = n > 192 ? pt_at(192 + lane) : 0;
-  auto phys = [&](int i) __attribute__((always_inline)) {
-    const int l = i & 63;
-    return i < 64 ? __builtin_amdgcn_readlane(ptv0, l)
-         : i < 128 ? __builtin_amdgcn_readlane(ptv1, l)
-         : i < 192 ? __builtin_amdgcn_readlane(ptv2, l)
-                   : __builtin_amdgcn_readlane(ptv3, l);
-  };
-  // a decode row's own token, when the call carries it: the workgroup of the
-  // row's last split rotates it and stores it into the pool (as
+  // ---- the split's physical page ids and, on the wave that appends a
+  // decode row's own token, that token's inputs go out first, in one round
+  // trip, and are waited for before anything else is issued: the compiler
+  // does not see the direct-to-LDS transfers below, and a wait of its own
+  // placed after them would hold for them too.  The workgroup of the row's
+  // last split rotates the token and stores it into the pool (as
   // gw_kv_append does) before any transfer, and into its LDS copy of that
-  // page once the page has landed
+  // page once the page has landed.
+  SplitPages phys;
+  phys.load(a.page_table + (int64_t)s * a.pt_stride + pg0, n, lane);
   const bool append_here = a.v_new != nullptr && split == nsplit - 1;
   GlobalRecordLane rec{};
   if (append_here && w == 0)
     rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
-  asm volatile("" ::"v"(ptv0), "v"(ptv1), "v"(ptv2), "v"(ptv3));
+  asm volatile("" ::"v"(phys.v0), "v"(phys.v1), "v"(phys.v2), "v"(phys.v3));
   if (append_here && w == 0)
-    put_global_record_as<COMPRESSED, FP8>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
-                                          p & 15, lane);
+    put_global_record<false>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec, p & 15, lane);
 
-  // ---- q into LDS by direct transfers, ahead of the pages (bf16: in ring
-  // slot NP - 1, free until the loop's first transfer): 1 KiB per head, the
-  // row's 16-byte chunk c of head h stored at chunk c ^ (h % 8), so that the
-  // Q^T operand reads below hit distinct banks.  Wave w moves heads
-  // 2 HB w .. +2 HB - 1; lane i fetches the chunk that lands at position i.
-  uint8_t* qs = FP8 ? smem + kQOff : smem + (NP - 1) * kPair;
+  // ---- q into ring slot NP - 1 (free until the loop's first transfer) by
+  // direct transfers: 1 KiB per head, the row's 16-byte chunk c of head h at
+  // chunk c ^ (h % 8), so that the Q^T operand reads hit distinct banks
+  uint8_t* qs = smem + (NP - 1) * kPair;
   {
     const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
@@ -295,46 +622,34 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 
   // ---- transfers: unit u (1 KiB) of pair j is unit u % (kUnits / 2) of
   // page 2j (u < kUnits / 2) or page 2j + 1, landing at unit u of the pair's
-  // ring slot, so the LDS copy has the pool's layout.  Wave w moves units
-  // kEven w .. + kEven - 1 and, below kExtra, unit 8 kEven + w.  An odd
-  // split's last pair repeats its last page as the second; that copy's
-  // scores are masked and its V zeroed.  The loop's waits count transfers
-  // only; the appending wave's pool stores and the q transfers are older
-  // than all of them, so they are covered too.
-  const int my_units = kEven + (w < kExtra ? 1 : 0);
-  const uint32_t ring_base = uniform_i32((int)lds_address(smem));
+  // ring slot (the pool's layout); wave w moves units kPerWave w .. +kPerWave
+  // - 1.  An odd split's last pair repeats its last page as the second; that
+  // copy's scores are masked and its V zeroed.
+  const uint32_t ring_lds = uniform_i32((int)lds_address(smem));
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
     const uint8_t* src0 = a.pool + (int64_t)phys(2 * j) * a.page_bytes + 16 * lane;
     const uint8_t* src1 = a.pool + (int64_t)phys(min(2 * j + 1, n - 1)) * a.page_bytes + 16 * lane;
-    const uint32_t dst = ring_base + (uint32_t)((j % NP) * kPair);
-    auto unit = [&](int u) __attribute__((always_inline)) {
-      constexpr int kHalf = kUnits / 2;
-      const uint8_t* src = u < kHalf ? src0 + 1024 * u : src1 + 1024 * (u - kHalf);
-      dma16_to_lds(src, dst + 1024 * u);
-    };
+    const uint32_t dst = ring_lds + (uint32_t)((j % NP) * kPair);
 #pragma unroll
-    for (int u = 0; u < kEven; ++u) unit(kEven * w + u);
-    if (kExtra > 0 && w < kExtra) unit(8 * kEven + w);
-  };
-  // at most k pairs' transfers of this wave left in flight
-  auto wait_pairs_after = [&](int k) __attribute__((always_inline)) {
-    if (kExtra > 0 && my_units == kEven) wait_groups_after<(kExtra > 0 ? kEven : kPerWave)>(k);
-    else wait_groups_after<kPerWave>(k);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int u = kPerWave * w + i;
+      constexpr int kHalf = kUnits / 2;
+      dma16_to_lds(u < kHalf ? src0 + 1024 * u : src1 + 1024 * (u - kHalf), dst + 1024 * u);
+    }
   };
 #pragma unroll
   for (int j = 0; j < NP - 1; ++j)
     if (j < n_pairs) issue_pair(j);
 
-  // Q^T operand for the wave's score part: head 16hb + l16, dims
-  // 32 ks + 8g .. +7 (16-byte chunk 4ks + g), ks = 4 sp + k, once every
-  // wave's q transfers (older than its page transfers) are in
-  wait_pairs_after(min(NP - 1, n_pairs));
+  // Q^T operands of the wave's score block (head 16 hb + l16, dims 256 dh +
+  // 32 k + 8g .. +7), once every wave's q transfers are in
+  wait_groups_after<kPerWave>(min(NP - 1, n_pairs));
   lds_barrier();
-  bf16x8 qf[4];
+  bf16x8 qf[1][8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int ks = 4 * sp + k;
-    qf[k] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + (((4 * ks + g) ^ (head & 7)) * 16));
+  for (int k = 0; k < 8; ++k) {
+    const int c = 4 * (8 * dh + k) + g;
+    qf[0][k] = *reinterpret_cast<const bf16x8*>(qs + head * 1024 + ((c ^ (head & 7)) * 16));
   }
   f32x4* xs = reinterpret_cast<f32x4*>(smem + kXsOff);
 
@@ -342,70 +657,52 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  // V^T read offsets: bf16, the tr16 lane offset inside page a (page b at
-  // + kBytes); e4m3, the tr8 row r = l16 / 2 of the lane's group names token
-  // 4g + r % 4 of page a (r < 4) or b, half l16 % 2 of the block's 16 dims
-  int vo;
-  if constexpr (FP8) {
-    const int r = l16 >> 1;
-    vo = (r < 4 ? 0 : PG::kBytes) + PG::kVOff + (((d_lo >> 4) * 16 + 4 * g + (r & 3)) * 16) + 8 * (l16 & 1);
-  } else {
-    vo = global_v_lane_off<COMPRESSED>(d_lo, g, l16);
-  }
-  const uint32_t ring_lds = uniform_i32((int)lds_address(smem));
+  const int vo = global_v_lane_off<false>(d_lo, g, l16);
 
   for (int j = 0; j < n_pairs; ++j) {
-    wait_pairs_after(min(NP - 2, n_pairs - 1 - j));
+    wait_groups_after<kPerWave>(min(NP - 2, n_pairs - 1 - j));
     lds_barrier();   // pair j is in LDS for every wave; pair j - 1 is done
     if (j + NP - 1 < n_pairs) issue_pair(j + NP - 1);
-    const uint32_t slot = ring_lds + (uint32_t)((j % NP) * kPair);
-    const lds_u8* pa = (const lds_u8*)(uintptr_t)slot;
-    if (append_here && j == ((n - 1) >> 1)) {
-      if (w == 0) put_global_record_as<COMPRESSED, FP8>(smem + (j % NP) * kPair + ((n - 1) & 1) * PG::kBytes, rec,
-                                                        p & 15, lane);
+    const lds_u8* pa = (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((j % NP) * kPair));
+    if (append_here && j == n_pairs - 1) {
+      if (w == 0) put_global_record<false>(smem + (j % NP) * kPair + ((n - 1) & 1) * PG::kBytes, rec, p & 15, lane);
       lds_barrier();
     }
-    // ---- scores: the wave's part, then the head block's four parts added
-    // in part order
-    f32x4 sc[2];
-    global_pair_scores<COMPRESSED, FP8>(sc, pa, qf, sp, g, l16);
-    if (HB == 2 || w < 4) {
-      xs[(w * 64 + lane) * 2 + 0] = sc[0];
-      xs[(w * 64 + lane) * 2 + 1] = sc[1];
+    if (scorer) {
+      f32x4 sc[1];
+      global_tile_scores<false, false, 1>(sc, pa + t_sc * PG::kBytes, qf, dh, g, l16);
+      xs[((2 * t_sc + dh) * HB + hb) * 64 + lane] = sc[0] * a.scale_log2;
     }
     lds_barrier();
-    const int w0 = HB == 2 ? hb : 0, ws = HB == 2 ? 2 : 1;   // wave of part q: w0 + ws q
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const f32x4 x0 = xs[((w0 + 0 * ws) * 64 + lane) * 2 + t], x1 = xs[((w0 + 1 * ws) * 64 + lane) * 2 + t];
-      const f32x4 x2 = xs[((w0 + 2 * ws) * 64 + lane) * 2 + t], x3 = xs[((w0 + 3 * ws) * 64 + lane) * 2 + t];
-      sc[t] = (x0 + x1) + (x2 + x3);
-    }
 
-    // ---- online softmax for head l16 over the pair's 32 tokens; on the
-    // split's last pair, tokens past p and a missing second page are masked
-    const int tok_a = (pg0 + 2 * j) * 16 + 4 * g;   // the lane's first token of page a; page b: + 16
-    const bool last = j == n_pairs - 1;             // uniform
+    // ---- online softmax for head l16 over the pair's 32 tokens (lane:
+    // tokens 4g .. 4g+3 of page a, then of page b); on the split's last
+    // pair, tokens past p and a missing second page are masked
     float z[2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 sc = xs[((2 * t + 0) * HB + hb) * 64 + lane] + xs[((2 * t + 1) * HB + hb) * 64 + lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[t][r] = sc[t][r] * a.scale_log2;
+      for (int r = 0; r < 4; ++r) z[t][r] = sc[r];
+    }
+    const bool last = j == n_pairs - 1;   // uniform
     uint32_t vm[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (last) {
+      const int tok_a = (pg0 + 2 * j) * 16 + 4 * g;
       const bool b_ok = 2 * j + 1 < n;
+      bool ok[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool ok = tok_a + 16 * t + r <= p && (t == 0 || b_ok);
-          z[t][r] = ok ? z[t][r] : -INFINITY;
+          ok[t][r] = tok_a + 16 * t + r <= p && (t == 0 || b_ok);
+          z[t][r] = ok[t][r] ? z[t][r] : -INFINITY;
         }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          vm[2 * t + h] = (z[t][2 * h] != -INFINITY ? 0x0000ffffu : 0u) | (z[t][2 * h + 1] != -INFINITY ? 0xffff0000u : 0u);
+          vm[2 * t + h] = (ok[t][2 * h] ? 0x0000ffffu : 0u) | (ok[t][2 * h + 1] ? 0xffff0000u : 0u);
     }
     const float mx = max_lanes_xor16_32(fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
                                               fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3]))));
@@ -423,15 +720,13 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         pp[2 * t + h] = pack_bf16(__builtin_amdgcn_exp2f(z[t][2 * h] - m_run), __builtin_amdgcn_exp2f(z[t][2 * h + 1] - m_run));
-    l_run += ((bf16_lo(pp[0]) + bf16_hi(pp[0])) + (bf16_lo(pp[1]) + bf16_hi(pp[1]))) +
-             ((bf16_lo(pp[2]) + bf16_hi(pp[2])) + (bf16_lo(pp[3]) + bf16_hi(pp[3])));
+    l_run = dot2_bf16(pp[3], kBf16Ones, dot2_bf16(pp[2], kBf16Ones, dot2_bf16(pp[1], kBf16Ones, dot2_bf16(pp[0], kBf16Ones, l_run))));
     const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pp[0], pp[1], pp[2], pp[3]});
 
     // ---- O^T += V^T . P^T over the pair's 32 tokens, per 16-dim block
     uint4 vf[kBlocks];
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) vf[b] = global_pair_vt<COMPRESSED, FP8>(pa, vo, b);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int b = 0; b < kBlocks; ++b) vf[b] = global_pair_vt<false, false>(pa, pa + PG::kBytes, vo, b);
     if (last) {
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
@@ -454,13 +749,13 @@ __global__ __launch_bounds__(512, 1) void global_decode_kernel(GlobalAttnArgs a)
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b] * inv;
   } else {
-    const int64_t pi = ((int64_t)s * a.num_q_heads + head) * a.max_splits + split;
-    float* op = a.part_acc + pi * kGD + d_lo + 4 * g;
+    const int64_t item = (int64_t)s * a.max_splits + split;
+    f32x4* op = reinterpret_cast<f32x4*>(a.part_acc) + ((item * HB + hb) * 32 + (d_lo >> 4)) * 64 + lane;
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) *reinterpret_cast<f32x4*>(op + 16 * b) = acc[b];
+    for (int b = 0; b < kBlocks; ++b) op[64 * b] = acc[b];
     if (d_lo == 0 && g == 0) {
-      a.part_ml[pi * 2 + 0] = m_run;
-      a.part_ml[pi * 2 + 1] = l_tot;
+      a.part_ml[(item * a.num_q_heads + head) * 2 + 0] = m_run;
+      a.part_ml[(item * a.num_q_heads + head) * 2 + 1] = l_tot;
     }
   }
 }
@@ -705,16 +1000,20 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
-// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  One
-// workgroup per (sequence, q head), 128 threads: thread t owns output dims
-// 4t .. 4t+3.  Every load of a chunk of 32 splits (each thread's acc
-// quarter-rows, and (m, l) of split t by thread t) goes out at once, so a
-// chunk costs one round trip; M and the weights are shared through LDS.
-constexpr int kReduceChunk = 32;
+// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  The
+// partials sit in MFMA fragment order (fragment (hb, block) of a split: 64
+// lanes x 4 floats, lane g*16 + l16 holding head 16 hb + l16, dims
+// 16 block + 4g .. +3), so each wave of the reduce takes one fragment of a
+// sequence and every load moves 1 KiB in one piece.  A thread merges its
+// lane's splits in chunks of kReduceChunk (one round trip per chunk; a
+// later chunk with a larger max rescales what came before).
+constexpr int kReduceChunk = 16;
 
-__global__ __launch_bounds__(128) void global_split_reduce_kernel(ReduceArgs a) {
-  __shared__ float sm_m[kReduceChunk], sm_l[kReduceChunk];
-  const int s = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(256) void global_split_reduce_kernel(ReduceArgs a) {
+  const int s = blockIdx.x, lane = threadIdx.x & 63;
+  const int frag = blockIdx.y * 4 + (threadIdx.x >> 6);   // hb * 32 + block
+  const int hbs = a.num_q_heads / 16;
+  if (frag >= hbs * 32) return;
   int row = s;
   if (a.q_indptr) {
     row = a.q_indptr[s];
@@ -722,26 +1021,24 @@ __global__ __launch_bounds__(128) void global_split_reduce_kernel(ReduceArgs a) 
   }
   const int nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
   if (nsplit <= 1) return;
-  const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_splits;
-  const float* pa = a.part_acc + base * kGD + 4 * t;
-  const float* ml = a.part_ml + base * 2;
+  const int head = 16 * (frag >> 5) + (lane & 15);
+  const f32x4* pa = reinterpret_cast<const f32x4*>(a.part_acc) + ((int64_t)s * a.max_splits * hbs * 32 + frag) * 64 + lane;
+  const float* ml = a.part_ml + ((int64_t)s * a.max_splits * a.num_q_heads + head) * 2;
+  const int64_t acc_step = (int64_t)hbs * 32 * 64, ml_step = 2 * (int64_t)a.num_q_heads;
   float M = -INFINITY, lsum = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk) {
     const int nc = min(kReduceChunk, nsplit - c0);
     f32x4 v[kReduceChunk];
+    float2 x[kReduceChunk];
 #pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i)
-      v[i] = i < nc ? *reinterpret_cast<const f32x4*>(pa + (int64_t)(c0 + i) * kGD) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < nc) {
-      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * (c0 + t));
-      sm_m[t] = x.x;
-      sm_l[t] = x.y;
+    for (int i = 0; i < kReduceChunk; ++i) {
+      v[i] = i < nc ? pa[(c0 + i) * acc_step] : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[i] = i < nc ? *reinterpret_cast<const float2*>(ml + (c0 + i) * ml_step) : float2{-INFINITY, 0.f};
     }
-    __syncthreads();
-    // the running max over the splits so far; earlier chunks rescale once
     float mc = -INFINITY;
-    for (int i = 0; i < nc; ++i) mc = fmaxf(mc, sm_m[i]);
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i) mc = fmaxf(mc, x[i].x);
     const float mnew = fmaxf(M, mc);
     if (mnew > M) {
       const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
@@ -752,20 +1049,20 @@ __global__ __launch_bounds__(128) void global_split_reduce_kernel(ReduceArgs a) 
 #pragma unroll
     for (int i = 0; i < kReduceChunk; ++i) {
       if (i < nc) {
-        const float w = __builtin_amdgcn_exp2f(sm_m[i] - M);
-        lsum += sm_l[i] * w;
+        const float w = __builtin_amdgcn_exp2f(x[i].x - M);
+        lsum += x[i].y * w;
         o += v[i] * w;
       }
     }
-    __syncthreads();   // sm_m / sm_l are rewritten by the next chunk
   }
-  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + h) * kGD + 4 * t) = o / lsum;
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + head) * kGD + 16 * (frag & 31) + 4 * (lane >> 4)) =
+      o / lsum;
 }
 
 }  // namespace
 
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs, a.num_q_heads), block(128);
+  dim3 grid(num_seqs, a.num_q_heads / 16 * 32 / 4), block(256);
   hipLaunchKernelGGL(global_split_reduce_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
@@ -773,21 +1070,21 @@ hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t st
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool fp8, hipStream_t stream) {
   dim3 grid(a.max_splits * a.num_seqs), block(512);
   const bool h32 = a.num_q_heads == 32;
-  constexpr int kNc = GW_GLOBAL_NP_C, kNf = GW_GLOBAL_NP_F, kNc8 = GW_GLOBAL_NP_C8, kNf8 = GW_GLOBAL_NP_F8;
+  constexpr int kNc = GW_GLOBAL_NS_C, kNf = GW_GLOBAL_NP_F, kNc8 = GW_GLOBAL_NS_C8, kNf8 = GW_GLOBAL_NS_F8;
   if (fp8) {
     if (compressed) {
-      if (h32) hipLaunchKernelGGL((global_decode_kernel<true, 2, kNc8, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((global_decode_kernel<true, 1, kNc8, true>), grid, block, 0, stream, a);
+      if (h32) hipLaunchKernelGGL((global_decode_ws_kernel<true, 2, kNc8, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((global_decode_ws_kernel<true, 1, kNc8, true>), grid, block, 0, stream, a);
     } else {
-      if (h32) hipLaunchKernelGGL((global_decode_kernel<false, 2, kNf8, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((global_decode_kernel<false, 1, kNf8, true>), grid, block, 0, stream, a);
+      if (h32) hipLaunchKernelGGL((global_decode_ws_kernel<false, 2, kNf8, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((global_decode_ws_kernel<false, 1, kNf8, true>), grid, block, 0, stream, a);
     }
   } else if (compressed) {
-    if (h32) hipLaunchKernelGGL((global_decode_kernel<true, 2, kNc>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_decode_kernel<true, 1, kNc>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_decode_ws_kernel<true, 2, kNc, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_decode_ws_kernel<true, 1, kNc, false>), grid, block, 0, stream, a);
   } else {
-    if (h32) hipLaunchKernelGGL((global_decode_kernel<false, 2, kNf>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_decode_kernel<false, 1, kNf>), grid, block, 0, stream, a);
+    if (h32) hipLaunchKernelGGL((global_decode_full_kernel<2, kNf>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((global_decode_full_kernel<1, kNf>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

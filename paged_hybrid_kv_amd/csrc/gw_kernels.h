@@ -45,8 +45,8 @@ struct GlobalAttnArgs {
   int32_t num_q_heads;        // 16 or 32
   float scale_log2;
   float* out;                 // fp32 [rows][Hq][512]
-  float* part_acc;            // fp32 [S][Hq][max_splits][512]
-  float* part_ml;             // fp32 [S][Hq][max_splits][2]
+  float* part_acc;            // fp32 [S][max_splits][Hq / 16][32 blocks][64 lanes][4] (MFMA fragment order)
+  float* part_ml;             // fp32 [S][max_splits][Hq][2]
   int* counters;              // [S] splits finished; zero between calls
   int32_t max_splits;
   int32_t num_seqs;
@@ -60,8 +60,8 @@ struct GlobalAttnArgs {
 struct ReduceArgs {
   const int32_t* q_indptr;
   const int32_t* seq_lens;
-  const float* part_acc;      // fp32 [S][Hq][max_splits][512]
-  const float* part_ml;       // fp32 [S][Hq][max_splits][2]
+  const float* part_acc;      // fp32 [S][max_splits][Hq / 16][32 blocks][64 lanes][4]
+  const float* part_ml;       // fp32 [S][max_splits][Hq][2]
   float* out;                 // fp32 [rows][Hq][512]
   int32_t num_q_heads;
   int32_t max_splits;
