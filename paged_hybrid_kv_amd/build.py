@@ -11,6 +11,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgw.so")
+# the trace build (GW_TRACE): the same library with per-workgroup event
+# times recorded by the decode kernels (paged_hybrid_kv_amd/trace.py)
+TRACE_LIB = os.path.join(PKG, "libgw_trace.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -28,10 +31,12 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into paged_hybrid_kv_amd/libgw.so; return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile every source into paged_hybrid_kv_amd/libgw.so (trace=True:
+    the trace build, libgw_trace.so); return its path."""
+    lib = TRACE_LIB if trace else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(["-DGW_TRACE"] if trace else []), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,9 +48,9 @@ def build(verbose: bool = False) -> str:
         lines = [x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x]
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv))

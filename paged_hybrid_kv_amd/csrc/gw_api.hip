@@ -33,6 +33,9 @@ int ok() {
   return GW_OK;
 }
 
+// The trace build's event buffer (gw_trace_buffer), else null.
+uint64_t* g_trace = nullptr;
+
 constexpr size_t kAlign = 256;
 // Longest sequence served (tokens): keeps every page count and split bound
 // of the plans well inside 32-bit arithmetic.
@@ -158,6 +161,17 @@ int hip_fail(const char* fn, hipError_t e) {
 }  // namespace
 
 extern "C" {
+
+#ifdef GW_TRACE
+// Trace builds only (not part of the C ABI in gw.h): the device buffer of
+// 16 x grid uint64 slots the decode kernels record their event times into
+// (null: stop recording).
+int gw_trace_buffer(void* dev_buf) {
+  g_trace = static_cast<uint64_t*>(dev_buf);
+  return GW_OK;
+}
+#endif
+
 
 const char* gw_version(void) { return "gw 0.1.0 (gfx950, paged hybrid-KV decode attention)"; }
 
@@ -352,6 +366,7 @@ int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t 
   }
 
   gw::LocalAttnArgs a{};
+  a.trace = g_trace;
   a.pool = static_cast<const uint8_t*>(pool->base);
   a.page_bytes = page_bytes_of(pool);
   a.head_bytes = (int32_t)(a.page_bytes / pool->num_kv_heads);
@@ -472,6 +487,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if (num_seqs == 0 || num_rows == 0) return ok();
 
   gw::GlobalAttnArgs a{};
+  a.trace = g_trace;
   a.pool = static_cast<const uint8_t*>(pool->base);
   a.page_bytes = page_bytes_of(pool);
   a.q = static_cast<const uint16_t*>(q);

@@ -123,6 +123,32 @@ __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Event times of the trace build (compiled with GW_TRACE; nothing otherwise):
+// workgroup b records event k at trace[16 b + k], in ticks of the 100 MHz
+// constant clock (s_memrealtime), or a value (GW_TRACE_V).  The slots each
+// kernel uses are listed where it records them; paged_hybrid_kv_amd/trace.py
+// reads them back.
+#ifdef GW_TRACE
+#define GW_TRACE_T(args, k, cond)                                                                         \
+  do {                                                                                                   \
+    if ((args).trace && (cond)) (args).trace[16 * (int64_t)blockIdx.x + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define GW_TRACE_V(args, k, cond, val)                                                 \
+  do {                                                                                \
+    if ((args).trace && (cond)) (args).trace[16 * (int64_t)blockIdx.x + (k)] = (uint64_t)(val); \
+  } while (0)
+// the XCD (XCC_ID hardware register, bits 3:0) the workgroup runs on
+#define GW_TRACE_XCC() ((uint64_t)__builtin_amdgcn_s_getreg((3 << 11) | 20))
+#else
+#define GW_TRACE_T(args, k, cond) \
+  do {                            \
+  } while (0)
+#define GW_TRACE_V(args, k, cond, val) \
+  do {                                 \
+  } while (0)
+#define GW_TRACE_XCC() 0ull
+#endif
+
 // Reductions over the lanes l, l^16, l^32, l^48 (the four lanes holding one
 // MFMA 16x16 column): v_permlane32_swap / v_permlane16_swap exchange the
 // halves / the 16-lane rows of a register with itself, so each step pairs a

@@ -26,7 +26,7 @@
 // Work split: one workgroup per (sequence, split) item, numbered compactly
 // (workgroup b takes item b); a split is a balanced run of the row's pages
 // (gw_plan.h), streamed in pairs straight from HBM into an LDS ring
-// (global_load_lds_dwordx4, every wave moving its share of every pair).
+// (global_load_lds_dwordx4, issued by the waves with time to spare).
 // The score and value steps of a pair are split between waves and
 // pipelined a pair apart (global_decode_ws_kernel: four score waves, each
 // taking one page and half the score contraction's dims for every head, so
@@ -271,15 +271,19 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   constexpr int kXsBytes = HB * 4 * 1024;     // one pair's partial scores: [page][dim half][hb][lane] f32x4
   constexpr int kXsOff = NS * PG::kBytes;
   // pages issued before the loop: every slot q does not hold, at most 10
-  // (so that no wait below counts more than 31 transfers)
+  // (so that no wait below counts more than 31 transfers of a score wave)
   constexpr int kPro = NS - kQPages < 10 ? NS - kQPages : 10;
-  static_assert(NS >= 6 && kPro >= 2 && (NS - 4) * ((kU + 7) / 8) <= 31 && kPro * ((kU + 7) / 8) <= 31, "ring depth");
+  static_assert(NS >= 6 && kPro >= 2 && (NS - 4) * ((kU + 3) / 4) <= 31 && kPro * ((kU + 3) / 4) <= 31, "ring depth");
   static_assert(!FP8 || NS % 2 == 0, "an e4m3 pair's pages sit side by side");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + 2 * kXsBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
   const bool scorer = w < 4;
+  // trace slots: 0 XCD | split << 8 | sequence << 32, 1 pairs, 2 entry,
+  // 3 pair 0 in LDS, 4 step 1 open, 5 value waves' loop done, 6 score
+  // waves' loop done, 7 exit (value wave 4)
+  GW_TRACE_T(a, 2, tid == 0);
   const int g = lane >> 4, l16 = lane & 15;
 
   GlobalItem it;
@@ -321,26 +325,29 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   // ---- transfers: page q of the split (pages 2j, 2j + 1 make pair j; an
   // odd split's last pair repeats its last page as the second, whose scores
   // are masked and V zeroed) lands in page slot q % NS, in the pool's
-  // layout; its 1 KiB unit u is moved by wave (kU q + u) % 8, so each wave
-  // moves its share of every pair.  The waits count transfers only: q's
-  // transfers are older than all of them, and the appending wave's loads and
-  // pool stores come after the first pages' transfers (the compiler waits for
-  // those loads, and with them for everything older) and before every later
-  // transfer, so a later wait covers the stores too.
+  // layout; its 1 KiB unit u is moved by score wave (kU q + u) % 4.  The
+  // value waves, the pipeline's longer path, issue no page transfers: a
+  // direct-to-LDS transfer can hold its wave at issue for a good part of a
+  // microsecond when many are in flight, and that stall then falls on the
+  // waves with time to spare.  The waits count page transfers only: q's
+  // transfers are older than all of them, and the appending wave (a value
+  // wave) has no page transfers, so each of its waits covers its pool stores.
   const uint32_t ring_lds = uniform_i32((int)lds_address(smem));
   const int n_pg = 2 * n_pairs;
-  auto first_unit = [&](int q) __attribute__((always_inline)) { return (w - kU * q) & 7; };
+  auto first_unit = [&](int q) __attribute__((always_inline)) { return (w - kU * q) & 3; };
   auto units_of = [&](int q) __attribute__((always_inline)) {
+    if (!scorer) return 0;
     const int u0 = first_unit(q);
-    return u0 < kU ? (kU - 1 - u0) / 8 + 1 : 0;
+    return u0 < kU ? (kU - 1 - u0) / 4 + 1 : 0;
   };
   auto issue_page = [&](int q) __attribute__((always_inline)) {
+    if (!scorer) return;
     const uint8_t* src = a.pool + (int64_t)phys(min(q, n - 1)) * a.page_bytes + 16 * lane;
     const uint32_t dst = ring_lds + (uint32_t)((q % NS) * PG::kBytes);
     const int u0 = first_unit(q);
 #pragma unroll
-    for (int k = 0; k < (kU + 7) / 8; ++k) {
-      const int u = u0 + 8 * k;
+    for (int k = 0; k < (kU + 3) / 4; ++k) {
+      const int u = u0 + 4 * k;
       if (u < kU) dma16_to_lds(src + 1024 * u, dst + 1024 * u);
     }
   };
@@ -379,6 +386,9 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   // pair 0 and q in LDS for every wave
   wait_through(1);
   lds_barrier();
+  GW_TRACE_T(a, 3, tid == 0);
+  GW_TRACE_V(a, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)split << 8 | (uint64_t)s << 32);
+  GW_TRACE_V(a, 1, tid == 0, n_pairs);
 
   if (scorer) {
     // ---- score waves: Q^T operands (head 16 hb + l16, dims 256 dh + 32 k +
@@ -403,6 +413,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
         for (int hb = 0; hb < HB; ++hb) xb[((2 * t_sc + dh) * HB + hb) * 64 + lane] = sc[hb] * a.scale_log2;
       }
     }
+    GW_TRACE_T(a, 6, tid == 0);
     return;
   }
 
@@ -434,6 +445,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   }
   for (int i = 0; i <= n_pairs; ++i) {
     step_open(i);
+    GW_TRACE_T(a, 4, tid == 256 && i == 1);
     if (i == 0) continue;
     {
       const int j = i - 1;
@@ -527,6 +539,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
     }
   }
 
+  GW_TRACE_T(a, 5, tid == 256);
   // ---- write: lane holds head 16 hb + l16, dims v_lo + 16b + 4g .. +3
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -548,6 +561,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
       }
     }
   }
+  GW_TRACE_T(a, 7, tid == 256);
 }
 
 // The full bf16 record (64 KiB pairs, a ring of two): all eight waves on
@@ -573,6 +587,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform_i32(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
+  // trace slots: those of global_decode_ws_kernel, 3 q in LDS, 5 loop done
+  GW_TRACE_T(a, 2, tid == 0);
   const bool scorer = HB == 2 || w < 4;
   const int t_sc = HB == 2 ? (w >> 1) & 1 : w & 1;     // score block: page,
   const int dh = HB == 2 ? w >> 2 : (w >> 1) & 1;      // dim half,
@@ -645,6 +661,9 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
   // 32 k + 8g .. +7), once every wave's q transfers are in
   wait_groups_after<kPerWave>(min(NP - 1, n_pairs));
   lds_barrier();
+  GW_TRACE_T(a, 3, tid == 0);
+  GW_TRACE_V(a, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)split << 8 | (uint64_t)s << 32);
+  GW_TRACE_V(a, 1, tid == 0, n_pairs);
   bf16x8 qf[1][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -741,6 +760,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[b]), pb, acc[b], 0, 0, 0);
   }
 
+  GW_TRACE_T(a, 5, tid == 0);
   // ---- write: lane holds head 16hb + l16, dims d_lo + 16b + 4g .. +3
   const float l_tot = sum_lanes_xor16_32(l_run);
   if (nsplit == 1) {
@@ -758,6 +778,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
       a.part_ml[(item * a.num_q_heads + head) * 2 + 1] = l_tot;
     }
   }
+  GW_TRACE_T(a, 7, tid == 0);
 }
 
 // The scores half of the page for the prompt rows: S^T = K . Q^T per row

@@ -32,6 +32,7 @@ struct LocalAttnArgs {
   const uint16_t* v_new;      // bf16 [rows][Hkv][256], or null (no append)
   const float* rope_cos;      // [max_pos][128] or null (K stored as given)
   const float* rope_sin;
+  uint64_t* trace;            // per-workgroup event times (trace builds only), else null
 };
 
 struct GlobalAttnArgs {
@@ -54,6 +55,7 @@ struct GlobalAttnArgs {
   const uint16_t* v_new;      // bf16 [rows][512] raw V (= K before rotation) of each row's token, or null
   const float* rope_cos;      // [max_pos][64]
   const float* rope_sin;
+  uint64_t* trace;            // per-workgroup event times (trace builds only), else null
 };
 
 // Global family's cross-split reduce (gw_global.hip).

@@ -445,6 +445,11 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   constexpr int kLocalWaves = local_waves(G);
   constexpr int kLocalThreads = 64 * kLocalWaves;
   const int tid = threadIdx.x, lane = tid & 63;
+  // trace slots: 0 XCD | split << 8 | KV head << 16 | sequence << 32,
+  // 1 pages of wave 0 | splits << 16 | merged << 32, 2 entry, 3 q and page
+  // table in LDS, 4 wave 0's pages done, 5 waves merged, 6 arrival counted,
+  // 7 exit, 8 + w wave w's pages done
+  GW_TRACE_T(a, 2, tid == 0);
   const int w = uniform_i32(tid >> 6);
   // Workgroups go split-major (every pair's split 0, then every pair's
   // split 1, ...), rows fastest: a pair's splits are dispatched apart, which
@@ -540,6 +545,8 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
     *reinterpret_cast<u32x4*>(&sm_q[tid / 32][4 * (j ^ ((j >> 3) & 7))]) = qv;
   }
   __syncthreads();
+  GW_TRACE_T(a, 3, tid == 0);
+  GW_TRACE_V(a, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)split << 8 | (uint64_t)g << 16 | (uint64_t)s << 32);
 
   // q of the group, this lane's quarter of the dims, as bf16 pairs (bf16
   // pages; e4m3 pages read it from LDS)
@@ -643,6 +650,9 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   }
 
   asm volatile("" : "+v"(epoch));
+  GW_TRACE_T(a, 4, tid == 0);
+  GW_TRACE_T(a, 8 + w, lane == 0);
+  GW_TRACE_V(a, 1, tid == 0, (uint64_t)nw | (uint64_t)nsplit << 16);
   // ---- merge the waves in LDS, in wave order
   __shared__ float sm_acc[kLocalWaves][G][kLocalD];
   __shared__ float sm_m[kLocalWaves][G], sm_l[kLocalWaves][G];
@@ -682,11 +692,13 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
       o[h] += sm_acc[ww][h][d] * sw;
     }
   }
+  GW_TRACE_T(a, 5, tid == 0);
   if (nsplit == 1) {
     if (!dt) return;
 #pragma unroll
     for (int h = 0; h < G; ++h)
       a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = o[h] / lsum[h];
+    GW_TRACE_T(a, 7, tid == 0);
     return;
   }
 
@@ -720,7 +732,11 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   if (tid == 0)
     sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   lds_barrier();
-  if (!sm_last || !dt) return;
+  GW_TRACE_T(a, 6, tid == 0);
+  if (!sm_last || !dt) {
+    GW_TRACE_T(a, 7, tid == 0);
+    return;
+  }
   // The heads of the group are merged together, so their loads share one
   // round trip; a row's range of up to 68 pages has at most 4 splits (at
   // either split size).
@@ -738,6 +754,8 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
     __hip_atomic_store(a.epochs + (int64_t)s * a.num_kv_heads + g, epoch + 1u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
+  GW_TRACE_V(a, 1, tid == 0, (uint64_t)nw | (uint64_t)nsplit << 16 | 1ull << 32);
+  GW_TRACE_T(a, 7, tid == 0);
 }
 
 }  // namespace
