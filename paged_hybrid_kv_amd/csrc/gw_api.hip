@@ -128,6 +128,38 @@ WsPlan plan_workspace(int family, int num_seqs, int num_kv_heads, int num_q_head
   return w;
 }
 
+// Compute units of the current device, read once per device (0 if the
+// query fails).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Consecutive splits of a (sequence, KV head) per local decode workgroup:
+// the fewest (1, 2 or 4, up to gw::local_max_splits_per_wg) with which the
+// launch needs no more workgroups than the device has CUs, and no more than
+// the most splits a row has.  The plan and the arithmetic do not change
+// with it (gw_local.hip), only how many workgroups carry the splits: a
+// large batch runs fewer, longer workgroups, which merge their own splits
+// in registers.
+int local_splits_per_wg(long long pairs, int max_splits, int group, bool fp8) {
+  const int cus = device_cus();
+  const int most = gw::local_max_splits_per_wg(group, fp8);
+  if (cus <= 0) return 1;
+  int spw = 1;
+  while (spw < most && spw < max_splits && pairs * gw::cdiv_i(max_splits, spw) > cus) spw *= 2;
+  return spw;
+}
+
 // Arguments common to both attention entry points.
 int check_attn_common(const char* fn, const void* q, int num_q_heads, const int32_t* q_indptr,
                       const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
@@ -329,7 +361,9 @@ int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t 
                                   max_seq_len, window, group);
   // grids: (split, KV head, sequence) for the decode rows, (row block, KV
   // head) for the prompt rows
-  const long long dec_wgs = (long long)std::max(w.max_splits, 1) * pool->num_kv_heads * num_seqs;
+  const int spw = local_splits_per_wg((long long)pool->num_kv_heads * num_seqs, std::max(w.max_splits, 1), group,
+                                      pool->kv_dtype == GW_KV_E4M3);
+  const long long dec_wgs = (long long)gw::cdiv_i(std::max(w.max_splits, 1), spw) * pool->num_kv_heads * num_seqs;
   if (dec_wgs > kMaxGrid)
     return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups (served: up to %lld)", dec_wgs, kMaxGrid);
   if (max_q_len > 1) {
@@ -385,7 +419,8 @@ int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t 
   a.epochs = w.total ? reinterpret_cast<uint32_t*>(ws + w.counter_bytes) : nullptr;
   a.part_acc = w.total ? reinterpret_cast<uint64_t*>(ws + w.counter_bytes + w.epoch_bytes) : nullptr;
   a.part_ml = w.total ? reinterpret_cast<uint64_t*>(ws + w.counter_bytes + w.epoch_bytes + w.acc_bytes) : nullptr;
-  a.max_splits = w.max_splits;
+  a.max_splits = std::max(w.max_splits, 1);
+  a.splits_per_wg = spw;
   a.num_seqs = num_seqs;
   a.num_rows = num_rows;
   a.k_new = static_cast<const uint16_t*>(k_new);

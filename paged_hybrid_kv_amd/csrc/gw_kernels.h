@@ -26,6 +26,7 @@ struct LocalAttnArgs {
   int* counters;              // [S][Hkv] splits finished; zero between calls
   uint32_t* epochs;           // [S][Hkv] calls with split partials so far
   int32_t max_splits;
+  int32_t splits_per_wg;      // consecutive splits of a (sequence, KV head) per workgroup: 1, 2 or 4
   int32_t num_seqs;
   int32_t num_rows;
   const uint16_t* k_new;      // bf16 [rows][Hkv][256] raw K of each row's own token, or null

@@ -236,14 +236,15 @@ __device__ __forceinline__ void process_page(PageRegs<FP8>& r, const uint32_t (&
   if (b % kTok != 0) {
     // the V unit holding slots b - 1 and b: slots >= b come from the first page
     const uint32_t keep = FP8 ? (1u << (8 * (b % 4))) - 1u : 0x0000ffffu;
+    // as masks on every unit (a branch per unit would select a register by
+    // a run-time index, which the compiler may place in scratch)
 #pragma unroll
     for (int u = 0; u < LocalLayout<FP8>::kLoads; ++u) {
-      if (u == b / kTok) {
-        r.v[u].x = (r.v[u].x & keep) | (r.vx.x & ~keep);
-        r.v[u].y = (r.v[u].y & keep) | (r.vx.y & ~keep);
-        r.v[u].z = (r.v[u].z & keep) | (r.vx.z & ~keep);
-        r.v[u].w = (r.v[u].w & keep) | (r.vx.w & ~keep);
-      }
+      const uint32_t take = u == b / kTok ? ~keep : 0u;
+      r.v[u].x = (r.v[u].x & ~take) | (r.vx.x & take);
+      r.v[u].y = (r.v[u].y & ~take) | (r.vx.y & take);
+      r.v[u].z = (r.v[u].z & ~take) | (r.vx.z & take);
+      r.v[u].w = (r.v[u].w & ~take) | (r.vx.w & take);
     }
   }
   // ---- scores: lane (t, c) dots its quarter of K_t with q, then quad sum;
@@ -440,7 +441,25 @@ __device__ __forceinline__ bool merge_splits(const LocalAttnArgs& a, int s, int 
   return ok;
 }
 
-template <int G, bool FP8>
+// A split index of the workgroup's range as a type (its value known at
+// compile time, so per-split state stays in registers).
+template <int J>
+struct SplitIndex {
+  static constexpr int value = J;
+};
+// a or b, chosen at compile time (a run-time choice of a reference would
+// make both addressable and move them to scratch)
+template <bool FIRST, class T>
+__device__ __forceinline__ T& pick(T& a, T& b) {
+  if constexpr (FIRST) return a;
+  else return b;
+}
+
+// SPW: consecutive splits of a (sequence, KV head) taken by one workgroup
+// (1, 2 or 4; the host picks it from the batch).  The plan, the pages each
+// wave walks for a split and the order it walks them, and every merge are
+// those of one split per workgroup, so results do not depend on SPW.
+template <int G, bool FP8, int SPW>
 __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(LocalAttnArgs a) {
   constexpr int kLocalWaves = local_waves(G);
   constexpr int kLocalThreads = 64 * kLocalWaves;
@@ -458,10 +477,10 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   // (one row each; prompt rows go elsewhere) are numbered compactly, in
   // order, so that the workgroups the grid holds for the prompt sequences
   // come last and leave, instead of holding CUs ahead of working ones.
-  int split, g, s, row;
+  int split, g, s, row;   // split: the first of the workgroup's SPW splits
   if (a.q_indptr == nullptr) {
     const int npairs = a.num_kv_heads * a.num_seqs;
-    split = (int)blockIdx.x / npairs;
+    split = (int)blockIdx.x / npairs * SPW;
     const int rem = (int)blockIdx.x % npairs;
     g = rem / a.num_seqs;
     s = row = rem % a.num_seqs;
@@ -481,8 +500,8 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
       n_dec += __popcll(chunk(c0, r1));
     }
     const int ndp = a.num_kv_heads * n_dec;
-    if (ndp == 0 || (int)blockIdx.x >= a.max_splits * ndp) return;
-    split = (int)blockIdx.x / ndp;
+    if (ndp == 0 || (int)blockIdx.x >= cdiv_i(a.max_splits, SPW) * ndp) return;
+    split = (int)blockIdx.x / ndp * SPW;
     const int rem = (int)blockIdx.x % ndp;
     g = rem / n_dec;
     int k = rem % n_dec;   // rank of the sequence among the decode sequences
@@ -524,11 +543,20 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   const LocalWindow win = local_window(p, a.window);
   const int nsplit = local_nsplit(win.nv, G);
   if (split >= nsplit) return;
-  const int v0 = split_lo(win.nv, nsplit, split);
-  const int v1 = split_lo(win.nv, nsplit, split + 1);
+  const int n_own = min(SPW, nsplit - split);   // splits split .. split + n_own - 1
+  // the whole row's range in this workgroup: its splits merge in registers
+  const bool covers_all = split == 0 && n_own == nsplit;
+  int v0s[SPW], v1s[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    v0s[j] = j < n_own ? split_lo(win.nv, nsplit, split + j) : 0;
+    v1s[j] = j < n_own ? split_lo(win.nv, nsplit, split + j + 1) : 0;
+  }
+  const int v0 = v0s[0], v1 = v1s[0];
+  const int v_end = SPW == 1 ? v1 : split_lo(win.nv, nsplit, split + n_own);
   // the virtual page holding position p, where a decode row's new token goes
   const int vt = win.wrap ? 0 : win.nv - 1;
-  const bool token_here = vt >= v0 && vt < v1;
+  const bool token_here = vt >= v0 && vt < v_end;
   const bool append_here = a.v_new != nullptr && token_here;
 
   // q chunk j of a head sits at chunk j ^ ((j / 8) % 8) in LDS, so that the
@@ -588,8 +616,8 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   const CI32P pt = (CI32P)(a.page_table + (int64_t)s * a.pt_stride);
   const uint8_t* head_base = a.pool + (int64_t)g * a.head_bytes;
   const int mlo = win.lo & 15, mhi = p & 15;
-  auto vpage = [&](int k) __attribute__((always_inline)) {
-    const int v = v0 + w + kLocalWaves * k;
+  auto vpage_at = [&](int vbase, int k) __attribute__((always_inline)) {
+    const int v = vbase + w + kLocalWaves * k;
     const bool merged = win.wrap && v == 0;
     const int id0 = pt_lds ? uniform_i32(sm_pt[win.pg0 + v]) : pt[win.pg0 + v];
     const int id1 = merged ? (pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl]) : id0;
@@ -607,6 +635,7 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
     d.mask = m & 0xffffu;
     return d;
   };
+  auto vpage = [&](int k) __attribute__((always_inline)) { return vpage_at(v0, k); };
 
   // this (sequence, KV head)'s call count, the tag of this call's partials:
   // read behind the first page's loads (a device-scope load goes to memory,
@@ -619,6 +648,7 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   };
 
   __shared__ uint32_t sm_tok[kLocalWaves][128];   // a patching wave's rotated token K
+  if constexpr (SPW == 1) {
   PageRegs<FP8> A, B;
   VPage dA{}, dB{};
   if (nw > 0) {
@@ -756,18 +786,231 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   }
   GW_TRACE_V(a, 1, tid == 0, (uint64_t)nw | (uint64_t)nsplit << 16 | 1ull << 32);
   GW_TRACE_T(a, 7, tid == 0);
+  } else {
+    // ---- SPW splits per workgroup.  Wave w walks, for each split j, the
+    // same pages in the same order as the workgroup of that split alone
+    // would (virtual pages v0_j + w + W k; the token's page first on the
+    // wave that holds it), into a softmax state of that split's own.  The
+    // walk interleaves the splits page by page, items (i, j) in that order,
+    // with item (i, j) in buffer A (j even) or B (j odd), so the next item
+    // always loads into the other buffer while this one is processed.  An
+    // item past a split's pages (or of a split past the row's last) is
+    // processed as a page with no slot in range: no load, nothing added.
+    static_assert(SPW == 2 || SPW == 4, "items alternate between the two buffers");
+    float m_s[SPW][G], l_s[SPW][G], acc_s[SPW][G][4];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m_s[j][h] = -INFINITY;
+        l_s[j][h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc_s[j][h][e] = 0.f;
+      }
+    int nws[SPW];
+    int nw_max = 0;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      nws[j] = j < n_own ? max(0, (v1s[j] - v0s[j] - w + kLocalWaves - 1) / kLocalWaves) : 0;
+      nw_max = max(nw_max, nws[j]);
+    }
+    int j_tok = 0;
+#pragma unroll
+    for (int j = 1; j < SPW; ++j)
+      if (j < n_own && vt >= v0s[j]) j_tok = j;
+    int v0_tok = v0s[0];
+#pragma unroll
+    for (int j = 1; j < SPW; ++j)
+      if (j == j_tok) v0_tok = v0s[j];
+    const bool tok_w = token_here && w == (vt - v0_tok) % kLocalWaves;
+    const int k_tk = tok_w ? (vt - v0_tok) / kLocalWaves : 0;
+    auto k_at = [&](int j, int i) __attribute__((always_inline)) {
+      return (!tok_w || j != j_tok) ? i : i == 0 ? k_tk : (i <= k_tk ? i - 1 : i);
+    };
+    auto real = [&](int j, int i) __attribute__((always_inline)) { return i < nws[j]; };
+    const bool patch = append_here && tok_w;
+    NewTokenLoads tok{};
+    if (patch) tok = load_new_token(a, row, g, p, lane);
+    PageRegs<FP8> A, B;
+    VPage dA{}, dB{};
+    if (real(0, 0)) {
+      dA = vpage_at(v0s[0], k_at(0, 0));
+      load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
+    }
+    if (nsplit > 1 && !covers_all) epoch = load_epoch();
+    // item (i, J): prefetch the next item into the other buffer, then
+    // process this one with split J's state
+    auto item = [&](auto jc, int i) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int kNj = (J + 1) % SPW;
+      PageRegs<FP8>& cur = pick<J % 2 == 0>(A, B);
+      PageRegs<FP8>& nxt = pick<J % 2 == 0>(B, A);
+      const int ni = J + 1 < SPW ? i : i + 1;
+      if (real(kNj, ni)) {
+        const VPage nd = vpage_at(v0s[kNj], k_at(kNj, ni));
+        pick<kNj % 2 == 0>(dA, dB) = nd;
+        load_vpage<FP8>(nxt, nd.r0, nd.r1, nd.b, lane);
+      }
+      const VPage& dc = pick<J % 2 == 0>(dA, dB);
+      const bool rl = real(J, i);
+      if (patch && rl && i == 0 && J == j_tok) {
+        const int id_tok = pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl];
+        uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)id_tok * a.page_bytes;
+        put_new_token<FP8>(cur, rec, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
+      }
+      process_page<G, FP8>(cur, qr, qh, rl ? dc.mask : 0u, rl ? dc.b : 0, a.scale_log2, lane, m_s[J], l_s[J],
+                           acc_s[J]);
+    };
+    for (int i = 0; i < nw_max; ++i) {
+      item(SplitIndex<0>{}, i);
+      item(SplitIndex<1>{}, i);
+      if constexpr (SPW == 4) {
+        item(SplitIndex<2>{}, i);
+        item(SplitIndex<3>{}, i);
+      }
+    }
+
+    asm volatile("" : "+v"(epoch));
+    GW_TRACE_T(a, 4, tid == 0);
+    GW_TRACE_T(a, 8 + w, lane == 0);
+    GW_TRACE_V(a, 1, tid == 0, (uint64_t)nws[0] | (uint64_t)nsplit << 16);
+    // ---- per split, merge the waves in LDS, in wave order
+    __shared__ float sm_acc_s[SPW][kLocalWaves][G][kLocalD];
+    __shared__ float sm_m_s[SPW][kLocalWaves][G], sm_l_s[SPW][kLocalWaves][G];
+    __shared__ int sm_last_s;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float lv = (c == 0) ? l_s[j][h] : 0.f;   // one lane per token slot
+        lv += shfl_xor_f32(lv, 4);
+        lv += shfl_xor_f32(lv, 8);
+        lv += shfl_xor_f32(lv, 16);
+        lv += shfl_xor_f32(lv, 32);
+        if (lane == 0) {
+          sm_m_s[j][w][h] = m_s[j][h];
+          sm_l_s[j][w][h] = lv;
+        }
+        *reinterpret_cast<f32x4*>(&sm_acc_s[j][w][h][4 * lane]) =
+            f32x4{acc_s[j][h][0], acc_s[j][h][1], acc_s[j][h][2], acc_s[j][h][3]};
+      }
+    __syncthreads();
+    const bool dt = tid < kLocalD;
+    const int d = dt ? tid : 0;
+    float o[SPW][G], M[SPW][G], lsum[SPW][G];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        M[j][h] = sm_m_s[j][0][h];
+#pragma unroll
+        for (int ww = 1; ww < kLocalWaves; ++ww) M[j][h] = fmaxf(M[j][h], sm_m_s[j][ww][h]);
+        lsum[j][h] = 0.f;
+        o[j][h] = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kLocalWaves; ++ww) {
+          const float mw = sm_m_s[j][ww][h];
+          const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M[j][h]);
+          lsum[j][h] += sm_l_s[j][ww][h] * sw;
+          o[j][h] += sm_acc_s[j][ww][h][d] * sw;
+        }
+      }
+    GW_TRACE_T(a, 5, tid == 0);
+    if (nsplit == 1) {
+      if (!dt) return;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = o[0][h] / lsum[0][h];
+      GW_TRACE_T(a, 7, tid == 0);
+      return;
+    }
+    if (covers_all) {
+      // the row's splits merged here, as merge_splits merges published ones
+      if (!dt) return;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+          if (j < nsplit) Mx = fmaxf(Mx, M[j][h]);
+        float ls = 0.f, ov = 0.f;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          if (j < nsplit) {
+            const float sw = __builtin_amdgcn_exp2f(M[j][h] - Mx);
+            ls += lsum[j][h] * sw;
+            ov += o[j][h] * sw;
+          }
+        }
+        a.out[((int64_t)row * a.num_q_heads + g * G + h) * kLocalD + d] = ov / ls;
+      }
+      GW_TRACE_T(a, 7, tid == 0);
+      return;
+    }
+    // ---- publish this workgroup's splits; the last workgroup of the
+    // (sequence, KV head) to arrive reduces all of them, as with one split
+    // per workgroup (the counter counts splits)
+    const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      if (j >= n_own || !dt) break;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int64_t pi = ((int64_t)s * a.num_q_heads + g * G + h) * a.max_splits + split + j;
+        __hip_atomic_store(a.part_acc + pi * kLocalD + d, tag | f32_to_bits(o[j][h]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(a.part_ml + pi * 2 + 0, tag | f32_to_bits(M[j][h]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.part_ml + pi * 2 + 1, tag | f32_to_bits(lsum[j][h]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    lds_barrier();
+    int* counter = a.counters + (int64_t)s * a.num_kv_heads + g;
+    if (tid == 0)
+      sm_last_s = __hip_atomic_fetch_add(counter, n_own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - n_own;
+    lds_barrier();
+    GW_TRACE_T(a, 6, tid == 0);
+    if (!sm_last_s || !dt) {
+      GW_TRACE_T(a, 7, tid == 0);
+      return;
+    }
+    if (nsplit <= 4) {
+      merge_splits<G, 4>(a, s, g * G, row, d, nsplit, tag);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) merge_splits<1, kLocalMaxSplits>(a, s, g * G + h, row, d, nsplit, tag);
+    }
+    if (tid == 0) {   // ready for the next call
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.epochs + (int64_t)s * a.num_kv_heads + g, epoch + 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    GW_TRACE_V(a, 1, tid == 0, (uint64_t)nws[0] | (uint64_t)nsplit << 16 | 1ull << 32);
+    GW_TRACE_T(a, 7, tid == 0);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
-  const int64_t n = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
+  const int spw = a.splits_per_wg;
+  const int64_t n = (int64_t)cdiv_i(a.max_splits, spw) * a.num_kv_heads * a.num_seqs;
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)n);
-#define GW_LOCAL_CASE(G_, F_) \
-  if (group == G_ && fp8 == F_) { hipLaunchKernelGGL((local_decode_kernel<G_, F_>), grid, dim3(64 * local_waves(G_)), 0, stream, a); return hipGetLastError(); }
-  GW_LOCAL_CASE(1, false) GW_LOCAL_CASE(2, false) GW_LOCAL_CASE(4, false)
-  GW_LOCAL_CASE(1, true) GW_LOCAL_CASE(2, true) GW_LOCAL_CASE(4, true)
+#define GW_LOCAL_CASE(G_, F_, S_)                                                                           \
+  if (group == G_ && fp8 == F_ && spw == S_) {                                                              \
+    hipLaunchKernelGGL((local_decode_kernel<G_, F_, S_>), grid, dim3(64 * local_waves(G_)), 0, stream, a); \
+    return hipGetLastError();                                                                               \
+  }
+  // the multi-split variants that fit the registers (local_max_splits_per_wg)
+  GW_LOCAL_CASE(1, false, 1) GW_LOCAL_CASE(2, false, 1) GW_LOCAL_CASE(4, false, 1)
+  GW_LOCAL_CASE(1, true, 1) GW_LOCAL_CASE(2, true, 1) GW_LOCAL_CASE(4, true, 1)
+  GW_LOCAL_CASE(4, false, 2)
+  GW_LOCAL_CASE(1, true, 2) GW_LOCAL_CASE(2, true, 2) GW_LOCAL_CASE(4, true, 2)
+  GW_LOCAL_CASE(4, true, 4)
 #undef GW_LOCAL_CASE
   return hipErrorInvalidValue;
 }

@@ -17,6 +17,13 @@ namespace gw {
 constexpr int kLocalMaxSplits = 16;
 __host__ __device__ constexpr int local_waves(int group) { return group >= 4 ? 4 : 8; }
 __host__ __device__ constexpr int local_min_pages_per_split(int group) { return group >= 4 ? 17 : 33; }
+// Most consecutive splits one local decode workgroup takes: a wave keeps
+// one softmax state per split, and the bf16 pages of group sizes 1 and 2
+// leave no registers for a second (the 4-wave workgroups of group size 4
+// have twice the registers per wave).
+__host__ __device__ constexpr int local_max_splits_per_wg(int group, bool fp8) {
+  return fp8 ? (group >= 4 ? 4 : 2) : (group >= 4 ? 2 : 1);
+}
 
 // Global family: splits of at least 20 pages (320 tokens), at most 64 per
 // row unless that would put more than 256 pages in one split: 16 rows of

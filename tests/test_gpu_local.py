@@ -183,6 +183,32 @@ def test_row_order_and_batch_bitexact(fp8):
         assert np.array_equal(o1[0], o_all[s])
 
 
+@pytest.mark.parametrize("fp8,hq", [(True, 16), (True, 32), (False, 32)])
+def test_split_grouping_batch_invariant(fp8, hq):
+    """A batch with more (sequence, KV head) splits than the device has CUs
+    runs workgroups that each take 2 or 4 splits of a pair (e4m3 pages at
+    group sizes 2 and 4, bf16 pages at group size 4); every row must equal,
+    bit for bit, the same row computed alone (one split per workgroup)."""
+    rng = np.random.default_rng(77 + hq + fp8)
+    lens = [int(x) for x in rng.integers(2048, 8193, 48)]
+    lens[5] = 2048          # aligned window
+    lens[6] = 1030          # window that wraps a page
+    lens[7] = 700           # shorter than the window: one split
+    base = SY.local_case("grouped", 12, lens, window=1024, num_q_heads=hq, num_kv_heads=8,
+                         rope=True, fp8=fp8, fill_window_only=True)
+    _, o_all = run(base)
+    for s in (0, 5, 6, 7, 47):
+        one = SY.local_case("one", 12, [lens[s]], window=1024, num_q_heads=hq, num_kv_heads=8,
+                            rope=True, fp8=fp8, fill_window_only=True)
+        sel = base.tok_seq == s
+        one.q = base.q[s:s + 1]
+        one.k, one.v = base.k[sel], base.v[sel]
+        one.tok_seq = np.zeros(sel.sum(), np.int32)
+        one.tok_pos = base.tok_pos[sel]
+        _, o1 = run(one)
+        assert np.array_equal(o1[0], o_all[s]), f"row {s} (L={lens[s]}) differs from its solo call"
+
+
 def test_repeat_determinism():
     case = SY.local_case("repeat", 9, [5000, 2000, 8000], window=1024, num_q_heads=16,
                          num_kv_heads=8, rope=True)
