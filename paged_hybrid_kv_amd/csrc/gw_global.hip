@@ -117,8 +117,8 @@ __device__ __forceinline__ bf16x8 widen_e4m3x8(uint32_t w0, uint32_t w1) {
 }
 
 // The V^T operand of output block b (16 dims) for a pair of pages in LDS
-// (page a at pa, page b at pb; an e4m3 pair must have pb = pa + kBytes, as
-// one transposing read spans both pages): lane (g, l16) gets dim (its
+// (page a at pa, page b at pb; for an e4m3 pair each lane's offset vo
+// already names its page, as one transposing read spans both): lane (g, l16) gets dim (its
 // block's first dim + l16) of tokens 4g .. 4g+3 of page a, then of page b,
 // as 8 bf16.  vo: the lane's byte offset for block 0 (bf16:
 // global_v_lane_off in a page; e4m3: the tr8 row it names, in page a or b).
@@ -267,9 +267,14 @@ template <bool COMPRESSED, int HB, int NS, bool FP8>
 __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs a) {
   using PG = GlobalPage<COMPRESSED, FP8>;
   constexpr int kU = PG::kBytes / 1024;       // 1 KiB transfer units per page
-  constexpr int kQPages = (HB * 16 * 1024 + PG::kBytes - 1) / PG::kBytes;   // page slots q holds at first
+  // page slot stride: e4m3 slots are 128 bytes apart beyond the page, so the
+  // two pages a transposing V read spans (a pair sits in adjacent slots) hit
+  // opposite halves of the 64 LDS banks; the pages' sizes are multiples of
+  // the 256-byte bank width
+  constexpr int kSlot = PG::kBytes + (FP8 ? 128 : 0);
+  constexpr int kQPages = (HB * 16 * 1024 + kSlot - 1) / kSlot;   // page slots q holds at first
   constexpr int kXsBytes = HB * 4 * 1024;     // one pair's partial scores: [page][dim half][hb][lane] f32x4
-  constexpr int kXsOff = NS * PG::kBytes;
+  constexpr int kXsOff = NS * kSlot;
   // pages issued before the loop: every slot q does not hold, at most 10
   // (so that no wait below counts more than 31 transfers of a score wave)
   constexpr int kPro = NS - kQPages < 10 ? NS - kQPages : 10;
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   // ---- q into the ring's last kQPages slots (1 KiB per head, chunk c of
   // head h at chunk c ^ (h % 8), so the operand reads hit distinct banks),
   // ahead of the pages; wave w moves heads 2 HB w .. +2 HB - 1
-  uint8_t* qs = smem + (NS - kQPages) * PG::kBytes;
+  uint8_t* qs = smem + (NS - kQPages) * kSlot;
   {
     const uint32_t qs_lds = uniform_i32((int)lds_address(qs));
 #pragma unroll
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   auto issue_page = [&](int q) __attribute__((always_inline)) {
     if (!scorer) return;
     const uint8_t* src = a.pool + (int64_t)phys(min(q, n - 1)) * a.page_bytes + 16 * lane;
-    const uint32_t dst = ring_lds + (uint32_t)((q % NS) * PG::kBytes);
+    const uint32_t dst = ring_lds + (uint32_t)((q % NS) * kSlot);
     const int u0 = first_unit(q);
 #pragma unroll
     for (int k = 0; k < (kU + 3) / 4; ++k) {
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   };
   for (int q = 0; q < issued; ++q) issue_page(q);
   auto page_lds = [&](int q) __attribute__((always_inline)) {
-    return (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((q % NS) * PG::kBytes));
+    return (const lds_u8*)(uintptr_t)(ring_lds + (uint32_t)((q % NS) * kSlot));
   };
 
   // ---- the loop's synchronisation, the same on both roles: step i > 0
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
     }
     if (append_here && i == n_pairs - 1) {
       if (w == kAppendWave)
-        put_global_record_as<COMPRESSED, FP8>(smem + ((n - 1) % NS) * PG::kBytes, rec, p & 15, lane);
+        put_global_record_as<COMPRESSED, FP8>(smem + ((n - 1) % NS) * kSlot, rec, p & 15, lane);
       lds_barrier();
     }
   };
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   int vo;
   if constexpr (FP8) {
     const int r = l16 >> 1;
-    vo = (r < 4 ? 0 : PG::kBytes) + PG::kVOff + (((v_lo >> 4) * 16 + 4 * g + (r & 3)) * 16) + 8 * (l16 & 1);
+    vo = (r < 4 ? 0 : kSlot) + PG::kVOff + (((v_lo >> 4) * 16 + 4 * g + (r & 3)) * 16) + 8 * (l16 & 1);
   } else {
     vo = global_v_lane_off<COMPRESSED>(v_lo, g, l16);
   }
