@@ -16,6 +16,12 @@ markdown table:
     python -m paged_hybrid_kv_amd.counters collect /tmp/pmc_a pass_a.json
     python -m paged_hybrid_kv_amd.counters table pass_a.json pass_b.json ... [--match substr ...]
 
+and, for a kernel-trace run (rocprofv3 --kernel-trace --stats --output-format csv
+-d DIR ...), ``trace`` prints calls and mean / min / max duration per (kernel,
+grid size), which separates the launches of one kernel at different shapes:
+
+    python -m paged_hybrid_kv_amd.counters trace DIR [--match substr ...]
+
 Derived figures (per dispatch):
   cycles        GRBM_GUI_ACTIVE / 8 (the eight XCDs run the dispatch side by side)
   VALU, MFMA, LDS, VMEM, SALU instr/wave   SQ_INSTS_* / SQ_WAVES
@@ -118,12 +124,34 @@ def table(passes: list[dict], match: list[str] | None = None) -> str:
     return "\n".join(lines)
 
 
+def trace(run_dir: str, match: list[str] | None = None) -> str:
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = _kernel_name(r["Kernel_Name"])
+                grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+                per.setdefault(f"{name} grid={grid}", []).append(dur)
+    lines = ["| kernel (grid) | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for k in sorted(per):
+        if match and not any(s in k for s in match):
+            continue
+        v = per[k]
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(lines)
+
+
 def main(argv):
     if len(argv) >= 3 and argv[0] == "collect":
         res = collect(argv[1])
         with open(argv[2], "w") as f:
             json.dump(res, f, indent=1)
         print(f"{len(res)} kernel/grid entries -> {argv[2]}")
+        return 0
+    if len(argv) >= 2 and argv[0] == "trace":
+        match = [argv[i + 1] for i, a in enumerate(argv) if a == "--match" and i + 1 < len(argv)]
+        print(trace(argv[1], match or None))
         return 0
     if len(argv) >= 2 and argv[0] == "table":
         files, match = [], []
