@@ -261,10 +261,13 @@ int gw_decode_attn_local_noalloc(const gw_pool_desc* pool /* host */, const void
  * or e4m3).  num_q_heads 16 or 32.  The two layouts give bit-identical
  * results.  An e4m3 pool is read as the exact bf16 values of its codes; it
  * serves decode rows only: max_q_len > 1 returns GW_ERR_UNSUPPORTED.
- * v_new: bf16 [num_rows][512] (K is V before rotation), with the rotary
- * tables fp32 [max_pos][64]; NULL when the pool already holds the rows. */
+ * v_new: bf16 [num_rows][512], with the rotary tables fp32 [max_pos][64];
+ * NULL when the pool already holds the rows.  k_new: bf16 [num_rows][512],
+ * each row's K before rotation, of which only dims 0..127 are read (the
+ * quarter that rotates into K_rot), as gw_kv_append reads k_raw; NULL when K
+ * is V before rotation (the tied store); set only with v_new. */
 int gw_decode_attn_global(const gw_pool_desc* pool /* host */, const void* q,
-                          int32_t num_q_heads, const void* v_new, const float* rope_cos,
+                          int32_t num_q_heads, const void* k_new, const void* v_new, const float* rope_cos,
                           const float* rope_sin, const int32_t* q_indptr,
                           const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
                           int32_t num_seqs, int32_t num_rows, int32_t max_q_len,

@@ -487,7 +487,7 @@ int gw_decode_attn_local_noalloc(const gw_pool_desc* pool, const void* q, int32_
 }
 
 int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q_heads,
-                          const void* v_new, const float* rope_cos, const float* rope_sin,
+                          const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
                           const int32_t* q_indptr, const int32_t* seq_lens, const int32_t* page_table,
                           int32_t pt_stride, int32_t num_seqs, int32_t num_rows, int32_t max_q_len,
                           int32_t max_seq_len, float scale, float* out, void* workspace,
@@ -508,6 +508,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
+  if (k_new && !v_new) return fail(GW_ERR_INVALID_ARG, fn, "k_new is set but v_new is null");
   const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0, 1);
   if (max_q_len > 1) {
     const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads));
@@ -540,6 +541,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   a.max_splits = w.max_splits;
   a.num_seqs = num_seqs;
   a.num_rows = num_rows;
+  a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
@@ -547,12 +549,13 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   const bool compressed = pool->family == GW_FAMILY_GLOBAL_COMPRESSED;
   hipError_t e;
   if (v_new && max_q_len > 1) {
-    // the prompt rows' own tokens go in first (K is V before rotation); the
-    // decode kernel appends its rows itself
+    // the prompt rows' own tokens go in first; the decode kernel appends its
+    // rows itself
     gw::AppendArgs ap{};
     ap.pool = const_cast<uint8_t*>(a.pool);
     ap.page_bytes = a.page_bytes;
     ap.head_bytes = (int32_t)a.page_bytes;
+    ap.k_raw = a.k_new;
     ap.v = a.v_new;
     ap.page_table = page_table;
     ap.pt_stride = pt_stride;

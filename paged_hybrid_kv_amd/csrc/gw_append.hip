@@ -399,7 +399,9 @@ __global__ __launch_bounds__(256) void append_global_rows_kernel(AppendArgs a) {
   if (tid < 128) {
     const int c = tid >> 4, t = tid & 15;
     if (t >= rp.t0 && t <= rp.t1) {
-      const GlobalRecordLane r = global_record_lane(row_v(t), row_v(t), a.rope_cos, a.rope_sin, rp.pg * kPage + t, c);
+      const uint16_t* vr = row_v(t);
+      const uint16_t* kr = a.k_raw ? a.k_raw + (vr - a.v) : vr;   // the same row of k_raw
+      const GlobalRecordLane r = global_record_lane(vr, kr, a.rope_cos, a.rope_sin, rp.pg * kPage + t, c);
       *reinterpret_cast<uint4*>(kblock + (c * 16 + t) * 16) = r.ka;
       *reinterpret_cast<uint4*>(kblock + ((c + 8) * 16 + t) * 16) = r.kb;
     }

@@ -424,7 +424,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
 
   // ---- value waves: output dims v_lo .. +127 of every head
   if (append_here && w == kAppendWave) {
-    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+    rec = global_record_lane(a.v_new + (int64_t)row * kGD, (a.k_new ? a.k_new : a.v_new) + (int64_t)row * kGD,
+                             a.rope_cos, a.rope_sin, p, lane);
     put_global_record_as<COMPRESSED, FP8>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec,
                                           p & 15, lane);
   }
@@ -622,7 +623,8 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
   const bool append_here = a.v_new != nullptr && split == nsplit - 1;
   GlobalRecordLane rec{};
   if (append_here && w == 0)
-    rec = global_record_lane(a.v_new + (int64_t)row * kGD, a.v_new + (int64_t)row * kGD, a.rope_cos, a.rope_sin, p, lane);
+    rec = global_record_lane(a.v_new + (int64_t)row * kGD, (a.k_new ? a.k_new : a.v_new) + (int64_t)row * kGD,
+                             a.rope_cos, a.rope_sin, p, lane);
   asm volatile("" ::"v"(phys.v0), "v"(phys.v1), "v"(phys.v2), "v"(phys.v3));
   if (append_here && w == 0)
     put_global_record<false>(const_cast<uint8_t*>(a.pool) + (int64_t)phys(n - 1) * a.page_bytes, rec, p & 15, lane);

@@ -53,7 +53,8 @@ struct GlobalAttnArgs {
   int32_t max_splits;
   int32_t num_seqs;
   int32_t num_rows;
-  const uint16_t* v_new;      // bf16 [rows][512] raw V (= K before rotation) of each row's token, or null
+  const uint16_t* k_new;      // bf16 [rows][512] raw K of each row's token (dims 0..127 read), or null: K = V
+  const uint16_t* v_new;      // bf16 [rows][512] raw V of each row's token, or null
   const float* rope_cos;      // [max_pos][64]
   const float* rope_sin;
   uint64_t* trace;            // per-workgroup event times (trace builds only), else null

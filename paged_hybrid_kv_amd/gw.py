@@ -88,7 +88,7 @@ def lib():
         L.gw_decode_attn_local_noalloc.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P,
                                                    _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P]
         L.gw_decode_attn_global.restype = ctypes.c_int
-        L.gw_decode_attn_global.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P, _P,
+        L.gw_decode_attn_global.argtypes = [ctypes.POINTER(gw_pool_desc), _P, _I, _P, _P, _P, _P, _P, _P, _P,
                                             _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                             _P]
         L.gw_alloc_create.restype = ctypes.c_int
@@ -189,10 +189,10 @@ def gw_decode_attn_local_noalloc(desc: gw_pool_desc, q, num_q_heads, k_new, v_ne
                                               _stream(stream)))
 
 
-def gw_decode_attn_global(desc: gw_pool_desc, q, num_q_heads, v_new, rope_cos, rope_sin, q_indptr,
+def gw_decode_attn_global(desc: gw_pool_desc, q, num_q_heads, k_new, v_new, rope_cos, rope_sin, q_indptr,
                           seq_lens, page_table, pt_stride, num_seqs, num_rows, max_q_len, max_seq_len,
                           scale, out, workspace, workspace_bytes, stream=None):
-    _check(lib().gw_decode_attn_global(ctypes.byref(desc), _ptr(q), num_q_heads, _ptr(v_new),
+    _check(lib().gw_decode_attn_global(ctypes.byref(desc), _ptr(q), num_q_heads, _ptr(k_new), _ptr(v_new),
                                        _ptr(rope_cos), _ptr(rope_sin), _ptr(q_indptr),
                                        _ptr(seq_lens), _ptr(page_table), pt_stride, num_seqs,
                                        num_rows, max_q_len, max_seq_len, scale, _ptr(out),

@@ -207,7 +207,7 @@ def attend(dc: DeviceCase, out: torch.Tensor | None = None, ws: Workspace | None
                                 dc.page_table, dc.pt_stride, dc.num_seqs, dc.num_rows, dc.max_q_len,
                                 dc.max_seq_len, dc.window, dc.scale, out, wptr, wbytes, stream)
     else:
-        gw.gw_decode_attn_global(dc.pool.desc, dc.q, dc.num_q_heads, v_new, cos, sin,
+        gw.gw_decode_attn_global(dc.pool.desc, dc.q, dc.num_q_heads, k_new, v_new, cos, sin,
                                  dc.q_indptr, dc.seq_lens,
                                  dc.page_table, dc.pt_stride, dc.num_seqs, dc.num_rows, dc.max_q_len,
                                  dc.max_seq_len, dc.scale, out, wptr, wbytes, stream)

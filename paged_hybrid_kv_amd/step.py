@@ -121,7 +121,7 @@ class HybridStep:
                                     self.ws_ptr[fam], self.ws_bytes[fam])
         else:
             vn, cs, sn = (L["v_new"], L["cos"], L["sin"]) if append else (None,) * 3
-            gw.gw_decode_attn_global(L["pool"].desc, L["q"], sh.global_q_heads, vn, cs, sn,
+            gw.gw_decode_attn_global(L["pool"].desc, L["q"], sh.global_q_heads, None, vn, cs, sn,
                                      self.q_indptr, self.seq_lens, L["pt"], L["stride"], self.S, self.rows,
                                      self.max_q_len, self.max_len, 1.0 / np.sqrt(sh.global_head_dim),
                                      L["out"] if out is None else out,

@@ -113,9 +113,9 @@ def local(d=None, q=FAKE, hq=16, kn=None, vn=None, cos=None, sin=None, indptr=No
                             msl, win, scale, out, ws, wsb, None)
 
 
-def glob(d=None, q=FAKE, hq=32, vn=None, cos=None, sin=None, indptr=None, lens=FAKE, pt=FAKE,
+def glob(d=None, q=FAKE, hq=32, kn=None, vn=None, cos=None, sin=None, indptr=None, lens=FAKE, pt=FAKE,
          stride=8192, S=4, rows=4, mql=1, msl=131072, scale=0.044, out=FAKE, ws=FAKE, wsb=1 << 30):
-    gw.gw_decode_attn_global(d or desc(gw.GW_FAMILY_GLOBAL_COMPRESSED), q, hq, vn, cos, sin, indptr, lens,
+    gw.gw_decode_attn_global(d or desc(gw.GW_FAMILY_GLOBAL_COMPRESSED), q, hq, kn, vn, cos, sin, indptr, lens,
                              pt, stride, S, rows, mql, msl, scale, out, ws, wsb, None)
 
 
@@ -165,6 +165,7 @@ def test_local_rejects(call, code, frag):
     (lambda: glob(wsb=0), gw.GW_ERR_WORKSPACE, "workspace"),
     (lambda: glob(msl=0), gw.GW_ERR_INVALID_ARG, "max_seq_len"),
     (lambda: glob(vn=FAKE), gw.GW_ERR_INVALID_ARG, "rotary tables"),
+    (lambda: glob(kn=FAKE), gw.GW_ERR_INVALID_ARG, "k_new is set but v_new is null"),
 ])
 def test_global_rejects(call, code, frag):
     with pytest.raises(gw.GwError) as e:

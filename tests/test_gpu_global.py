@@ -169,6 +169,52 @@ def test_norm_weighted_k(rope):
     assert np.abs(ot - outs[0]).max() > 1e-2
 
 
+@pytest.mark.parametrize("mixed", [False, True])
+def test_norm_weighted_k_in_call(mixed):
+    """The query rows' own tokens appended inside the attention call, with K
+    before rotation given apart from V (k_new: a norm weight on K), in decode
+    rows and, in a mixed call, prompt rows too: the outputs equal, bit for
+    bit, those of the same tokens appended beforehand by gw_kv_append with
+    k_raw, in both records, and match the oracle's attention over the true K."""
+    lens = [700, 4097, 33, 2000]
+    q_len = [1, 1, 1, 1] if not mixed else [1, 24, 1, 7]
+    case = SY.global_case("knorm_call", 41, lens, num_q_heads=32, rope=True, k_norm=True, q_len=q_len)
+    k_raw = k_before_rotation(case)
+    q_fold = case.q.copy()
+    q_fold[..., 128:] *= case.w_k[128:]
+    # the rows' tokens: the last q_len of each sequence, in row order
+    rows = []
+    for s, (L, ql) in enumerate(zip(lens, q_len)):
+        for pos in range(L - ql, L):
+            rows.append(int(np.nonzero((case.tok_seq == s) & (case.tok_pos == pos))[0][0]))
+    rows = np.array(rows)
+    keep = np.ones(case.tok_seq.shape[0], bool)
+    keep[rows] = False
+    import copy
+    pre = copy.copy(case)
+    pre.tok_seq, pre.tok_pos, pre.v = case.tok_seq[keep], case.tok_pos[keep], case.v[keep]
+    rope = RT.rope_tables(max(lens), 128, 512, RT.GLOBAL_THETA)
+    outs = {}
+    for compressed in (True, False):
+        dc = RT.upload_global(case, compressed=compressed, k_raw=k_raw, q=q_fold)
+        outs[compressed, "before"] = RT.attend(dc).cpu().numpy()
+        del dc
+        dc = RT.upload_global(pre, compressed=compressed, k_raw=k_raw[keep], q=q_fold)
+        outs[compressed, "in_call"] = RT.attend(dc, k_new=RT.to_bf16_dev(k_raw[rows]),
+                                                v_new=RT.to_bf16_dev(case.v[rows]), rope=rope).cpu().numpy()
+        del dc
+        torch.cuda.empty_cache()
+    for compressed in (True, False):
+        assert np.array_equal(outs[compressed, "in_call"], outs[compressed, "before"]), \
+            f"in-call append with k_new differs from gw_kv_append with k_raw (compressed={compressed})"
+    assert np.array_equal(outs[True, "in_call"], outs[False, "in_call"]), "compressed and full records differ"
+    ref = oracle_out(case)
+    qi = case.q_indptr
+    mx = max(compare(outs[True, "in_call"][qi[s]:qi[s + 1]], r, f"k_norm in call mixed={mixed} seq {s}")[0]
+             for s, r in ref.items())
+    print(f"global k_norm in-call mixed={mixed}: max abs err {mx:.2e}", flush=True)
+
+
 def test_append_global_norm_weighted_k():
     """The record's rotated quarter comes from k_raw, V from v, in both layouts."""
     case = SY.global_case("append_knorm", 39, [40, 300], rope=True, k_norm=True)
