@@ -364,8 +364,16 @@ int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t 
   const int spw = local_splits_per_wg((long long)pool->num_kv_heads * num_seqs, std::max(w.max_splits, 1), group,
                                       pool->kv_dtype == GW_KV_E4M3);
   const long long dec_wgs = (long long)gw::cdiv_i(std::max(w.max_splits, 1), spw) * pool->num_kv_heads * num_seqs;
-  if (dec_wgs > kMaxGrid)
-    return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups (served: up to %lld)", dec_wgs, kMaxGrid);
+  // the prompt rows' own tokens are appended by workgroups after the decode items
+  const long long app_units =
+      v_new && max_q_len > 1
+          ? gw::rows_append_items(num_rows, num_seqs, max_q_len) *
+                gw::cdiv_i(pool->num_kv_heads, gw::kRowsAppendHeads)
+          : 0;
+  const int units_per_wg = 64 * gw::local_waves(group) / 256;
+  if (app_units > kMaxGrid || dec_wgs + (app_units + units_per_wg - 1) / units_per_wg > kMaxGrid)
+    return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups and %lld append workgroups (served: up to %lld)",
+                dec_wgs, (app_units + units_per_wg - 1) / units_per_wg, kMaxGrid);
   if (max_q_len > 1) {
     const long long pre_wgs =
         gw::prefill_items(num_rows, num_seqs, max_q_len, gw::local_prefill_rows(group)) * pool->num_kv_heads;
@@ -427,30 +435,12 @@ int attn_local(const char* fn, const gw_pool_desc* pool, const void* q, int32_t 
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
+  a.append_units = (int32_t)app_units;
   (void)hipGetLastError();   // a stale error from earlier work is not ours to report
   const bool fp8 = pool->kv_dtype == GW_KV_E4M3;
   hipError_t e;
-  if (max_q_len > 1 && v_new) {
-    // the prompt rows' own tokens go in first; the decode kernel appends its rows itself
-    gw::AppendArgs ap{};
-    ap.pool = const_cast<uint8_t*>(a.pool);
-    ap.page_bytes = a.page_bytes;
-    ap.head_bytes = a.head_bytes;
-    ap.k_raw = a.k_new;
-    ap.v = a.v_new;
-    ap.page_table = page_table;
-    ap.pt_stride = pt_stride;
-    ap.rope_cos = rope_cos;
-    ap.rope_sin = rope_sin;
-    ap.n_tok = num_rows;
-    ap.num_kv_heads = pool->num_kv_heads;
-    ap.q_indptr = q_indptr;
-    ap.seq_lens = seq_lens;
-    ap.num_seqs = num_seqs;
-    ap.skip_single = 1;
-    e = gw::launch_append_local_rows(ap, fp8, rope_cos != nullptr, max_q_len, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
+  // the decode rows (each appending its own token) and the prompt rows'
+  // append in one launch; the prompt rows attend in the next
   e = gw::launch_local_decode(a, group, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (max_q_len > 1) {
@@ -510,6 +500,11 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
   if (k_new && !v_new) return fail(GW_ERR_INVALID_ARG, fn, "k_new is set but v_new is null");
   const WsPlan w = plan_workspace(pool->family, num_seqs, 1, num_q_heads, 512, max_seq_len, 0, 1);
+  // the prompt rows' own tokens are appended by workgroups after the decode items, two units each
+  const long long app_units = v_new && max_q_len > 1 ? gw::rows_append_items(num_rows, num_seqs, max_q_len) : 0;
+  if ((long long)w.max_splits * num_seqs + (app_units + 1) / 2 > kMaxGrid)
+    return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups and %lld append workgroups (served: up to %lld)",
+                (long long)w.max_splits * num_seqs, (app_units + 1) / 2, kMaxGrid);
   if (max_q_len > 1) {
     const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads));
     if (pre_wgs > kMaxGrid)
@@ -545,31 +540,12 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
+  a.append_units = (int32_t)app_units;
   (void)hipGetLastError();
   const bool compressed = pool->family == GW_FAMILY_GLOBAL_COMPRESSED;
   hipError_t e;
-  if (v_new && max_q_len > 1) {
-    // the prompt rows' own tokens go in first; the decode kernel appends its
-    // rows itself
-    gw::AppendArgs ap{};
-    ap.pool = const_cast<uint8_t*>(a.pool);
-    ap.page_bytes = a.page_bytes;
-    ap.head_bytes = (int32_t)a.page_bytes;
-    ap.k_raw = a.k_new;
-    ap.v = a.v_new;
-    ap.page_table = page_table;
-    ap.pt_stride = pt_stride;
-    ap.rope_cos = rope_cos;
-    ap.rope_sin = rope_sin;
-    ap.n_tok = num_rows;
-    ap.num_kv_heads = 1;
-    ap.q_indptr = q_indptr;
-    ap.seq_lens = seq_lens;
-    ap.num_seqs = num_seqs;
-    ap.skip_single = 1;
-    e = gw::launch_append_global_rows(ap, compressed, max_q_len, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
+  // the decode rows (each appending its own token) and the prompt rows'
+  // append in one launch; the prompt rows attend after the reduce
   e = gw::launch_global_decode(a, compressed, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (w.max_splits > 1) {

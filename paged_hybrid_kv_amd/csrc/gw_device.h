@@ -137,6 +137,16 @@ __device__ __forceinline__ void wait_stores_done() {
   do {                                                                                \
     if ((args).trace && (cond)) (args).trace[16 * (int64_t)blockIdx.x + (k)] = (uint64_t)(val); \
   } while (0)
+// the same at trace row `row` (kernels that share a call's buffer with
+// another kernel record at rows of their own)
+#define GW_TRACE_AT(args, row, k, cond)                                                                  \
+  do {                                                                                                   \
+    if ((args).trace && (cond)) (args).trace[16 * (int64_t)(row) + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define GW_TRACE_VAT(args, row, k, cond, val)                                        \
+  do {                                                                              \
+    if ((args).trace && (cond)) (args).trace[16 * (int64_t)(row) + (k)] = (uint64_t)(val); \
+  } while (0)
 // the XCD (XCC_ID hardware register, bits 3:0) the workgroup runs on
 #define GW_TRACE_XCC() ((uint64_t)__builtin_amdgcn_s_getreg((3 << 11) | 20))
 #else
@@ -146,8 +156,17 @@ __device__ __forceinline__ void wait_stores_done() {
 #define GW_TRACE_V(args, k, cond, val) \
   do {                                 \
   } while (0)
+#define GW_TRACE_AT(args, row, k, cond) \
+  do {                                  \
+  } while (0)
+#define GW_TRACE_VAT(args, row, k, cond, val) \
+  do {                                        \
+  } while (0)
 #define GW_TRACE_XCC() 0ull
 #endif
+// first trace row of the prompt-row kernels (the decode kernels of the same
+// call record at rows 0 .. grid - 1)
+constexpr int kTracePrefillRow = 4096;
 
 // Reductions over the lanes l, l^16, l^32, l^48 (the four lanes holding one
 // MFMA 16x16 column): v_permlane32_swap / v_permlane16_swap exchange the
@@ -341,6 +360,134 @@ template <bool COMPRESSED, bool FP8>
 __device__ __forceinline__ void put_global_record_as(uint8_t* pb, const GlobalRecordLane& r, int slot, int l) {
   if constexpr (FP8) put_global_record_e4m3<COMPRESSED>(pb, r, slot, l);
   else put_global_record<COMPRESSED>(pb, r, slot, l);
+}
+
+}  // namespace gw
+
+namespace gw {
+
+// Sum / max over the 64 lanes of a wave, by DPP moves (no LDS round
+// trips): inclusive prefixes within each 16-lane row (row_shr 1, 2, 4, 8),
+// then lane 15 of rows 0 and 2 into rows 1 and 3 (row_bcast:15) and lane 31
+// into rows 2 and 3 (row_bcast:31); lane 63 ends with the whole wave's
+// value.  A lane a move does not reach takes 0, which neither changes a sum
+// nor, for values >= 0, a max (wave_max_nonneg_i32 takes only such values).
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int wave_max_nonneg_i32(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Prompt-row work items of an attention call.  The prompt sequences (more
+// than one query row) are cut into groups of `rows` consecutive rows, and
+// the groups are numbered level by level: level k holds, in sequence order,
+// the k-th last group of every prompt sequence that has more than k groups.
+// A later group of a sequence attends a longer key range, so the items with
+// the longest ranges of all sequences are dispatched first and the shorter
+// ones fill in behind them as workgroups finish.
+struct PromptItem {
+  int s;       // sequence
+  int grp;     // row group (rows grp * rows ..), counted from the sequence's first row
+  int row0;    // the sequence's first row in the call
+  int q_len;   // its rows in the call
+  int len;     // its length, the call's tokens included
+};
+
+// Sequences held in registers, 64 per chunk; a call with more reads the
+// rest again on every pass.
+constexpr int kPromptItemChunks = 4;
+
+// Item `item` (uniform) of the call; false past the last.  Every lane of the
+// wave must take part.
+__device__ inline bool prompt_item(const int32_t* q_indptr, const int32_t* seq_lens, int num_seqs, int rows,
+                                   int item, int lane, PromptItem& it) {
+  constexpr int kC = kPromptItemChunks;
+  auto load = [&](int c0, int& o_cnt, int& o_row0, int& o_qlen, int& o_len) __attribute__((always_inline)) {
+    const int sl = c0 + lane;
+    o_cnt = o_row0 = o_qlen = o_len = 0;
+    if (sl < num_seqs) {
+      o_row0 = q_indptr[sl];
+      o_qlen = q_indptr[sl + 1] - o_row0;
+      o_len = seq_lens[sl];
+      if (o_qlen > 1) o_cnt = (o_qlen + rows - 1) / rows;
+    }
+  };
+  int cnt[kC], r0[kC], ql[kC], ln[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) load(64 * c, cnt[c], r0[c], ql[c], ln[c]);
+  // items in the levels below k: sum over sequences of min(groups, k)
+  auto count_below = [&](int k) __attribute__((always_inline)) {
+    int t = 0;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) t += min(cnt[c], k);
+    for (int c0 = 64 * kC; c0 < num_seqs; c0 += 64) {
+      int cn, a, b, d;
+      load(c0, cn, a, b, d);
+      t += min(cn, k);
+    }
+    return wave_sum_i32(t);
+  };
+  int mx = 0;
+#pragma unroll
+  for (int c = 0; c < kC; ++c) mx = max(mx, cnt[c]);
+  for (int c0 = 64 * kC; c0 < num_seqs; c0 += 64) {
+    int cn, a, b, d;
+    load(c0, cn, a, b, d);
+    mx = max(mx, cn);
+  }
+  const int levels = wave_max_nonneg_i32(mx);
+  if (item < 0 || item >= count_below(levels)) return false;
+  // the item's level k: count_below(k) <= item < count_below(k + 1)
+  int lo = 0, hi = levels;   // count_below(lo) <= item < count_below(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_below(mid) <= item) lo = mid;
+    else hi = mid;
+  }
+  const int k = lo;
+  int r = item - count_below(k);   // rank of the item's sequence among those with more than k groups
+  auto pick = [&](uint64_t m, int c0, int cn, int rr, int qq, int ll) __attribute__((always_inline)) {
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint64_t hit = __ballot(((m >> lane) & 1) && rank == r);
+    if (hit == 0) return false;   // r < popcount(m) makes this unreachable
+    const int ls = __builtin_ctzll(hit);
+    it.s = c0 + ls;
+    it.grp = __builtin_amdgcn_readlane(cn, ls) - 1 - k;
+    it.row0 = __builtin_amdgcn_readlane(rr, ls);
+    it.q_len = __builtin_amdgcn_readlane(qq, ls);
+    it.len = __builtin_amdgcn_readlane(ll, ls);
+    return true;
+  };
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const uint64_t m = __ballot(cnt[c] > k);
+    const int p = __popcll(m);
+    if (r < p) return pick(m, 64 * c, cnt[c], r0[c], ql[c], ln[c]);
+    r -= p;
+  }
+  for (int c0 = 64 * kC; c0 < num_seqs; c0 += 64) {   // ends: the item exists
+    int cn, rr, qq, ll;
+    load(c0, cn, rr, qq, ll);
+    const uint64_t m = __ballot(cn > k);
+    const int p = __popcll(m);
+    if (r < p) return pick(m, c0, cn, rr, qq, ll);
+    r -= p;
+  }
+  return false;
 }
 
 }  // namespace gw

@@ -51,6 +51,7 @@
 #include "gw_device.h"
 #include "gw_kernels.h"
 #include "gw_plan.h"
+#include "gw_rows_append.h"
 
 namespace gw {
 namespace {
@@ -290,6 +291,15 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   // waves' loop done, 7 exit (value wave 4)
   GW_TRACE_T(a, 2, tid == 0);
   const int g = lane >> 4, l16 = lane & 15;
+  // the workgroups past the decode items append the prompt rows' own
+  // tokens, two units of 256 threads each (the prompt rows attend in a
+  // later launch; e4m3 pools serve decode rows only)
+  if constexpr (!FP8) {
+    if ((int)blockIdx.x >= a.append_wg0) {
+      global_rows_append_unit<COMPRESSED>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
+      return;
+    }
+  }
 
   GlobalItem it;
   if (!global_item(a, blockIdx.x, lane, it)) return;
@@ -600,6 +610,11 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
   const int dh = HB == 2 ? w >> 2 : (w >> 1) & 1;      // dim half,
   const int hb = HB == 2 ? w & 1 : 0;                   // head block (also of the PV step)
   const int d_lo = HB == 2 ? 128 * (w >> 1) : 64 * w;   // output dims d_lo .. + 16 kBlocks
+  // the workgroups past the decode items append the prompt rows' own tokens
+  if ((int)blockIdx.x >= a.append_wg0) {
+    global_rows_append_unit<false>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
+    return;
+  }
 
   GlobalItem it;
   if (!global_item(a, blockIdx.x, lane, it)) return;
@@ -883,8 +898,9 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
 // waves per SIMD; two rows per wave do not fit the registers), through a
 // ring of NS pages that all waves fill.  No split: a row's whole range is
 // one pass, and the output is written directly.  Items are (prompt
-// sequence, row group), numbered compactly, a sequence's last groups
-// (longest ranges) first.
+// sequence, row group), numbered compactly level by level (every
+// sequence's last group first, then every sequence's second last, ...: the
+// longest ranges of the call first).
 template <bool COMPRESSED, int HB, int NR, int NS>
 __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(GlobalAttnArgs a) {
   using PG = GlobalPage<COMPRESSED>;
@@ -898,6 +914,12 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
+  // trace slots (row kTracePrefillRow + b): 0 XCD | row group << 8 |
+  // sequence << 32, 1 pages, 2 entry, 3 first page in LDS, 4 wave 0's loop
+  // done, 5 iteration 1 open, 6 last iteration open, 7 exit, 8 + w wave w's
+  // loop done
+  const int trow = kTracePrefillRow + (int)blockIdx.x;
+  GW_TRACE_AT(a, trow, 2, tid == 0);
   const int wv = uniform_i32(tid >> 6);
   const int hb = HB == 2 ? (wv & 1) : 0;
   const int rp = HB == 2 ? (wv >> 1) : wv;
@@ -906,35 +928,13 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
 
   int s = -1, mg = 0, row0 = 0, q_len = 0, L = 0;
   {
-    const int item = blockIdx.x;
-    int base = 0;
-    for (int c = 0; c < a.num_seqs; c += 64) {
-      const int sl = c + lane;
-      int cnt = 0, r0 = 0, ql = 0, len = 0;
-      if (sl < a.num_seqs) {
-        r0 = a.q_indptr[sl];
-        ql = a.q_indptr[sl + 1] - r0;
-        len = a.seq_lens[sl];
-        if (ql > 1) cnt = (ql + kRows - 1) / kRows;
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int up = __shfl_up(incl, d, 64);
-        incl += lane >= d ? up : 0;
-      }
-      const int total = __builtin_amdgcn_readlane(incl, 63);
-      if (item < base + total) {
-        const int ls = __builtin_ctzll(__ballot(base + incl > item));
-        s = c + ls;
-        const int nb = __builtin_amdgcn_readlane(cnt, ls);
-        mg = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
-        row0 = __builtin_amdgcn_readlane(r0, ls);
-        q_len = __builtin_amdgcn_readlane(ql, ls);
-        L = __builtin_amdgcn_readlane(len, ls);
-        break;
-      }
-      base += total;
+    PromptItem it;
+    if (prompt_item(a.q_indptr, a.seq_lens, a.num_seqs, kRows, (int)blockIdx.x, lane, it)) {
+      s = it.s;
+      mg = it.grp;
+      row0 = it.row0;
+      q_len = it.q_len;
+      L = it.len;
     }
   }
   if (s < 0) return;
@@ -949,6 +949,8 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   const int r_last = min(kRows * mg + kRows - 1, q_len - 1);
   const int p_last = L - q_len + r_last;
   const int n = (p_last >> 4) + 1;
+  GW_TRACE_VAT(a, trow, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)mg << 8 | (uint64_t)s << 32);
+  GW_TRACE_VAT(a, trow, 1, tid == 0, n);
   int rw[NR], pr[NR];
   bool rok[NR];
 #pragma unroll
@@ -1001,12 +1003,15 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   if (nu > kPerWave) wait_groups_after<kPerWave + 1>(min(NS - 2, n - 1));
   else wait_groups_after<kPerWave>(min(NS - 2, n - 1));
   lds_barrier();
+  GW_TRACE_AT(a, trow, 3, tid == 0);
   f32x4 sc[NR][2];
   global_rows_scores<COMPRESSED, NR>(sc, ring[0], qf, g, l16);
   for (int i = 0; i < n; ++i) {
     if (nu > kPerWave) wait_groups_after<kPerWave + 1>(max(0, min(NS - 3, n - 2 - i)));
     else wait_groups_after<kPerWave>(max(0, min(NS - 3, n - 2 - i)));
     lds_barrier();   // pages i and i + 1 are in LDS for every wave; page i - 1 is done
+    GW_TRACE_AT(a, trow, 5, tid == 0 && i == 1);
+    GW_TRACE_AT(a, trow, 6, tid == 0 && i == n - 1);
     if (i + NS - 1 < n) issue_page(i + NS - 1);
     f32x4 sn[NR][2];
     global_rows_scores<COMPRESSED, NR>(sn, ring[min(i + 1, n - 1) % NS], qf, g, l16);
@@ -1015,6 +1020,8 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
 #pragma unroll
     for (int r = 0; r < NR; ++r) { sc[r][0] = sn[r][0]; sc[r][1] = sn[r][1]; }
   }
+  GW_TRACE_AT(a, trow, 4, tid == 0);
+  GW_TRACE_AT(a, trow, 8 + wv, lane == 0);
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     if (!rok[i]) continue;
@@ -1025,6 +1032,7 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
 #pragma unroll
     for (int b = 0; b < 32; ++b) __builtin_nontemporal_store(acc[i][b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
   }
+  GW_TRACE_AT(a, trow, 7, tid == 0);
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
@@ -1095,8 +1103,14 @@ hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool fp8, hipStream_t stream) {
-  dim3 grid(a.max_splits * a.num_seqs), block(512);
+hipError_t launch_global_decode(const GlobalAttnArgs& a_in, bool compressed, bool fp8, hipStream_t stream) {
+  // the decode items, then the prompt rows' append units (two per workgroup)
+  const int64_t n_dec = (int64_t)a_in.max_splits * a_in.num_seqs;
+  const int64_t n = n_dec + (fp8 ? 0 : (a_in.append_units + 1) / 2);
+  if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GlobalAttnArgs a = a_in;
+  a.append_wg0 = (int32_t)n_dec;
+  dim3 grid((unsigned)n), block(512);
   const bool h32 = a.num_q_heads == 32;
   constexpr int kNc = GW_GLOBAL_NS_C, kNf = GW_GLOBAL_NP_F, kNc8 = GW_GLOBAL_NS_C8, kNf8 = GW_GLOBAL_NS_F8;
   if (fp8) {

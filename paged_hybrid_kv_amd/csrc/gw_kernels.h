@@ -33,6 +33,11 @@ struct LocalAttnArgs {
   const uint16_t* v_new;      // bf16 [rows][Hkv][256], or null (no append)
   const float* rope_cos;      // [max_pos][128] or null (K stored as given)
   const float* rope_sin;
+  // the prompt rows' own tokens: append units (page item x block of two KV
+  // heads) taken by the decode kernel's workgroups from append_wg0 on, 256
+  // threads a unit; 0 when the call appends none
+  int32_t append_units;
+  int32_t append_wg0;
   uint64_t* trace;            // per-workgroup event times (trace builds only), else null
 };
 
@@ -57,6 +62,11 @@ struct GlobalAttnArgs {
   const uint16_t* v_new;      // bf16 [rows][512] raw V of each row's token, or null
   const float* rope_cos;      // [max_pos][64]
   const float* rope_sin;
+  // the prompt rows' own tokens: append units (one page item each) taken by
+  // the decode kernel's workgroups from append_wg0 on, 256 threads a unit;
+  // 0 when the call appends none
+  int32_t append_units;
+  int32_t append_wg0;
   uint64_t* trace;            // per-workgroup event times (trace builds only), else null
 };
 
@@ -85,11 +95,12 @@ struct AppendArgs {
   const float* rope_sin;
   int32_t n_tok;
   int32_t num_kv_heads;
-  // Rows mode (seq_lens non-null): token i is query row i of an attention
-  // call -- its sequence found in q_indptr (or i itself when q_indptr is
-  // null: one row per sequence), its position seq_lens[s] - q_len +
-  // (i - q_indptr[s]); seq_idx / pos are unused.  skip_single: leave out the
-  // rows of one-row sequences (their decode kernel appends them).
+  // Rows mode (the prompt rows of an attention call, gw_rows_append.h):
+  // token i is query row i of the call -- its sequence found in q_indptr
+  // (or i itself when q_indptr is null: one row per sequence), its position
+  // seq_lens[s] - q_len + (i - q_indptr[s]); seq_idx / pos are unused.
+  // skip_single: leave out the rows of one-row sequences (their decode
+  // kernel appends them).  The per-token kernels take seq_idx / pos.
   const int32_t* q_indptr;
   const int32_t* seq_lens;
   int32_t num_seqs;
@@ -106,8 +117,6 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int m
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStream_t stream);
 // Rows mode (seq_lens set): one workgroup per (sequence, page of its rows).
-hipError_t launch_append_local_rows(const AppendArgs& a, bool fp8, bool rope, int max_q_len, hipStream_t stream);
-hipError_t launch_append_global_rows(const AppendArgs& a, bool compressed, int max_q_len, hipStream_t stream);
 hipError_t launch_append_global(const AppendArgs& a, bool compressed, bool fp8, hipStream_t stream);
 hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int rot_dim,
                              int head_dim, double theta, hipStream_t stream);

@@ -37,6 +37,7 @@
 #include "gw_device.h"
 #include "gw_kernels.h"
 #include "gw_plan.h"
+#include "gw_rows_append.h"
 
 namespace gw {
 namespace {
@@ -469,6 +470,12 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
   // table in LDS, 4 wave 0's pages done, 5 waves merged, 6 arrival counted,
   // 7 exit, 8 + w wave w's pages done
   GW_TRACE_T(a, 2, tid == 0);
+  // the workgroups past the decode items append the prompt rows' own
+  // tokens, 256 threads a unit (the prompt rows attend in the next launch)
+  if ((int)blockIdx.x >= a.append_wg0) {
+    local_rows_append_unit<FP8>(a, ((int)blockIdx.x - a.append_wg0) * (kLocalThreads / 256) + tid / 256, tid % 256);
+    return;
+  }
   const int w = uniform_i32(tid >> 6);
   // Workgroups go split-major (every pair's split 0, then every pair's
   // split 1, ...), rows fastest: a pair's splits are dispatched apart, which
@@ -997,12 +1004,17 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
 
 hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipStream_t stream) {
   const int spw = a.splits_per_wg;
-  const int64_t n = (int64_t)cdiv_i(a.max_splits, spw) * a.num_kv_heads * a.num_seqs;
+  // the decode items, then the prompt rows' append units (256 threads each)
+  const int64_t n_dec = (int64_t)cdiv_i(a.max_splits, spw) * a.num_kv_heads * a.num_seqs;
+  const int per_wg = 64 * local_waves(group) / 256;
+  const int64_t n = n_dec + (a.append_units + per_wg - 1) / per_wg;
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  LocalAttnArgs b = a;
+  b.append_wg0 = (int32_t)n_dec;
   dim3 grid((unsigned)n);
 #define GW_LOCAL_CASE(G_, F_, S_)                                                                           \
   if (group == G_ && fp8 == F_ && spw == S_) {                                                              \
-    hipLaunchKernelGGL((local_decode_kernel<G_, F_, S_>), grid, dim3(64 * local_waves(G_)), 0, stream, a); \
+    hipLaunchKernelGGL((local_decode_kernel<G_, F_, S_>), grid, dim3(64 * local_waves(G_)), 0, stream, b); \
     return hipGetLastError();                                                                               \
   }
   // the multi-split variants that fit the registers (local_max_splits_per_wg)

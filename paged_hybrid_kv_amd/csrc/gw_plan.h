@@ -78,6 +78,17 @@ inline long long prefill_items(long long num_rows, long long num_seqs, long long
   return by_rows < by_len ? by_rows : by_len;
 }
 
+// Page items of the prompt rows' append in an attention call: a sequence
+// of q rows touches at most (q + 14) / 16 + 1 pages, so the call at most
+// (rows + 30 sequences) / 16 (and at most sequences * pages of max_q_len).
+// A local item covers kRowsAppendHeads KV heads of its page.
+constexpr int kRowsAppendHeads = 2;
+inline long long rows_append_items(long long num_rows, long long num_seqs, long long max_q_len) {
+  const long long by_rows = (num_rows + 30 * num_seqs) / 16;
+  const long long by_len = num_seqs * ((max_q_len + 14) / 16 + 1);
+  return by_rows < by_len ? by_rows : by_len;
+}
+
 // Pages touched by the window of a query at position p: [p_lo/16, p/16].
 __host__ __device__ inline int local_range_pages(int p, int window) {
   int lo = p - window + 1;

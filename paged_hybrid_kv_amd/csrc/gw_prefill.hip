@@ -33,9 +33,11 @@
 // convert to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the
 // products are the same as on the bf16 values.  P is rounded to bf16 for
 // PV and the sum l adds exactly those rounded values.  Workgroups are
-// numbered compactly over the prompt sequences' row blocks, a sequence's
-// longest ranges first, with the KV head as the fastest index (so one
-// head's blocks share an XCD when there are eight heads).
+// numbered compactly over the prompt sequences' row blocks, level by level
+// (every sequence's last block first, then every sequence's second last,
+// ...: the longest ranges of the call first), with the KV head as the
+// fastest index (so one head's blocks share an XCD when there are eight
+// heads).
 
 #include "gw_device.h"
 #include "gw_kernels.h"
@@ -143,43 +145,26 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   // workgroup b: KV head b % Hkv of item b / Hkv (the head fastest)
   const int gk = (int)blockIdx.x % a.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
+  // trace slots (row kTracePrefillRow + b): 0 XCD | row block << 8 | KV
+  // head << 16 | sequence << 32, 1 steps, 2 entry, 3 first step in LDS,
+  // 4 wave 0's loop done, 5 iteration 1 open, 6 last iteration open, 7 exit,
+  // 8 + w wave w's loop done
+  const int trow = kTracePrefillRow + (int)blockIdx.x;
+  GW_TRACE_AT(a, trow, 2, tid == 0);
   const int w = uniform_i32(tid >> 6);
   const int gq = lane >> 4, l16 = lane & 15;
 
-  // ---- work item: the call's (prompt sequence, row block) items, numbered
-  // sequence by sequence, the blocks of a sequence from its last (longest
-  // range) to its first
+  // ---- work item: the call's (prompt sequence, row block) items, level by
+  // level (every sequence's last block -- the longest range -- first)
   int s = -1, rb = 0, row0 = 0, q_len = 0, L = 0;
   {
-    const int item = (int)blockIdx.x / a.num_kv_heads;
-    int base = 0;
-    for (int c = 0; c < a.num_seqs; c += 64) {
-      const int sl = c + lane;
-      int cnt = 0, r0 = 0, ql = 0, len = 0;
-      if (sl < a.num_seqs) {
-        r0 = a.q_indptr[sl];
-        ql = a.q_indptr[sl + 1] - r0;
-        len = a.seq_lens[sl];
-        if (ql > 1) cnt = cdiv_i(ql, kRows);
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int up = __shfl_up(incl, d, 64);
-        incl += lane >= d ? up : 0;
-      }
-      const int total = __builtin_amdgcn_readlane(incl, 63);
-      if (item < base + total) {
-        const int ls = __builtin_ctzll(__ballot(base + incl > item));
-        s = c + ls;
-        const int nb = __builtin_amdgcn_readlane(cnt, ls);
-        rb = nb - 1 - (item - (base + __builtin_amdgcn_readlane(incl, ls) - nb));
-        row0 = __builtin_amdgcn_readlane(r0, ls);
-        q_len = __builtin_amdgcn_readlane(ql, ls);
-        L = __builtin_amdgcn_readlane(len, ls);
-        break;
-      }
-      base += total;
+    PromptItem it;
+    if (prompt_item(a.q_indptr, a.seq_lens, a.num_seqs, kRows, (int)blockIdx.x / a.num_kv_heads, lane, it)) {
+      s = it.s;
+      rb = it.grp;
+      row0 = it.row0;
+      q_len = it.q_len;
+      L = it.len;
     }
   }
   if (s < 0) return;
@@ -204,6 +189,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   // every row of the block attends [lo_max, p_min] (at least)
   const int lo_max = max(0, pos0 + r_last - a.window + 1);
   const int p_min = pos0 + r_first;
+  GW_TRACE_VAT(a, trow, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)rb << 8 | (uint64_t)gk << 16 | (uint64_t)s << 32);
+  GW_TRACE_VAT(a, trow, 1, tid == 0, n_steps);
 
   // this lane's two query vectors, v = 32 w + 16 qb + l16: row
   // r_first + v / G, head v % G of the group; each masks its own window
@@ -293,12 +280,15 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   // slot is refilled once every wave is past iteration j - 1.
   wait_groups_after<kPerStep>(min(n_steps - 1, NS - 2));
   lds_barrier();
+  GW_TRACE_AT(a, trow, 3, tid == 0);
   f32x4 sc[2][QB];
   scores(0, sc);
   for (int j = 0; j < n_steps; ++j) {
     const int jn = min(j + 1, n_steps - 1);   // the last iteration recomputes its own step's scores, unused
     wait_groups_after<kPerStep>(max(0, min(n_steps - 2 - j, NS - 3)));
     lds_barrier();   // step j + 1 is in LDS for every wave; step j - 1 is done
+    GW_TRACE_AT(a, trow, 5, tid == 0 && j == 1);
+    GW_TRACE_AT(a, trow, 6, tid == 0 && j == n_steps - 1);
     if (j + NS - 1 < n_steps) issue_step(j + NS - 1);
     const uint8_t* pg0 = ring[j % NS][0];
     const uint8_t* pg1 = ring[j % NS][1];
@@ -392,6 +382,9 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
       for (int qb = 0; qb < QB; ++qb) sc[tb][qb] = sn[tb][qb];
   }
 
+  GW_TRACE_AT(a, trow, 4, tid == 0);
+  GW_TRACE_AT(a, trow, 8 + w, lane == 0);
+
   // ---- write: lane holds query vector l16 of each block, dims 16 b + 4 gq .. +3
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -407,6 +400,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
 #pragma unroll
     for (int b = 0; b < 16; ++b) __builtin_nontemporal_store(acc[qb][b] * inv, reinterpret_cast<f32x4*>(op + 16 * b));
   }
+  GW_TRACE_AT(a, trow, 7, tid == 0);
 }
 
 }  // namespace

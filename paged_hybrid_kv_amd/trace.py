@@ -10,7 +10,14 @@ kernel, where a workgroup's time goes: start-up until its first pages are
 in, the page loop per unit of work, the tail after the loop, and the spread
 of workgroup starts and ends across the launch.
 
-    python -m paged_hybrid_kv_amd.trace [--big] [--dump rows.npz]
+    python -m paged_hybrid_kv_amd.trace [--big] [--prefill] [--dump rows.npz]
+
+With --prefill it times the prompt-row kernels instead, in one local and
+one global layer of the mixed step (4 new 512-token prompts) and of the
+chunked-prefill step (a 512-token chunk after a 3584-token prefix): per
+workgroup, the start-up until the first step's keys are in LDS, the cost of
+a step of the key loop (fitted over workgroups with different range
+lengths), the write-out, and when the workgroups start and end.
 
 It needs the GPU and the trace build; it changes nothing in the product
 library (libgw.so), which records nothing.
@@ -68,6 +75,71 @@ def summarize(name: str, rows: np.ndarray, unit_slot: int, unit_name: str, loop_
 HEADER = ("| launch | active WGs | units/WG (med) | last WG start (µs) | start-up: entry → slot 3 (med µs) | "
           "loop per unit (med µs) | loop (med µs) | tail: loop end → exit (med µs) | exit (med µs) | "
           "last exit (µs) | last exit per XCD 0..7 (µs) |\n|---|---|---|---|---|---|---|---|---|---|---|")
+
+
+PREFILL_HEADER = ("| launch | active WGs | steps/WG min / med / max | last WG start (µs) | start-up: entry → slot 3 "
+                  "(med µs) | µs per step (fit) | fixed µs (fit) | middle steps (med µs/step) | wave spread at loop "
+                  "end (med µs) | write-out: loop end → exit (med µs) | exit (med µs) | last exit (µs) |\n"
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|")
+
+
+def summarize_prefill(name: str, rows: np.ndarray) -> str:
+    """rows: the prompt-row kernel's trace rows (from kTracePrefillRow) of one launch."""
+    rows = rows.astype(np.int64)
+    a = rows[rows[:, 3] != 0]
+    t0 = rows[rows[:, 2] != 0, 2].min()
+    us = lambda x: (x - t0) * TICK_US
+    n = a[:, 1]
+    startup = (a[:, 3] - a[:, 2]) * TICK_US
+    loop = (a[:, 4] - a[:, 3]) * TICK_US
+    wall = (a[:, 4] - a[:, 2]) * TICK_US
+    slope, icpt = np.polyfit(n, wall, 1) if len(np.unique(n)) > 1 else (float("nan"), float("nan"))
+    mid = a[n >= 3]
+    mid_step = (mid[:, 6] - mid[:, 5]) * TICK_US / np.maximum(mid[:, 1] - 2, 1)
+    wend = a[:, 8:16]
+    spread = (wend.max(1) - wend[:, :8].min(1)) * TICK_US
+    tail = (a[:, 7] - a[:, 4]) * TICK_US
+    end = us(a[:, 7])
+    return (f"| {name} | {len(a)} | {n.min()} / {_med(n):.0f} / {n.max()} | {us(a[:, 2]).max():.2f} | "
+            f"{_med(startup):.2f} | {slope:.3f} | {icpt:.2f} | {_med(mid_step):.3f} | {_med(spread):.2f} | "
+            f"{_med(tail):.2f} | {_med(end):.2f} | {end.max():.2f} |")
+
+
+def run_prefill(dump: str | None = None) -> str:
+    import torch
+
+    L = load_trace_lib()
+    from .step import HybridStep
+    from .synth import HybridShape
+
+    buf = torch.zeros(SLOTS * 8192, dtype=torch.int64, device="cuda")
+    raw = {}
+    assert L.gw_trace_buffer(buf.data_ptr()) == 0
+    lines = ["Per-workgroup event times of the prompt-row kernels, one launch each (trace build), times from "
+             "the launch's first workgroup start.  A step is 32 tokens (two pages, local) or one page (global); "
+             "the per-step cost and the fixed cost are the least-squares line of entry-to-loop-end time against "
+             "the workgroup's step count; middle steps = iteration 1 to the last iteration's start.", "",
+             PREFILL_HEADER]
+    for prefix, label in ((0, "mixed step"), (3584, "chunked-prefill step")):
+        st = HybridStep(shape=HybridShape(prompt_prefix=prefix), with_prompts=True)
+        for _ in range(2):
+            st.run()
+        torch.cuda.synchronize()
+        loc = next(x for x in st.layers if x["local"])
+        glb = next(x for x in st.layers if not x["local"])
+        for kind, x in (("local", loc), ("global", glb)):
+            buf.zero_()
+            st.attend(x, append=True)
+            torch.cuda.synchronize()
+            rows = buf.view(-1, SLOTS).cpu().numpy().astype(np.uint64)[4096:]
+            raw[f"{kind}_prefill_{prefix}"] = rows
+            lines.append(summarize_prefill(f"{label}, layer {x['index']} {kind} prompt rows", rows))
+        del st
+        torch.cuda.empty_cache()
+    L.gw_trace_buffer(None)
+    if dump:
+        np.savez(dump, **raw)
+    return "\n".join(lines)
 
 
 def run(big: bool = False, layers: int = 4, dump: str | None = None) -> str:
@@ -144,4 +216,7 @@ def run(big: bool = False, layers: int = 4, dump: str | None = None) -> str:
 
 if __name__ == "__main__":
     dump = sys.argv[sys.argv.index("--dump") + 1] if "--dump" in sys.argv else None
-    print(run(big="--big" in sys.argv, dump=dump), flush=True)
+    if "--prefill" in sys.argv:
+        print(run_prefill(dump=dump), flush=True)
+    else:
+        print(run(big="--big" in sys.argv, dump=dump), flush=True)

@@ -141,10 +141,15 @@ def glob(d=None, q=FAKE, hq=32, kn=None, vn=None, cos=None, sin=None, indptr=Non
     (lambda: local(d=desc(rot=0), kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE), gw.GW_ERR_INVALID_ARG,
      "takes no rotary tables"),
     # grids past 2^31 - 1 workgroups are refused before any launch: the
-    # decode rows' (split, KV head, sequence) grid, and the prompt rows'
-    # (row block, KV head) grid
+    # decode rows' (split, KV head, sequence) grid ...
     (lambda: local(d=desc(heads=65535), hq=65535, S=65535, rows=65535, stride=512, wsb=1 << 62),
      gw.GW_ERR_UNSUPPORTED, "decode workgroups"),
+    # ... the same grid's workgroups past the decode items, which append the
+    # prompt rows' own tokens (page item x two KV heads)
+    (lambda: local(d=desc(heads=32768), hq=32768, S=4096, rows=2 ** 31 - 1, indptr=FAKE, mql=8192, win=1,
+                   kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE, ws=None, wsb=0),
+     gw.GW_ERR_UNSUPPORTED, "append workgroups"),
+    # ... and the prompt rows' (row block, KV head) grid
     (lambda: local(d=desc(heads=32768), hq=32768, S=65535, rows=2 ** 31 - 1, indptr=FAKE, mql=8192, win=1,
                    ws=None, wsb=0),
      gw.GW_ERR_UNSUPPORTED, "prompt-row workgroups"),
