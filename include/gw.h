@@ -79,7 +79,7 @@ typedef enum gw_kv_dtype {
  *   LOCAL:             page_size 16, head_dim 256, rot_dim 256 (or 0 = K is
  *                      stored as given), num_kv_heads >= 1, bf16 or e4m3.
  *   GLOBAL_COMPRESSED: page_size 16, head_dim 512, rot_dim 128, one KV head,
- *                      bf16 or e4m3 (e4m3: decode rows only).
+ *                      bf16 or e4m3.
  *   GLOBAL_FULL:       as GLOBAL_COMPRESSED.
  *
  * Element order inside a page (elements of kv_dtype):
@@ -259,8 +259,9 @@ int gw_decode_attn_local_noalloc(const gw_pool_desc* pool /* host */, const void
 
 /* Global family (GW_FAMILY_GLOBAL_COMPRESSED or GW_FAMILY_GLOBAL_FULL, bf16
  * or e4m3).  num_q_heads 16 or 32.  The two layouts give bit-identical
- * results.  An e4m3 pool is read as the exact bf16 values of its codes; it
- * serves decode rows only: max_q_len > 1 returns GW_ERR_UNSUPPORTED.
+ * results.  An e4m3 pool is read as the exact bf16 values of its codes, for
+ * decode and prompt rows alike; the rows' tokens appended in the call are
+ * stored as the codes gw_kv_append stores.
  * v_new: bf16 [num_rows][512], with the rotary tables fp32 [max_pos][64];
  * NULL when the pool already holds the rows.  k_new: bf16 [num_rows][512],
  * each row's K before rotation, of which only dims 0..127 are read (the

@@ -493,8 +493,6 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   if (num_q_heads != 16 && num_q_heads != 32)
     return fail(GW_ERR_UNSUPPORTED, fn, "num_q_heads %d (served: 16, 32)", num_q_heads);
   const bool fp8 = pool->kv_dtype == GW_KV_E4M3;
-  if (fp8 && max_q_len > 1)
-    return fail(GW_ERR_UNSUPPORTED, fn, "an e4m3 global pool serves decode rows only (max_q_len %d)", max_q_len);
   if ((rope_cos == nullptr) != (rope_sin == nullptr))
     return fail(GW_ERR_INVALID_ARG, fn, "rope_cos and rope_sin must both be set or both be null");
   if (v_new && !rope_cos) return fail(GW_ERR_INVALID_ARG, fn, "the global family needs rotary tables");
@@ -554,7 +552,7 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   if (max_q_len > 1) {
-    e = gw::launch_global_prefill(a, compressed, max_q_len, (hipStream_t)stream);
+    e = gw::launch_global_prefill(a, compressed, fp8, max_q_len, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ok();

@@ -293,12 +293,10 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   const int g = lane >> 4, l16 = lane & 15;
   // the workgroups past the decode items append the prompt rows' own
   // tokens, two units of 256 threads each (the prompt rows attend in a
-  // later launch; e4m3 pools serve decode rows only)
-  if constexpr (!FP8) {
-    if ((int)blockIdx.x >= a.append_wg0) {
-      global_rows_append_unit<COMPRESSED>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
-      return;
-    }
+  // later launch)
+  if ((int)blockIdx.x >= a.append_wg0) {
+    global_rows_append_unit<COMPRESSED, FP8>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
+    return;
   }
 
   GlobalItem it;
@@ -612,7 +610,7 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
   const int d_lo = HB == 2 ? 128 * (w >> 1) : 64 * w;   // output dims d_lo .. + 16 kBlocks
   // the workgroups past the decode items append the prompt rows' own tokens
   if ((int)blockIdx.x >= a.append_wg0) {
-    global_rows_append_unit<false>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
+    global_rows_append_unit<false, false>(a, ((int)blockIdx.x - a.append_wg0) * 2 + tid / 256, tid % 256);
     return;
   }
 
@@ -806,18 +804,24 @@ __global__ __launch_bounds__(512, 1) void global_decode_full_kernel(GlobalAttnAr
 // The scores half of the page for the prompt rows: S^T = K . Q^T per row
 // (16 steps over 512 dims, two accumulation chains, K read in batches of 4
 // fragments).
-template <bool COMPRESSED, int NR>
+template <bool COMPRESSED, bool FP8, int NR>
 __device__ __forceinline__ void global_rows_scores(f32x4 (&s)[NR][2], const uint8_t* pg, const bf16x8 (&qf)[NR][16],
                                                    int g, int l16) {
-  using PG = GlobalPage<COMPRESSED>;
+  using PG = GlobalPage<COMPRESSED, FP8>;
 #pragma unroll
   for (int r = 0; r < NR; ++r) s[r][0] = s[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int hk = 0; hk < 4; ++hk) {
     bf16x8 kf[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (4 * hk + k) + g, l16));
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (FP8) {   // e4m3 codes widen to bf16 exactly
+        const i32x2 kr = *reinterpret_cast<const i32x2*>(pg + PG::k_off(4 * (4 * hk + k) + g, l16));
+        kf[k] = widen_e4m3x8((uint32_t)kr[0], (uint32_t)kr[1]);
+      } else {
+        kf[k] = *reinterpret_cast<const bf16x8*>(pg + PG::k_off(4 * (4 * hk + k) + g, l16));
+      }
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -831,10 +835,11 @@ __device__ __forceinline__ void global_rows_scores(f32x4 (&s)[NR][2], const uint
 // and V fragment it reads from LDS feeds NR rows' products.  Per page:
 // the scores (global_rows_scores, issued a page ahead), the lazy
 // online-softmax update per row, then O^T += V^T . P^T over 32 output
-// blocks of 16 dims (V read in batches of 4 blocks).  V of tokens past p_v
-// (slots past the workgroup's last row, possibly never written) is zeroed
-// in the operand registers.
-template <bool COMPRESSED, int NR>
+// blocks of 16 dims (V read in batches of 4 blocks; an e4m3 page's
+// transposing read gives the operands of two blocks, widened exactly).  V
+// of tokens past p_v (slots past the workgroup's last row, possibly never
+// written) is zeroed in the operand registers.
+template <bool COMPRESSED, bool FP8, int NR>
 __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m_run)[NR], float (&l_run)[NR],
                                                  const uint8_t* pg, const f32x4 (&s)[NR][2], int tok_page0,
                                                  const int (&p)[NR], int p_v, int g, int l16, int v_lane_off,
@@ -872,9 +877,18 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     uint2 vf[4];
+    if constexpr (FP8) {   // blocks 2j, 2j + 1 per read, 512 bytes per pair of 16-dim chunks
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * (4 * bb + b))));
+      for (int h = 0; h < 2; ++h) {
+        const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 512 * (2 * bb + h)));
+        vf[2 * h] = uint2{e4m3x2_to_bf16x2<false>((uint32_t)r[0]), e4m3x2_to_bf16x2<true>((uint32_t)r[0])};
+        vf[2 * h + 1] = uint2{e4m3x2_to_bf16x2<false>((uint32_t)r[1]), e4m3x2_to_bf16x2<true>((uint32_t)r[1])};
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        vf[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 512 * (4 * bb + b))));
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -901,9 +915,9 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
 // sequence, row group), numbered compactly level by level (every
 // sequence's last group first, then every sequence's second last, ...: the
 // longest ranges of the call first).
-template <bool COMPRESSED, int HB, int NR, int NS>
+template <bool COMPRESSED, bool FP8, int HB, int NR, int NS>
 __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(GlobalAttnArgs a) {
-  using PG = GlobalPage<COMPRESSED>;
+  using PG = GlobalPage<COMPRESSED, FP8>;
   constexpr int kW = 8 / NR;                  // waves
   constexpr int kUnits = PG::kBytes / 1024;
   constexpr int kPerWave = kUnits / kW;       // units per wave per page ...
@@ -996,7 +1010,11 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
     m_run[i] = -INFINITY;
     l_run[i] = 0.f;
   }
-  const int v_lane_off = global_v_lane_off<COMPRESSED>(0, g, l16);
+  // V^T read offset of block 0 (bf16: the tr16 lane offset; e4m3: the tr8
+  // row r = l16 / 2 names token 4g + r % 4 of 16-dim chunk r / 4 (blocks 0
+  // and 1), half l16 % 2 of its 16 dims)
+  const int v_lane_off = FP8 ? PG::kVOff + ((((l16 >> 1) >> 2) * 16 + 4 * g + ((l16 >> 1) & 3)) * 16) + 8 * (l16 & 1)
+                             : global_v_lane_off<COMPRESSED>(0, g, l16);
 
   // software pipeline, one page deep: iteration i has pages i and i + 1 in
   // LDS; page i + 1's scores go out beside page i's weights and products
@@ -1005,7 +1023,7 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   lds_barrier();
   GW_TRACE_AT(a, trow, 3, tid == 0);
   f32x4 sc[NR][2];
-  global_rows_scores<COMPRESSED, NR>(sc, ring[0], qf, g, l16);
+  global_rows_scores<COMPRESSED, FP8, NR>(sc, ring[0], qf, g, l16);
   for (int i = 0; i < n; ++i) {
     if (nu > kPerWave) wait_groups_after<kPerWave + 1>(max(0, min(NS - 3, n - 2 - i)));
     else wait_groups_after<kPerWave>(max(0, min(NS - 3, n - 2 - i)));
@@ -1014,8 +1032,8 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
     GW_TRACE_AT(a, trow, 6, tid == 0 && i == n - 1);
     if (i + NS - 1 < n) issue_page(i + NS - 1);
     f32x4 sn[NR][2];
-    global_rows_scores<COMPRESSED, NR>(sn, ring[min(i + 1, n - 1) % NS], qf, g, l16);
-    global_rows_page<COMPRESSED, NR>(acc, m_run, l_run, ring[i % NS], sc, i * 16, pr, p_last, g, l16, v_lane_off,
+    global_rows_scores<COMPRESSED, FP8, NR>(sn, ring[min(i + 1, n - 1) % NS], qf, g, l16);
+    global_rows_page<COMPRESSED, FP8, NR>(acc, m_run, l_run, ring[i % NS], sc, i * 16, pr, p_last, g, l16, v_lane_off,
                                      a.scale_log2);
 #pragma unroll
     for (int r = 0; r < NR; ++r) { sc[r][0] = sn[r][0]; sc[r][1] = sn[r][1]; }
@@ -1106,7 +1124,7 @@ hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t st
 hipError_t launch_global_decode(const GlobalAttnArgs& a_in, bool compressed, bool fp8, hipStream_t stream) {
   // the decode items, then the prompt rows' append units (two per workgroup)
   const int64_t n_dec = (int64_t)a_in.max_splits * a_in.num_seqs;
-  const int64_t n = n_dec + (fp8 ? 0 : (a_in.append_units + 1) / 2);
+  const int64_t n = n_dec + (a_in.append_units + 1) / 2;
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
   GlobalAttnArgs a = a_in;
   a.append_wg0 = (int32_t)n_dec;
@@ -1131,7 +1149,8 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a_in, bool compressed, boo
   return hipGetLastError();
 }
 
-hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream) {
+hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, bool fp8, int max_q_len,
+                                 hipStream_t stream) {
   // one workgroup per (prompt sequence, group of 8 / HB rows); the entry
   // point has checked that the count fits a grid
   const bool h32 = a.num_q_heads == 32;
@@ -1139,14 +1158,16 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int m
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)items), block(512);
-  if (compressed) {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<true, 2, 1, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<true, 1, 1, 4>), grid, block, 0, stream, a);
-  } else {
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<false, 2, 1, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((global_prefill_kernel<false, 1, 1, 4>), grid, block, 0, stream, a);
+#define GW_GPREFILL_CASE(C_, F_)                                                                      \
+  if (compressed == C_ && fp8 == F_) {                                                                \
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 2, 1, 4>), grid, block, 0, stream, a); \
+    else hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 1, 1, 4>), grid, block, 0, stream, a);     \
+    return hipGetLastError();                                                                         \
   }
-  return hipGetLastError();
+  GW_GPREFILL_CASE(true, false) GW_GPREFILL_CASE(false, false) GW_GPREFILL_CASE(true, true)
+  GW_GPREFILL_CASE(false, true)
+#undef GW_GPREFILL_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gw

@@ -113,7 +113,8 @@ hipError_t launch_local_decode(const LocalAttnArgs& a, int group, bool fp8, hipS
 hipError_t launch_global_decode(const GlobalAttnArgs& a, bool compressed, bool fp8, hipStream_t stream);
 hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int max_q_len,
                                 hipStream_t stream);
-hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, int max_q_len, hipStream_t stream);
+hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, bool fp8, int max_q_len,
+                                 hipStream_t stream);
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_append_local(const AppendArgs& a, bool fp8, bool rope, hipStream_t stream);
 // Rows mode (seq_lens set): one workgroup per (sequence, page of its rows).

@@ -226,12 +226,24 @@ __device__ __forceinline__ void append_local_rows_page(const AppendArgs& a, int 
 // holds dims 8c .. 8c+7 of slot t; K_rot units (c, t) and (c + 8, t), c < 8,
 // hold the rotation of V's chunks c and c + 8 (pairs (i, i + 64)); the full
 // record's K block repeats V's chunks 16 .. 63.
-// Page item `item` by 256 threads (tid 0 .. 255).
-template <bool COMPRESSED>
+// Page item `item` by 256 threads (tid 0 .. 255).  An e4m3 page takes the
+// per-token record of the single-token append (global_record_lane, then
+// put_global_record_e4m3), one token per wave at a time.
+template <bool COMPRESSED, bool FP8>
 __device__ __forceinline__ void append_global_rows_page(const AppendArgs& a, int item, int tid) {
   RowsPage rp;
   if (!rows_page(a, item, tid & 63, rp)) return;
   uint8_t* pb = a.pool + (int64_t)rp.page * a.page_bytes;
+  if constexpr (FP8) {
+    const int w = tid >> 6, l = tid & 63;
+    for (int t = rp.t0 + w; t <= rp.t1; t += 4) {
+      const uint16_t* vr = a.v + (int64_t)(rp.r0 + rp.pg * kPage + t - rp.p0) * 512;
+      const uint16_t* kr = a.k_raw ? a.k_raw + (vr - a.v) : vr;   // the same row of k_raw
+      const GlobalRecordLane r = global_record_lane(vr, kr, a.rope_cos, a.rope_sin, rp.pg * kPage + t, l);
+      put_global_record_e4m3<COMPRESSED>(pb, r, t, l);
+    }
+    return;
+  }
   uint8_t* vblock = COMPRESSED ? pb : pb + 16384;
   uint8_t* kblock = COMPRESSED ? pb + 16384 : pb;
   auto row_v = [&](int t) __attribute__((always_inline)) {
@@ -312,10 +324,10 @@ __device__ __forceinline__ void local_rows_append_unit(const LocalAttnArgs& a, i
 }
 
 // Append unit u (one page item) of a global call, by 256 threads.
-template <bool COMPRESSED>
+template <bool COMPRESSED, bool FP8>
 __device__ __forceinline__ void global_rows_append_unit(const GlobalAttnArgs& a, int u, int tid) {
   if (u >= a.append_units) return;
-  append_global_rows_page<COMPRESSED>(rows_append_args(a), u, tid);
+  append_global_rows_page<COMPRESSED, FP8>(rows_append_args(a), u, tid);
 }
 
 }  // namespace gw

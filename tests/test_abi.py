@@ -165,8 +165,6 @@ def test_local_rejects(call, code, frag):
 @pytest.mark.parametrize("call,code,frag", [
     (lambda: glob(hq=8), gw.GW_ERR_UNSUPPORTED, "num_q_heads"),
     (lambda: glob(d=desc()), gw.GW_ERR_INVALID_ARG, "not a global family"),
-    (lambda: glob(d=desc(gw.GW_FAMILY_GLOBAL_COMPRESSED, dt=gw.GW_KV_E4M3), mql=2, indptr=FAKE),
-     gw.GW_ERR_UNSUPPORTED, "decode rows only"),
     (lambda: glob(wsb=0), gw.GW_ERR_WORKSPACE, "workspace"),
     (lambda: glob(msl=0), gw.GW_ERR_INVALID_ARG, "max_seq_len"),
     (lambda: glob(vn=FAKE), gw.GW_ERR_INVALID_ARG, "rotary tables"),

@@ -156,23 +156,25 @@ def test_local_in_call_append_mixed(fp8):
 
 
 # ----------------------------------------------------------------- global --
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("hq", [16, 32])
-def test_global_prompt_rows_mixed(hq):
+def test_global_prompt_rows_mixed(hq, fp8):
     lens = [700, 300, 33, 4100, 2]
     q_len = [300, 1, 33, 1, 2]
-    case = SY.global_case("prefill global", 100 + hq, lens, num_q_heads=hq, q_len=q_len, rope=True)
+    case = SY.global_case("prefill global", 100 + hq, lens, num_q_heads=hq, q_len=q_len, rope=True, fp8=fp8)
     _, oc = run_global(case, True)
     _, of = run_global(case, False)
     assert np.array_equal(oc, of), "compressed and full records differ"
-    mx = check(case, oc, f"global prompt rows hq={hq}")
-    print(f"global prompt rows hq={hq}: max abs err {mx:.2e}", flush=True)
+    mx = check(case, oc, f"global prompt rows hq={hq} fp8={fp8}")
+    print(f"global prompt rows hq={hq} fp8={fp8}: max abs err {mx:.2e}", flush=True)
 
 
-def test_global_prompt_dominant_keys():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_global_prompt_dominant_keys(fp8):
     L = 100
     probes = [0, 15, 16, 31, 50, 99]
     case = SY.global_case("prefill global dominant", 110, [L] * len(probes), num_q_heads=32,
-                          q_len=[L] * len(probes), rope=False)
+                          q_len=[L] * len(probes), rope=False, fp8=fp8)
     u = case.q[0, 0].copy()
     case.q[:] = u
     for s, j in enumerate(probes):
@@ -187,13 +189,14 @@ def test_global_prompt_dominant_keys():
             for r in range(j, L):
                 assert np.array_equal(got[r, 0], want) and np.array_equal(got[r, 31], want), \
                     f"probe j*={j} row {r}"
-        check(case, out, f"global dominant compressed={compressed}")
+        check(case, out, f"global dominant compressed={compressed} fp8={fp8}")
 
 
-def test_global_in_call_append_mixed():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_global_in_call_append_mixed(fp8):
     lens = [300, 45, 2000, 30]
     q_len = [1, 45, 1, 13]
-    case = SY.global_case("global append mixed", 115, lens, q_len=q_len, rope=True)
+    case = SY.global_case("global append mixed", 115, lens, q_len=q_len, rope=True, fp8=fp8)
     for compressed in (True, False):
         dc_sep = RT.upload_global(case, compressed=compressed)
         out_sep = RT.attend(dc_sep).cpu().numpy()
@@ -267,9 +270,10 @@ def test_local_many_sequences_in_call_append():
     assert np.array_equal(out_f, out_sep)
 
 
-def test_global_many_sequences_in_call_append():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_global_many_sequences_in_call_append(fp8):
     lens, q_len = _many_seqs(130, max_len=400)
-    case = SY.global_case("many global", 131, lens, num_q_heads=16, q_len=q_len, rope=True)
+    case = SY.global_case("many global", 131, lens, num_q_heads=16, q_len=q_len, rope=True, fp8=fp8)
     dc_sep, out_sep = run_global(case)
     check(case, out_sep, "many global")
     is_row = np.zeros(case.tok_seq.shape[0], bool)
