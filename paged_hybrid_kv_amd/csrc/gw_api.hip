@@ -504,7 +504,9 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups and %lld append workgroups (served: up to %lld)",
                 (long long)w.max_splits * num_seqs, (app_units + 1) / 2, kMaxGrid);
   if (max_q_len > 1) {
-    const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads));
+    // the prompt rows' items, then the decode rows' reduce (two units of 256 threads per workgroup)
+    const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads)) +
+                              (w.max_splits > 1 ? ((long long)num_seqs * (num_q_heads / 16 * 32 / 4) + 1) / 2 : 0);
     if (pre_wgs > kMaxGrid)
       return fail(GW_ERR_UNSUPPORTED, fn, "%lld prompt-row workgroups (served: up to %lld)", pre_wgs, kMaxGrid);
   }
@@ -543,16 +545,16 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
   const bool compressed = pool->family == GW_FAMILY_GLOBAL_COMPRESSED;
   hipError_t e;
   // the decode rows (each appending its own token) and the prompt rows'
-  // append in one launch; the prompt rows attend after the reduce
+  // append in one launch; then the prompt rows' attention and the decode
+  // rows' cross-split reduce in one launch, or the reduce alone
   e = gw::launch_global_decode(a, compressed, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(fn, e);
-  if (w.max_splits > 1) {
-    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, w.max_splits};
-    e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
   if (max_q_len > 1) {
     e = gw::launch_global_prefill(a, compressed, fp8, max_q_len, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  } else if (w.max_splits > 1) {
+    gw::ReduceArgs r{q_indptr, seq_lens, a.part_acc, a.part_ml, out, num_q_heads, w.max_splits};
+    e = gw::launch_split_reduce(r, num_seqs, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ok();

@@ -903,6 +903,75 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
   }
 }
 
+// Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
+// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  The
+// partials sit in MFMA fragment order (fragment (hb, block) of a split: 64
+// lanes x 4 floats, lane g*16 + l16 holding head 16 hb + l16, dims
+// 16 block + 4g .. +3), so each wave of the reduce takes one fragment of a
+// sequence and every load moves 1 KiB in one piece.  A thread merges its
+// lane's splits in chunks of kReduceChunk (one round trip per chunk; a
+// later chunk with a larger max rescales what came before).
+constexpr int kReduceChunk = 16;
+
+// Sequence s, fragments 4y .. 4y + 3, by 256 threads (tid 0 .. 255).
+__device__ __forceinline__ void global_split_reduce_unit(const ReduceArgs& a, int s, int y, int tid) {
+  const int lane = tid & 63;
+  const int frag = y * 4 + (tid >> 6);   // hb * 32 + block
+  const int hbs = a.num_q_heads / 16;
+  if (frag >= hbs * 32) return;
+  int row = s;
+  if (a.q_indptr) {
+    row = a.q_indptr[s];
+    if (a.q_indptr[s + 1] - row != 1) return;
+  }
+  const int nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
+  if (nsplit <= 1) return;
+  const int head = 16 * (frag >> 5) + (lane & 15);
+  const f32x4* pa = reinterpret_cast<const f32x4*>(a.part_acc) + ((int64_t)s * a.max_splits * hbs * 32 + frag) * 64 + lane;
+  const float* ml = a.part_ml + ((int64_t)s * a.max_splits * a.num_q_heads + head) * 2;
+  const int64_t acc_step = (int64_t)hbs * 32 * 64, ml_step = 2 * (int64_t)a.num_q_heads;
+  float M = -INFINITY, lsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk) {
+    const int nc = min(kReduceChunk, nsplit - c0);
+    f32x4 v[kReduceChunk];
+    float2 x[kReduceChunk];
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i) {
+      v[i] = i < nc ? pa[(c0 + i) * acc_step] : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[i] = i < nc ? *reinterpret_cast<const float2*>(ml + (c0 + i) * ml_step) : float2{-INFINITY, 0.f};
+    }
+    float mc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i) mc = fmaxf(mc, x[i].x);
+    const float mnew = fmaxf(M, mc);
+    if (mnew > M) {
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      o *= r;
+      lsum *= r;
+      M = mnew;
+    }
+#pragma unroll
+    for (int i = 0; i < kReduceChunk; ++i) {
+      if (i < nc) {
+        const float w = __builtin_amdgcn_exp2f(x[i].x - M);
+        lsum += x[i].y * w;
+        o += v[i] * w;
+      }
+    }
+  }
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + head) * kGD + 16 * (frag & 31) + 4 * (lane >> 4)) =
+      o / lsum;
+}
+
+// Fragment groups per sequence: 32 fragments per head block, four per unit.
+__host__ __device__ constexpr int reduce_groups(int num_q_heads) { return num_q_heads / 16 * 32 / 4; }
+
+__global__ __launch_bounds__(256) void global_split_reduce_kernel(ReduceArgs a) {
+  global_split_reduce_unit(a, blockIdx.x, blockIdx.y, threadIdx.x);
+}
+
+
 // Prompt rows (sequences with more than one query row: a new prompt's
 // rows, or a chunk of one after a cached prefix, computed in the same step
 // as the decode rows -- pegainfer "Gemma 4" page, Scheduling).  Row r of
@@ -934,6 +1003,18 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   // loop done
   const int trow = kTracePrefillRow + (int)blockIdx.x;
   GW_TRACE_AT(a, trow, 2, tid == 0);
+  // the workgroups past the prompt-row items merge the decode rows' splits
+  // (the decode kernel, an earlier launch, wrote them), two units of 256
+  // threads each
+  if ((int)blockIdx.x >= a.reduce_wg0) {
+    const int u = ((int)blockIdx.x - a.reduce_wg0) * 2 + tid / 256;
+    const int groups = reduce_groups(a.num_q_heads);
+    if (u < a.num_seqs * groups) {
+      const ReduceArgs r{a.q_indptr, a.seq_lens, a.part_acc, a.part_ml, a.out, a.num_q_heads, a.max_splits};
+      global_split_reduce_unit(r, u / groups, u % groups, tid % 256);
+    }
+    return;
+  }
   const int wv = uniform_i32(tid >> 6);
   const int hb = HB == 2 ? (wv & 1) : 0;
   const int rp = HB == 2 ? (wv >> 1) : wv;
@@ -1053,70 +1134,10 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   GW_TRACE_AT(a, trow, 7, tid == 0);
 }
 
-// Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
-// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  The
-// partials sit in MFMA fragment order (fragment (hb, block) of a split: 64
-// lanes x 4 floats, lane g*16 + l16 holding head 16 hb + l16, dims
-// 16 block + 4g .. +3), so each wave of the reduce takes one fragment of a
-// sequence and every load moves 1 KiB in one piece.  A thread merges its
-// lane's splits in chunks of kReduceChunk (one round trip per chunk; a
-// later chunk with a larger max rescales what came before).
-constexpr int kReduceChunk = 16;
-
-__global__ __launch_bounds__(256) void global_split_reduce_kernel(ReduceArgs a) {
-  const int s = blockIdx.x, lane = threadIdx.x & 63;
-  const int frag = blockIdx.y * 4 + (threadIdx.x >> 6);   // hb * 32 + block
-  const int hbs = a.num_q_heads / 16;
-  if (frag >= hbs * 32) return;
-  int row = s;
-  if (a.q_indptr) {
-    row = a.q_indptr[s];
-    if (a.q_indptr[s + 1] - row != 1) return;
-  }
-  const int nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
-  if (nsplit <= 1) return;
-  const int head = 16 * (frag >> 5) + (lane & 15);
-  const f32x4* pa = reinterpret_cast<const f32x4*>(a.part_acc) + ((int64_t)s * a.max_splits * hbs * 32 + frag) * 64 + lane;
-  const float* ml = a.part_ml + ((int64_t)s * a.max_splits * a.num_q_heads + head) * 2;
-  const int64_t acc_step = (int64_t)hbs * 32 * 64, ml_step = 2 * (int64_t)a.num_q_heads;
-  float M = -INFINITY, lsum = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk) {
-    const int nc = min(kReduceChunk, nsplit - c0);
-    f32x4 v[kReduceChunk];
-    float2 x[kReduceChunk];
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) {
-      v[i] = i < nc ? pa[(c0 + i) * acc_step] : f32x4{0.f, 0.f, 0.f, 0.f};
-      x[i] = i < nc ? *reinterpret_cast<const float2*>(ml + (c0 + i) * ml_step) : float2{-INFINITY, 0.f};
-    }
-    float mc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) mc = fmaxf(mc, x[i].x);
-    const float mnew = fmaxf(M, mc);
-    if (mnew > M) {
-      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
-      o *= r;
-      lsum *= r;
-      M = mnew;
-    }
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) {
-      if (i < nc) {
-        const float w = __builtin_amdgcn_exp2f(x[i].x - M);
-        lsum += x[i].y * w;
-        o += v[i] * w;
-      }
-    }
-  }
-  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + head) * kGD + 16 * (frag & 31) + 4 * (lane >> 4)) =
-      o / lsum;
-}
-
 }  // namespace
 
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs, a.num_q_heads / 16 * 32 / 4), block(256);
+  dim3 grid(num_seqs, reduce_groups(a.num_q_heads)), block(256);
   hipLaunchKernelGGL(global_split_reduce_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
@@ -1149,15 +1170,22 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a_in, bool compressed, boo
   return hipGetLastError();
 }
 
-hipError_t launch_global_prefill(const GlobalAttnArgs& a, bool compressed, bool fp8, int max_q_len,
+hipError_t launch_global_prefill(const GlobalAttnArgs& a_in, bool compressed, bool fp8, int max_q_len,
                                  hipStream_t stream) {
-  // one workgroup per (prompt sequence, group of 8 / HB rows); the entry
-  // point has checked that the count fits a grid
-  const bool h32 = a.num_q_heads == 32;
-  const long long items = prefill_items(a.num_rows, a.num_seqs, max_q_len, global_prefill_rows(a.num_q_heads));
-  if (items == 0) return hipSuccess;
-  if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)items), block(512);
+  // one workgroup per (prompt sequence, group of 8 / HB rows) (the entry
+  // point has checked that the count fits a grid), then the decode rows'
+  // cross-split reduce (two units of 256 threads per workgroup) when the
+  // decode rows have splits
+  const bool h32 = a_in.num_q_heads == 32;
+  const long long items =
+      prefill_items(a_in.num_rows, a_in.num_seqs, max_q_len, global_prefill_rows(a_in.num_q_heads));
+  const long long n_red =
+      a_in.max_splits > 1 ? ((long long)a_in.num_seqs * reduce_groups(a_in.num_q_heads) + 1) / 2 : 0;
+  if (items + n_red == 0) return hipSuccess;
+  if (items + n_red > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GlobalAttnArgs a = a_in;
+  a.reduce_wg0 = (int32_t)items;
+  dim3 grid((unsigned)(items + n_red)), block(512);
 #define GW_GPREFILL_CASE(C_, F_)                                                                      \
   if (compressed == C_ && fp8 == F_) {                                                                \
     if (h32) hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 2, 1, 4>), grid, block, 0, stream, a); \
