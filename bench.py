@@ -55,7 +55,7 @@ def time_events(fn, iters):
 
 
 COUNTER_FILE = os.path.join(ROOT, "profiles", "local_decode_hbm_counters.json")
-LOCAL_KERNEL_SOURCES = ["gw_local.hip", "gw_device.h", "gw_plan.h", "gw_kernels.h"]
+LOCAL_KERNEL_SOURCES = ["gw_local.hip", "gw_device.h", "gw_plan.h", "gw_kernels.h", "gw_rows_append.h"]
 
 
 def local_kernel_hash():
