@@ -17,7 +17,8 @@ The mixed step (the same plus 4 new 512-token prompts whose causal rows are
 computed in the same step) is reported beside it, and so is the same step
 with the prompt rows as a 512-token chunk after a cached 3584-token prefix
 (chunked prefill: every row attends a full local window and 3585..4096
-global keys).
+global keys), and the decode step with e4m3 pools: the local family's only
+(the opt-in fp8 pool of pegainfer PR #1012) and both families'.
 
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
@@ -368,6 +369,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-rounds", type=int, default=10)
     ap.add_argument("--no-mixed", action="store_true", help="skip the step with prompt rows")
+    ap.add_argument("--no-e4m3-steps", action="store_true", help="skip the decode step with e4m3 pools")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the local bf16, global tied and local e4m3 workloads at full size")
     ap.add_argument("--copy-calib", action="store_true",
@@ -443,6 +445,35 @@ def main():
             else:
                 chunked = r
 
+    def e4m3_decode_step(local_dt, global_dt, label):
+        """The headline step with e4m3 pools (pegainfer PR #1012, Verification:
+        the opt-in fp8 local pool measured against bf16 at the same
+        concurrency): its time, tok/s and the bytes its pools hold."""
+        st2 = HybridStep(with_prompts=False, local_kv_dtype=local_dt, global_kv_dtype=global_dt)
+        if not args.no_graph:
+            st2.capture()
+        for _ in range(args.warmup):
+            st2.replay()
+        ems = time_events(st2.replay, args.steps)
+        kvb = st2.decode_kv_bytes()
+        res = {"ms_per_step": round(ems, 4), "decode_tok_s": round(st2.shape.decode_slots / (ems * 1e-3), 1),
+               "decode_kv_bytes_per_step": kvb, "GB_per_s": round(kvb / (ems * 1e-3) / 1e9, 1),
+               "pct_of_peak": round(kvb / (ems * 1e-3) / PEAK_HBM * 100, 2),
+               "speedup_vs_bf16_step": round(ms / ems, 3)}
+        log(f"{label}: {ems:.3f} ms, {res['decode_tok_s']} tok/s ({res['speedup_vs_bf16_step']}x the bf16 step), "
+            f"{res['GB_per_s']} GB/s of e4m3 KV")
+        del st2
+        torch.cuda.empty_cache()
+        return res
+
+    e4m3_steps = None
+    if not args.no_e4m3_steps:
+        e4m3_steps = {
+            "local_e4m3": e4m3_decode_step(gw.GW_KV_E4M3, gw.GW_KV_BF16, "decode step, local pools e4m3"),
+            "local_and_global_e4m3": e4m3_decode_step(gw.GW_KV_E4M3, gw.GW_KV_E4M3,
+                                                      "decode step, both families' pools e4m3"),
+        }
+
     if args.copy_calib:
         copy_calibration()
 
@@ -471,6 +502,7 @@ def main():
         "roofline": roof,
         "mixed_step": mixed,
         "chunked_prefill_step": chunked,
+        "decode_step_e4m3": e4m3_steps,
         "cpu_baseline": cpu,
     }
     if configs is not None:

@@ -22,10 +22,13 @@ from .synth import HybridShape, make_page_table, layer_draws, step_tokens, PAGE
 
 class HybridStep:
     def __init__(self, shape: HybridShape | None = None, with_prompts: bool = True, device="cuda",
-                 fill_context: bool = True):
+                 fill_context: bool = True, local_kv_dtype: int = gw.GW_KV_BF16,
+                 global_kv_dtype: int = gw.GW_KV_BF16):
         self.shape = sh = shape or HybridShape()
         self.with_prompts = with_prompts
         self.device = device
+        # store type of each family's pools (bf16, or e4m3: PR #1012's opt-in fp8 pool)
+        self.local_kv_dtype, self.global_kv_dtype = local_kv_dtype, global_kv_dtype
         lens = sh.lens(with_prompts)
         q_len = sh.q_len(with_prompts)
         self.lens, self.q_len = lens, q_len
@@ -78,12 +81,12 @@ class HybridStep:
         local = not sh.is_global(l)
         d = layer_draws(sh, l, self.with_prompts, self.device)
         if local:
-            pool = Pool(gw.GW_FAMILY_LOCAL, gw.GW_KV_BF16, self.local_seqs.num_pages,
+            pool = Pool(gw.GW_FAMILY_LOCAL, self.local_kv_dtype, self.local_seqs.num_pages,
                         sh.local_kv_heads, 256, self.device)
             pt, stride = self.local_pt, self.local_seqs.page_table.shape[1]
             cos, sin = self.local_cos, self.local_sin
         else:
-            pool = Pool(gw.GW_FAMILY_GLOBAL_COMPRESSED, gw.GW_KV_BF16, self.global_seqs.num_pages,
+            pool = Pool(gw.GW_FAMILY_GLOBAL_COMPRESSED, self.global_kv_dtype, self.global_seqs.num_pages,
                         1, 128, self.device)
             pt, stride = self.global_pt, self.global_seqs.page_table.shape[1]
             cos, sin = self.global_cos, self.global_sin
@@ -154,12 +157,15 @@ class HybridStep:
             self.graph.replay()
 
     # ------------------------------------------------------------ accounting
+    def _esize(self, local: bool) -> int:
+        return 1 if (self.local_kv_dtype if local else self.global_kv_dtype) == gw.GW_KV_E4M3 else 2
+
     def decode_kv_bytes(self) -> int:
         """Algorithmic KV bytes the decode rows read in one step."""
         sh = self.shape
         dec = sh.decode_lens
-        local = sum(min(int(L), sh.window) for L in dec) * sh.local_kv_heads * 256 * 2 * 2
-        glob = sum(int(L) for L in dec) * (512 + 128) * 2
+        local = sum(min(int(L), sh.window) for L in dec) * sh.local_kv_heads * 256 * 2 * self._esize(True)
+        glob = sum(int(L) for L in dec) * (512 + 128) * self._esize(False)
         n_glob = sum(1 for l in range(sh.num_layers) if sh.is_global(l))
         return (sh.num_layers - n_glob) * local + n_glob * glob
 
@@ -171,8 +177,9 @@ class HybridStep:
         sh = self.shape
         n_glob = sum(1 for l in range(sh.num_layers) if sh.is_global(l))
         n_loc = sh.num_layers - n_glob
-        loc_tok = sh.local_kv_heads * 256 * 2 * 2            # K + V bf16, all KV heads
-        glob_tok = (512 + 128) * 2                          # compressed record
+        loc_raw = sh.local_kv_heads * 256 * 2 * 2            # the step's raw K + V (bf16), all KV heads
+        loc_tok = sh.local_kv_heads * 256 * 2 * self._esize(True)   # K + V as the pool stores them
+        glob_tok = (512 + 128) * self._esize(False)                 # compressed record
         prompts = [int(x) for x in self.q_len[sh.decode_slots:]]
         pre_tok = sum(prompts)
         new_tok = sh.decode_slots + pre_tok
@@ -182,7 +189,7 @@ class HybridStep:
         loc_rng = sum(P + n - max(0, P - sh.window + 1) for n in prompts)
         glob_rng = sum(P + n for n in prompts)
         kv = self.decode_kv_bytes() + n_loc * loc_rng * loc_tok + n_glob * glob_rng * glob_tok
-        app = (n_loc * new_tok * (loc_tok + loc_tok) + n_glob * new_tok * (512 * 2 + glob_tok))
+        app = (n_loc * new_tok * (loc_raw + loc_tok) + n_glob * new_tok * (512 * 2 + glob_tok))
         rows = self.rows
         qo = (n_loc * rows * sh.local_q_heads * 256 * (2 + 4) + n_glob * rows * sh.global_q_heads * 512 * (2 + 4))
         return {"kv_read": kv, "append": app, "q_out": qo, "total": kv + app + qo}
@@ -204,4 +211,5 @@ class HybridStep:
 
     def local_decode_kv_bytes_per_layer(self) -> int:
         sh = self.shape
-        return sum(min(int(L), sh.window) for L in sh.decode_lens) * sh.local_kv_heads * 256 * 2 * 2
+        return (sum(min(int(L), sh.window) for L in sh.decode_lens) * sh.local_kv_heads * 256 * 2 *
+                self._esize(True))

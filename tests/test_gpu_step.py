@@ -9,7 +9,9 @@ slots with seeded contexts in [2048, 8192], one row each, no q_indptr), the
 mixed step with 4 new 512-token prompts (pegainfer "Gemma 4" page,
 Scheduling: prompt rows share the step with the decode rows), and the same
 step with the prompt rows as a 512-token chunk after a cached 3584-token
-prefix (chunked prefill against cached context).  The oracle sees only the
+prefix (chunked prefill against cached context); the decode and the mixed
+step also with both families' pools in e4m3 (the oracle then takes the
+e4m3 code of every stored element).  The oracle sees only the
 seeded draws of the layer (q, the step's new K/V and the prior context K/V,
 all bf16) and rotates and rounds them itself; no value comes from the GPU
 path.  Every decode row is compared, and a sample of prompt rows (first,
@@ -70,6 +72,11 @@ def _sequence_kv(st, layer: int, s: int, host):
         v = v[:, None, :]
         K = np.full((L, 1, 512), np.nan)
         V = np.full((L, 1, 512), np.nan)
+    from paged_hybrid_kv_amd import gw
+    if (st.local_kv_dtype if local else st.global_kv_dtype) == gw.GW_KV_E4M3:
+        # an e4m3 pool holds the e4m3 code of every stored bf16 element
+        k = OC.e4m3_decode(OC.e4m3_encode(k))
+        v = OC.e4m3_decode(OC.e4m3_encode(v))
     K[pos] = k
     V[pos] = v
     indptr = np.concatenate([[0], np.cumsum(st.q_len)])
@@ -100,10 +107,12 @@ def _check_layer(st, layer: int, out):
     return worst
 
 
-def _run_and_check(shape, label, with_prompts=True):
+def _run_and_check(shape, label, with_prompts=True, e4m3=False):
     import torch
+    from paged_hybrid_kv_amd import gw
     from paged_hybrid_kv_amd.step import HybridStep
-    st = HybridStep(shape=shape, with_prompts=with_prompts)
+    dt = gw.GW_KV_E4M3 if e4m3 else gw.GW_KV_BF16
+    st = HybridStep(shape=shape, with_prompts=with_prompts, local_kv_dtype=dt, global_kv_dtype=dt)
     st.capture()
     for _ in range(2):
         st.replay()
@@ -133,3 +142,13 @@ def test_hybrid_step_chunked_prefill_sampled_parity():
     # local window, or 3585..4096 global keys, the cached prefix included
     from paged_hybrid_kv_amd.synth import HybridShape
     _run_and_check(HybridShape(prompt_prefix=3584), "hybrid step, chunk after a 3584-token prefix")
+
+
+def test_decode_step_e4m3_graph_parity():
+    # the headline step with both families' pools in e4m3 (pegainfer PR
+    # #1012, Description: the opt-in fp8 pool; here the global family too)
+    _run_and_check(None, "decode step, e4m3 pools", with_prompts=False, e4m3=True)
+
+
+def test_hybrid_step_e4m3_graph_sampled_parity():
+    _run_and_check(None, "mixed step, e4m3 pools", e4m3=True)
