@@ -245,11 +245,13 @@ def _many_seqs(seed, n=150, max_len=300):
     return lens, q_len
 
 
-def test_local_many_sequences_in_call_append():
-    """150 sequences mixing decode and prompt rows, every row's token
-    appended in the call: all rows against the oracle, and the pool and the
-    outputs equal to a standalone append followed by the call."""
-    lens, q_len = _many_seqs(120)
+@pytest.mark.parametrize("n", [150, 300])
+def test_local_many_sequences_in_call_append(n):
+    """150 or 300 sequences mixing decode and prompt rows (300: past the 256
+    sequences the prompt-row item lookup holds in registers), every row's
+    token appended in the call: all rows against the oracle, and the pool
+    and the outputs equal to a standalone append followed by the call."""
+    lens, q_len = _many_seqs(120 if n == 150 else 125, n=n, max_len=300 if n == 150 else 160)
     case = SY.local_case("many local", 121, lens, window=64, num_q_heads=4, num_kv_heads=2,
                          q_len=q_len, rope=True, q_scale=0.5, kv_scale=0.5)
     dc_sep = RT.upload_local(case)
@@ -270,9 +272,10 @@ def test_local_many_sequences_in_call_append():
     assert np.array_equal(out_f, out_sep)
 
 
+@pytest.mark.parametrize("n", [150, 300])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_global_many_sequences_in_call_append(fp8):
-    lens, q_len = _many_seqs(130, max_len=400)
+def test_global_many_sequences_in_call_append(fp8, n):
+    lens, q_len = _many_seqs(130 if n == 150 else 135, n=n, max_len=400 if n == 150 else 200)
     case = SY.global_case("many global", 131, lens, num_q_heads=16, q_len=q_len, rope=True, fp8=fp8)
     dc_sep, out_sep = run_global(case)
     check(case, out_sep, "many global")
