@@ -32,7 +32,11 @@
 // been written) is zeroed in LDS on the range's edge steps.  e4m3 codes
 // convert to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), so the
 // products are the same as on the bf16 values.  P is rounded to bf16 for
-// PV and the sum l adds exactly those rounded values.  Workgroups are
+// PV and the sum l adds exactly those rounded values.  A prompt that lies
+// inside one window has row blocks whose ranges grow with the block; its
+// workgroups fold (half of an early block with the same half of the
+// mirrored late block), so they stream about the same work, and waves
+// skip the steps past their own rows.  Workgroups are
 // numbered compactly over the prompt sequences' row blocks, level by level
 // (every sequence's last block first, then every sequence's second last,
 // ...: the longest ranges of the call first), with the KV head as the
@@ -174,35 +178,62 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   q_len = uniform_i32(q_len);
   L = uniform_i32(L);
 
-  // rows r_first .. r_last at positions pos0 + r; their union range
+  // The item's rows: two halves of kRows / 2 rows, the first taken by
+  // waves 0 .. kWaves / 2 - 1, the second by the others.  Normally the two
+  // halves of row block rb.  A prompt that lies inside one window (every
+  // row attends from key 0: the ranges grow with the row block) folds:
+  // item rb < 2 (nb / 2) takes half rb % 2 of block rb / 2 and the same
+  // half of block nb - 1 - rb / 2, and the middle block of an odd count
+  // stays whole, so the prompt's items stream about the same work; a wave
+  // skips the steps past its own rows.
+  const int pos0 = L - q_len;
+  constexpr int kHalf = kRows / 2;
+  constexpr int kHalfWaves = kWaves / 2;
+  const int nb = cdiv_i(q_len, kRows);
+  const bool in_window = L <= a.window;
+  const bool fold = in_window && rb < 2 * (nb / 2);   // uniform
+  const int blk = in_window ? nb / 2 : rb;             // the whole block of an item that does not fold
+  const int ra = fold ? (rb >> 1) * kRows + (rb & 1) * kHalf : blk * kRows;
+  const int rbh = fold ? (nb - 1 - (rb >> 1)) * kRows + (rb & 1) * kHalf : blk * kRows + kHalf;
+  // rows r_first .. r_last (the first half's first row, the last valid
+  // row of either half) at positions pos0 + r; their union range
   // [lo_first, p_last] covers pages pg_lo .. pg_lo + n_pages - 1, walked in
   // steps of two pages (an odd count's last step repeats its last page as
   // the second, every token of which lies past p_last)
-  const int pos0 = L - q_len;
-  const int r_first = rb * kRows;
-  const int r_last = min(r_first + kRows, q_len) - 1;
+  const int r_first = ra;
+  const int r_last = rbh < q_len ? min(rbh + kHalf, q_len) - 1 : min(ra + kHalf, q_len) - 1;
   const int p_last = pos0 + r_last;
   const int lo_first = max(0, pos0 + r_first - a.window + 1);
   const int pg_lo = lo_first >> 4;
   const int n_pages = (p_last >> 4) - pg_lo + 1;
   const int n_steps = (n_pages + 1) >> 1;
-  // every row of the block attends [lo_max, p_min] (at least)
-  const int lo_max = max(0, pos0 + r_last - a.window + 1);
-  const int p_min = pos0 + r_first;
+  // this wave's rows: w_first .. w_last (valid rows only; none when
+  // w_last < w_first), which attend [lo_max, p_min] at least, and its last
+  // step
+  const int wh = w % kHalfWaves;
+  const int wbase = w < kHalfWaves ? ra : rbh;
+  const int w_first = wbase + (16 * QB * wh) / G;
+  const int w_last = min(min(wbase + (16 * QB * wh + 16 * QB - 1) / G, wbase + kHalf - 1), q_len - 1);
+  const int lo_max = max(0, pos0 + w_last - a.window + 1);
+  const int p_min = pos0 + w_first;
+  const int last_step = w_last < w_first ? -1 : (((pos0 + w_last) >> 4) - pg_lo) >> 1;
   GW_TRACE_VAT(a, trow, 0, tid == 0, GW_TRACE_XCC() | (uint64_t)rb << 8 | (uint64_t)gk << 16 | (uint64_t)s << 32);
   GW_TRACE_VAT(a, trow, 1, tid == 0, n_steps);
 
-  // this lane's two query vectors, v = 32 w + 16 qb + l16: row
-  // r_first + v / G, head v % G of the group; each masks its own window
-  int pq[QB], loq[QB];
+  // this lane's query vectors, v = 16 QB (w % (kWaves / 2)) + 16 qb + l16
+  // of its half: row (first row of the half) + v / G, head v % G of the
+  // group; each masks its own window (a row past the prompt computes on
+  // r_last's query and position and is not written)
+  int pq[QB], loq[QB], rq[QB];
   bool rok[QB];
   bf16x8 qf[QB][8];   // Q^T operand: dims 32 ks + 8 gq .. +7
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int v = 16 * QB * w + 16 * qb + l16;
-    const int r = r_first + v / G;
-    rok[qb] = r <= r_last;
+    const int v = 16 * QB * wh + 16 * qb + l16;
+    const int r = wbase + v / G;
+    rok[qb] = r < q_len;
     const int rr = rok[qb] ? r : r_last;
+    rq[qb] = r;
     pq[qb] = pos0 + rr;
     loq[qb] = max(0, pq[qb] - a.window + 1);
     const uint16_t* qp = a.q + ((int64_t)(row0 + rr) * a.num_q_heads + gk * G + v % G) * 256 + 8 * gq;
@@ -282,7 +313,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   lds_barrier();
   GW_TRACE_AT(a, trow, 3, tid == 0);
   f32x4 sc[2][QB];
-  scores(0, sc);
+  if (last_step >= 0) scores(0, sc);
   for (int j = 0; j < n_steps; ++j) {
     const int jn = min(j + 1, n_steps - 1);   // the last iteration recomputes its own step's scores, unused
     wait_groups_after<kPerStep>(max(0, min(n_steps - 2 - j, NS - 3)));
@@ -300,10 +331,12 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
       if (tid < 256) LH::zero_v_outside(ring[j % NS][0], ring[j % NS][1], tok0, lo_first, p_last, tid);
       lds_barrier();
     }
+    // a wave whose rows end before this step only keeps the ring moving
+    if (j > last_step) continue;
 
-    // ---- scaled scores z; a step inside every row's window and the rows'
-    // range (the common case) takes no masks (rows past the block's last
-    // compute on its last row's q and are not written)
+    // ---- scaled scores z; a step inside every row's window of the wave
+    // (the common case) takes no masks (rows past the prompt compute on
+    // r_last's q and are not written)
     const bool full = tok0 >= lo_max && tok0 + 31 <= p_min;
     float z[QB][8];
     if (full) {
@@ -390,8 +423,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void local_prefill_kernel(LocalAt
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = lacc[qb][0];
     if (!rok[qb]) continue;
-    const int v = 16 * QB * w + 16 * qb + l16;
-    float* op = a.out + ((int64_t)(row0 + r_first + v / G) * a.num_q_heads + gk * G + v % G) * 256 + 4 * gq;
+    const int v = 16 * QB * wh + 16 * qb + l16;
+    float* op = a.out + ((int64_t)(row0 + rq[qb]) * a.num_q_heads + gk * G + v % G) * 256 + 4 * gq;
     const float inv = 1.f / l_tot;
     // streaming stores: nothing in this step reads the rows' outputs again,
     // so they go out to memory now, while this kernel leaves HBM idle,
