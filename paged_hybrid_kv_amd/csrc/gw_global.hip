@@ -904,67 +904,141 @@ __device__ __forceinline__ void global_rows_page(f32x4 (&acc)[NR][32], float (&m
 }
 
 // Cross-split reduce: M = max_i m_i, l = sum_i l_i 2^(m_i - M),
-// out = sum_i acc_i 2^(m_i - M) / l, both sums in split order.  The
-// partials sit in MFMA fragment order (fragment (hb, block) of a split: 64
-// lanes x 4 floats, lane g*16 + l16 holding head 16 hb + l16, dims
-// 16 block + 4g .. +3), so each wave of the reduce takes one fragment of a
-// sequence and every load moves 1 KiB in one piece.  A thread merges its
-// lane's splits in chunks of kReduceChunk (one round trip per chunk; a
-// later chunk with a larger max rescales what came before).
+// out = sum_i acc_i 2^(m_i - M) / l.  The partials sit in MFMA fragment
+// order (fragment (hb, block) of a split: 64 lanes x 4 floats, lane
+// g*16 + l16 holding head 16 hb + l16, dims 16 block + 4g .. +3), so every
+// load moves 1 KiB in one piece.  The order of the additions depends on the
+// row's split count only: the splits go in chunks of kReduceChunk, each
+// chunk's state (its max, and l and acc relative to it, summed in split
+// order) is computed on its own in one round trip, and the chunk states are
+// folded in chunk order.  Two ways to schedule the same arithmetic:
+//   sequential: a wave per fragment folds its chunks one after another
+//     (four fragments per unit of 256 threads);
+//   parallel: the four waves of a unit take chunks 4r .. 4r + 3 of one
+//     fragment at once and the first folds them, round r after round r - 1
+//     (rows of many splits: C3's 64 splits in one round trip).
 constexpr int kReduceChunk = 16;
+constexpr int kReduceWaves = 4;
+// LDS of a parallel unit: the round's chunk states, [wave][m, l, acc x 4][lane]
+constexpr int kReduceLdsFloats = kReduceWaves * 6 * 64;
 
-// Sequence s, fragments 4y .. 4y + 3, by 256 threads (tid 0 .. 255).
+struct ReduceState {
+  float m, l;
+  f32x4 o;
+};
+
+// State of splits [c0, c0 + nc) of the fragment (pa, ml: the lane's split-0 records).
+__device__ __forceinline__ ReduceState reduce_chunk(const f32x4* pa, const float* ml, int64_t acc_step,
+                                                    int64_t ml_step, int c0, int nc) {
+  f32x4 v[kReduceChunk];
+  float2 x[kReduceChunk];
+#pragma unroll
+  for (int i = 0; i < kReduceChunk; ++i) {
+    v[i] = i < nc ? pa[(c0 + i) * acc_step] : f32x4{0.f, 0.f, 0.f, 0.f};
+    x[i] = i < nc ? *reinterpret_cast<const float2*>(ml + (c0 + i) * ml_step) : float2{-INFINITY, 0.f};
+  }
+  ReduceState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < kReduceChunk; ++i) st.m = fmaxf(st.m, x[i].x);
+#pragma unroll
+  for (int i = 0; i < kReduceChunk; ++i) {
+    if (i < nc) {
+      const float w = __builtin_amdgcn_exp2f(x[i].x - st.m);
+      st.l += x[i].y * w;
+      st.o += v[i] * w;
+    }
+  }
+  return st;
+}
+
+// acc <- acc folded with the next chunk's state c (an empty state, max
+// -inf, adds nothing; the first fold returns c exactly).
+__device__ __forceinline__ void reduce_fold(ReduceState& acc, const ReduceState& c) {
+  const float mn = fmaxf(acc.m, c.m);
+  const float wa = acc.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(acc.m - mn);
+  const float wc = c.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(c.m - mn);
+  acc.l = acc.l * wa + c.l * wc;
+  acc.o = acc.o * wa + c.o * wc;
+  acc.m = mn;
+}
+
+// The row and split count of decode sequence s (false: not a decode row,
+// or one split, written by the decode kernel itself).
+__device__ __forceinline__ bool reduce_row(const ReduceArgs& a, int s, int& row, int& nsplit) {
+  row = s;
+  if (a.q_indptr) {
+    row = a.q_indptr[s];
+    if (a.q_indptr[s + 1] - row != 1) return false;
+  }
+  nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
+  return nsplit > 1;
+}
+
+__device__ __forceinline__ void reduce_store(const ReduceArgs& a, int row, int frag, int lane, const ReduceState& st) {
+  const int head = 16 * (frag >> 5) + (lane & 15);
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + head) * kGD + 16 * (frag & 31) + 4 * (lane >> 4)) =
+      st.o / st.l;
+}
+
+// Sequential schedule: sequence s, fragments 4y .. 4y + 3, by 256 threads
+// (tid 0 .. 255), one wave per fragment.
 __device__ __forceinline__ void global_split_reduce_unit(const ReduceArgs& a, int s, int y, int tid) {
   const int lane = tid & 63;
   const int frag = y * 4 + (tid >> 6);   // hb * 32 + block
   const int hbs = a.num_q_heads / 16;
   if (frag >= hbs * 32) return;
-  int row = s;
-  if (a.q_indptr) {
-    row = a.q_indptr[s];
-    if (a.q_indptr[s + 1] - row != 1) return;
-  }
-  const int nsplit = global_nsplit(cdiv_i(a.seq_lens[s], kPage));
-  if (nsplit <= 1) return;
+  int row, nsplit;
+  if (!reduce_row(a, s, row, nsplit)) return;
   const int head = 16 * (frag >> 5) + (lane & 15);
   const f32x4* pa = reinterpret_cast<const f32x4*>(a.part_acc) + ((int64_t)s * a.max_splits * hbs * 32 + frag) * 64 + lane;
   const float* ml = a.part_ml + ((int64_t)s * a.max_splits * a.num_q_heads + head) * 2;
   const int64_t acc_step = (int64_t)hbs * 32 * 64, ml_step = 2 * (int64_t)a.num_q_heads;
-  float M = -INFINITY, lsum = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk) {
-    const int nc = min(kReduceChunk, nsplit - c0);
-    f32x4 v[kReduceChunk];
-    float2 x[kReduceChunk];
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) {
-      v[i] = i < nc ? pa[(c0 + i) * acc_step] : f32x4{0.f, 0.f, 0.f, 0.f};
-      x[i] = i < nc ? *reinterpret_cast<const float2*>(ml + (c0 + i) * ml_step) : float2{-INFINITY, 0.f};
-    }
-    float mc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) mc = fmaxf(mc, x[i].x);
-    const float mnew = fmaxf(M, mc);
-    if (mnew > M) {
-      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
-      o *= r;
-      lsum *= r;
-      M = mnew;
-    }
-#pragma unroll
-    for (int i = 0; i < kReduceChunk; ++i) {
-      if (i < nc) {
-        const float w = __builtin_amdgcn_exp2f(x[i].x - M);
-        lsum += x[i].y * w;
-        o += v[i] * w;
-      }
-    }
-  }
-  *reinterpret_cast<f32x4*>(a.out + ((int64_t)row * a.num_q_heads + head) * kGD + 16 * (frag & 31) + 4 * (lane >> 4)) =
-      o / lsum;
+  ReduceState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int c0 = 0; c0 < nsplit; c0 += kReduceChunk)
+    reduce_fold(st, reduce_chunk(pa, ml, acc_step, ml_step, c0, min(kReduceChunk, nsplit - c0)));
+  reduce_store(a, row, frag, lane, st);
 }
 
-// Fragment groups per sequence: 32 fragments per head block, four per unit.
+// Parallel schedule: sequence s (blockIdx.x), fragment blockIdx.y.
+__global__ __launch_bounds__(256) void global_split_reduce_par_kernel(ReduceArgs a) {
+  __shared__ float red[kReduceLdsFloats];
+  const int s = blockIdx.x, frag = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, k = tid >> 6;
+  int row, nsplit;
+  if (!reduce_row(a, s, row, nsplit)) return;   // uniform over the workgroup
+  const int hbs = a.num_q_heads / 16;
+  const int head = 16 * (frag >> 5) + (lane & 15);
+  const f32x4* pa = reinterpret_cast<const f32x4*>(a.part_acc) + ((int64_t)s * a.max_splits * hbs * 32 + frag) * 64 + lane;
+  const float* ml = a.part_ml + ((int64_t)s * a.max_splits * a.num_q_heads + head) * 2;
+  const int64_t acc_step = (int64_t)hbs * 32 * 64, ml_step = 2 * (int64_t)a.num_q_heads;
+  const int nchunk = cdiv_i(nsplit, kReduceChunk);
+  ReduceState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int r0 = 0; r0 < nchunk; r0 += kReduceWaves) {
+    const int c = r0 + k;
+    const ReduceState cs = c < nchunk ? reduce_chunk(pa, ml, acc_step, ml_step, c * kReduceChunk,
+                                                     min(kReduceChunk, nsplit - c * kReduceChunk))
+                                      : ReduceState{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    float* q = red + k * 6 * 64 + lane;
+    q[0] = cs.m;
+    q[64] = cs.l;
+    q[128] = cs.o[0];
+    q[192] = cs.o[1];
+    q[256] = cs.o[2];
+    q[320] = cs.o[3];
+    __syncthreads();
+    if (k == 0) {
+      for (int j = 0; j < kReduceWaves && r0 + j < nchunk; ++j) {
+        const float* qj = red + j * 6 * 64 + lane;
+        reduce_fold(st, ReduceState{qj[0], qj[64], f32x4{qj[128], qj[192], qj[256], qj[320]}});
+      }
+    }
+    __syncthreads();
+  }
+  if (k == 0) reduce_store(a, row, frag, lane, st);
+}
+
+// Fragment groups per sequence of the sequential schedule: 32 fragments
+// per head block, four per unit.
 __host__ __device__ constexpr int reduce_groups(int num_q_heads) { return num_q_heads / 16 * 32 / 4; }
 
 __global__ __launch_bounds__(256) void global_split_reduce_kernel(ReduceArgs a) {
@@ -1137,8 +1211,15 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
 }  // namespace
 
 hipError_t launch_split_reduce(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs, reduce_groups(a.num_q_heads)), block(256);
-  hipLaunchKernelGGL(global_split_reduce_kernel, grid, block, 0, stream, a);
+  // rows of more than two chunks of splits take the parallel schedule (the
+  // same arithmetic: the choice moves no result)
+  if (a.max_splits > 2 * kReduceChunk) {
+    dim3 grid(num_seqs, a.num_q_heads / 16 * 32), block(256);
+    hipLaunchKernelGGL(global_split_reduce_par_kernel, grid, block, 0, stream, a);
+  } else {
+    dim3 grid(num_seqs, reduce_groups(a.num_q_heads)), block(256);
+    hipLaunchKernelGGL(global_split_reduce_kernel, grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

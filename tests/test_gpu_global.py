@@ -112,6 +112,26 @@ def test_repeat_determinism():
     assert np.array_equal(o1, o2)
 
 
+def test_reduce_schedules_bitexact():
+    """The cross-split reduce has two schedules of the same arithmetic, picked
+    from the call's largest split count: a row of 29 splits alone takes the
+    sequential one, beside a row of 63 splits the parallel one.  The row's
+    result must not depend on which (nor on the row's place in the batch);
+    the 63-split row is checked against the oracle."""
+    both = SY.global_case("sched", 37, [20000, 9000], rope=True)
+    alone = SY.global_case("sched", 38, [9000], rope=True)
+    sel = both.tok_seq == 1
+    alone.q = both.q[1:2]
+    alone.v, alone.tok_pos = both.v[sel], both.tok_pos[sel]
+    alone.tok_seq = np.zeros(int(sel.sum()), both.tok_seq.dtype)
+    for compressed in (True, False):
+        _, ob = run(both, compressed)
+        _, oa = run(alone, compressed)
+        assert np.array_equal(ob[1:2], oa), f"schedules differ (compressed={compressed})"
+    mx = check(both, ob, "reduce schedules", seqs=[0])
+    print(f"63-split row max abs err {mx:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("compressed", [True, False])
 def test_append_global(compressed):
     case = SY.global_case("append", 37, [40, 17, 300], rope=True, extra_pages=2)
