@@ -504,9 +504,9 @@ int gw_decode_attn_global(const gw_pool_desc* pool, const void* q, int32_t num_q
     return fail(GW_ERR_UNSUPPORTED, fn, "%lld decode workgroups and %lld append workgroups (served: up to %lld)",
                 (long long)w.max_splits * num_seqs, (app_units + 1) / 2, kMaxGrid);
   if (max_q_len > 1) {
-    // the prompt rows' items, then the decode rows' reduce (two units of 256 threads per workgroup)
+    // the decode rows' reduce (two units of 256 threads per workgroup), then the prompt rows' items
     const long long pre_wgs = gw::prefill_items(num_rows, num_seqs, max_q_len, gw::global_prefill_rows(num_q_heads)) +
-                              (w.max_splits > 1 ? ((long long)num_seqs * (num_q_heads / 16 * 32 / 4) + 1) / 2 : 0);
+                              (w.max_splits > 1 ? ((long long)num_seqs * gw::reduce_groups(num_q_heads) + 1) / 2 : 0);
     if (pre_wgs > kMaxGrid)
       return fail(GW_ERR_UNSUPPORTED, fn, "%lld prompt-row workgroups (served: up to %lld)", pre_wgs, kMaxGrid);
   }

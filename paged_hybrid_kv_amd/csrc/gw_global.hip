@@ -1037,10 +1037,6 @@ __global__ __launch_bounds__(256) void global_split_reduce_par_kernel(ReduceArgs
   if (k == 0) reduce_store(a, row, frag, lane, st);
 }
 
-// Fragment groups per sequence of the sequential schedule: 32 fragments
-// per head block, four per unit.
-__host__ __device__ constexpr int reduce_groups(int num_q_heads) { return num_q_heads / 16 * 32 / 4; }
-
 __global__ __launch_bounds__(256) void global_split_reduce_kernel(ReduceArgs a) {
   global_split_reduce_unit(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
@@ -1077,11 +1073,12 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   // loop done
   const int trow = kTracePrefillRow + (int)blockIdx.x;
   GW_TRACE_AT(a, trow, 2, tid == 0);
-  // the workgroups past the prompt-row items merge the decode rows' splits
-  // (the decode kernel, an earlier launch, wrote them), two units of 256
-  // threads each
-  if ((int)blockIdx.x >= a.reduce_wg0) {
-    const int u = ((int)blockIdx.x - a.reduce_wg0) * 2 + tid / 256;
+  // the first reduce_wgs workgroups merge the decode rows' splits (the
+  // decode kernel, an earlier launch, wrote them), two units of 256 threads
+  // each; placed ahead of the prompt-row items, their short work folds into
+  // the items' schedule instead of trailing it
+  if ((int)blockIdx.x < a.reduce_wgs) {
+    const int u = (int)blockIdx.x * 2 + tid / 256;
     const int groups = reduce_groups(a.num_q_heads);
     if (u < a.num_seqs * groups) {
       const ReduceArgs r{a.q_indptr, a.seq_lens, a.part_acc, a.part_ml, a.out, a.num_q_heads, a.max_splits};
@@ -1098,7 +1095,7 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   int s = -1, mg = 0, row0 = 0, q_len = 0, L = 0;
   {
     PromptItem it;
-    if (prompt_item(a.q_indptr, a.seq_lens, a.num_seqs, kRows, (int)blockIdx.x, lane, it)) {
+    if (prompt_item(a.q_indptr, a.seq_lens, a.num_seqs, kRows, (int)blockIdx.x - a.reduce_wgs, lane, it)) {
       s = it.s;
       mg = it.grp;
       row0 = it.row0;
@@ -1253,10 +1250,10 @@ hipError_t launch_global_decode(const GlobalAttnArgs& a_in, bool compressed, boo
 
 hipError_t launch_global_prefill(const GlobalAttnArgs& a_in, bool compressed, bool fp8, int max_q_len,
                                  hipStream_t stream) {
-  // one workgroup per (prompt sequence, group of 8 / HB rows) (the entry
-  // point has checked that the count fits a grid), then the decode rows'
-  // cross-split reduce (two units of 256 threads per workgroup) when the
-  // decode rows have splits
+  // the decode rows' cross-split reduce (two units of 256 threads per
+  // workgroup) when the decode rows have splits, then one workgroup per
+  // (prompt sequence, group of 8 / HB rows) (the entry point has checked
+  // that the count fits a grid)
   const bool h32 = a_in.num_q_heads == 32;
   const long long items =
       prefill_items(a_in.num_rows, a_in.num_seqs, max_q_len, global_prefill_rows(a_in.num_q_heads));
@@ -1265,7 +1262,7 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a_in, bool compressed, bo
   if (items + n_red == 0) return hipSuccess;
   if (items + n_red > 0x7fffffff) return hipErrorInvalidConfiguration;
   GlobalAttnArgs a = a_in;
-  a.reduce_wg0 = (int32_t)items;
+  a.reduce_wgs = (int32_t)n_red;
   dim3 grid((unsigned)(items + n_red)), block(512);
 #define GW_GPREFILL_CASE(C_, F_)                                                                      \
   if (compressed == C_ && fp8 == F_) {                                                                \

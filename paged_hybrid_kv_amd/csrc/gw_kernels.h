@@ -68,8 +68,8 @@ struct GlobalAttnArgs {
   int32_t append_units;
   int32_t append_wg0;
   // calls with prompt rows: the decode rows' cross-split reduce runs in the
-  // prompt-row kernel's workgroups from reduce_wg0 on
-  int32_t reduce_wg0;
+  // prompt-row kernel's first reduce_wgs workgroups
+  int32_t reduce_wgs;
   uint64_t* trace;            // per-workgroup event times (trace builds only), else null
 };
 

@@ -78,6 +78,11 @@ inline long long prefill_items(long long num_rows, long long num_seqs, long long
   return by_rows < by_len ? by_rows : by_len;
 }
 
+// Units of 256 threads of the global cross-split reduce per decode
+// sequence, in its sequential schedule: four 16-head x 16-dim output
+// fragments each (32 fragments per block of 16 q heads).
+__host__ __device__ constexpr int reduce_groups(int num_q_heads) { return num_q_heads / 16 * 32 / 4; }
+
 // Page items of the prompt rows' append in an attention call: a sequence
 // of q rows touches at most (q + 14) / 16 + 1 pages, so the call at most
 // (rows + 30 sequences) / 16 (and at most sequences * pages of max_q_len).
