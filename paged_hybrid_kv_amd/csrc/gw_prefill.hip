@@ -448,7 +448,7 @@ hipError_t launch_local_prefill(const LocalAttnArgs& a, int group, bool fp8, int
   const dim3 grid((unsigned)n), block(64 * (8 / kPrefillQB));
 #define GW_PREFILL_CASE(G_, F_)                                                                     \
   if (group == G_ && fp8 == F_) {                                                                   \
-    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 4, kPrefillQB>), grid, block, 0, stream, a);   \
+    hipLaunchKernelGGL((local_prefill_kernel<G_, F_, 3, kPrefillQB>), grid, block, 0, stream, a);   \
     return hipGetLastError();                                                                       \
   }
   GW_PREFILL_CASE(1, false) GW_PREFILL_CASE(2, false) GW_PREFILL_CASE(4, false)
