@@ -1266,8 +1266,8 @@ hipError_t launch_global_prefill(const GlobalAttnArgs& a_in, bool compressed, bo
   dim3 grid((unsigned)(items + n_red)), block(512);
 #define GW_GPREFILL_CASE(C_, F_)                                                                      \
   if (compressed == C_ && fp8 == F_) {                                                                \
-    if (h32) hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 2, 1, 4>), grid, block, 0, stream, a); \
-    else hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 1, 1, 4>), grid, block, 0, stream, a);     \
+    if (h32) hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 2, 1, 3>), grid, block, 0, stream, a); \
+    else hipLaunchKernelGGL((global_prefill_kernel<C_, F_, 1, 1, 3>), grid, block, 0, stream, a);     \
     return hipGetLastError();                                                                         \
   }
   GW_GPREFILL_CASE(true, false) GW_GPREFILL_CASE(false, false) GW_GPREFILL_CASE(true, true)
