@@ -277,9 +277,10 @@ __global__ __launch_bounds__(512, 1) void global_decode_ws_kernel(GlobalAttnArgs
   constexpr int kXsBytes = HB * 4 * 1024;     // one pair's partial scores: [page][dim half][hb][lane] f32x4
   constexpr int kXsOff = NS * kSlot;
   // pages issued before the loop: every slot q does not hold, at most 10
-  // (so that no wait below counts more than 31 transfers of a score wave)
+  // (so that no wait below counts more than 31 transfers of a score wave),
+  // and at least pairs 0 and 1: step 1 waits for pair 1 before it issues
   constexpr int kPro = NS - kQPages < 10 ? NS - kQPages : 10;
-  static_assert(NS >= 6 && kPro >= 2 && (NS - 4) * ((kU + 3) / 4) <= 31 && kPro * ((kU + 3) / 4) <= 31, "ring depth");
+  static_assert(NS >= 6 && kPro >= 4 && (NS - 4) * ((kU + 3) / 4) <= 31 && kPro * ((kU + 3) / 4) <= 31, "ring depth");
   static_assert(!FP8 || NS % 2 == 0, "an e4m3 pair's pages sit side by side");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kXsOff + 2 * kXsBytes];
 
