@@ -1064,7 +1064,8 @@ __global__ __launch_bounds__(64 * (8 / NR), 1) void global_prefill_kernel(Global
   constexpr int kPerWaveTail = kUnits % kW;   // ... the first kUnits % kW waves one more
   constexpr int kRows = kW * NR / HB;         // rows per workgroup
   static_assert(NR != 1 || kRows == global_prefill_rows(16 * HB), "the host's item count");
-  static_assert(NS >= 2 && NS - 2 <= 4 && (kPerWave + 1) * (NS - 2) < 64, "ring depth");
+  // NS >= 3: iteration i reads page i + 1, issued an iteration earlier
+  static_assert(NS >= 3 && NS - 2 <= 4 && (kPerWave + 1) * (NS - 2) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][PG::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
