@@ -59,7 +59,7 @@ namespace {
 constexpr int kGD = 512;
 
 // LDS ring depth: page slots of the wave-specialised kernel for the bf16
-// compressed record (7 x 20 KiB), e4m3 compressed (14 x 10 KiB) and e4m3
+// compressed record (7 x 20 KiB), e4m3 compressed (8 x 10 KiB) and e4m3
 // full (8 x 16 KiB), and pair slots of the full bf16 record's kernel
 // (2 x 64 KiB); with the score exchange, one workgroup per CU.
 #ifndef GW_GLOBAL_NS_C
@@ -69,7 +69,7 @@ constexpr int kGD = 512;
 #define GW_GLOBAL_NP_F 2
 #endif
 #ifndef GW_GLOBAL_NS_C8
-#define GW_GLOBAL_NS_C8 14
+#define GW_GLOBAL_NS_C8 8
 #endif
 #ifndef GW_GLOBAL_NS_F8
 #define GW_GLOBAL_NS_F8 8
