@@ -656,15 +656,21 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
 
   __shared__ uint32_t sm_tok[kLocalWaves][128];   // a patching wave's rotated token K
   if constexpr (SPW == 1) {
-  PageRegs<FP8> A, B;
-  VPage dA{}, dB{};
+  // One page buffer per wave: a page's loads are issued as soon as the page
+  // before it has been processed, so a wave has one page in flight while it
+  // waits and none while it computes.  Two or three buffers per wave (the
+  // next pages loading while one is processed) measured slower: the CU's
+  // eight waves keep enough in flight, and more queued transfers only
+  // lengthen each one's wait.
+  PageRegs<FP8> A;
+  VPage dA{}, dn{};   // this page's descriptor, the next page's
   if (nw > 0) {
     const bool patch = append_here && tok_wave;
     NewTokenLoads tok{};
     if (patch) tok = load_new_token(a, row, g, p, lane);
     dA = vpage(k_of(0));
     load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
-    if (nw > 1) dB = vpage(k_of(1));
+    if (nw > 1) dn = vpage(k_of(1));
     if (patch) {
       const int id_tok = pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl];
       uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)id_tok * a.page_bytes;
@@ -672,18 +678,13 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
     }
   }
   if (nsplit > 1) epoch = load_epoch();
-  for (int i = 0; i < nw; i += 2) {
-    if (i + 1 < nw) load_vpage<FP8>(B, dB.r0, dB.r1, dB.b, lane);
-    const VPage dA2 = i + 2 < nw ? vpage(k_of(i + 2)) : dA;
+  for (int j = 0; j < nw; ++j) {
     process_page<G, FP8>(A, qr, qh, dA.mask, dA.b, a.scale_log2, lane, m_run, l_run, acc);
-    if (i + 1 >= nw) break;
-    if (i + 2 < nw) {
-      dA = dA2;
+    if (j + 1 < nw) {
+      dA = dn;
       load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
+      if (j + 2 < nw) dn = vpage(k_of(j + 2));
     }
-    const VPage dB2 = i + 3 < nw ? vpage(k_of(i + 3)) : dB;
-    process_page<G, FP8>(B, qr, qh, dB.mask, dB.b, a.scale_log2, lane, m_run, l_run, acc);
-    dB = dB2;
   }
 
   asm volatile("" : "+v"(epoch));
@@ -838,6 +839,10 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
     const bool patch = append_here && tok_w;
     NewTokenLoads tok{};
     if (patch) tok = load_new_token(a, row, g, p, lane);
+    // bf16 pages: two buffers, the next item loading while one is processed;
+    // e4m3 pages: one buffer, loaded once the item before it is processed
+    // (faster for e4m3 at 64 x 8192, slower for bf16 at group size 4)
+    constexpr bool kOneBuf = FP8;
     PageRegs<FP8> A, B;
     VPage dA{}, dB{};
     if (real(0, 0)) {
@@ -845,28 +850,33 @@ __global__ __launch_bounds__(64 * local_waves(G), 1) void local_decode_kernel(Lo
       load_vpage<FP8>(A, dA.r0, dA.r1, dA.b, lane);
     }
     if (nsplit > 1 && !covers_all) epoch = load_epoch();
-    // item (i, J): prefetch the next item into the other buffer, then
-    // process this one with split J's state
+    // item (i, J): with two buffers, prefetch the next item into the other
+    // buffer, then process this one with split J's state; with one, process
+    // it, then load the next
     auto item = [&](auto jc, int i) __attribute__((always_inline)) {
       constexpr int J = decltype(jc)::value;
       constexpr int kNj = (J + 1) % SPW;
-      PageRegs<FP8>& cur = pick<J % 2 == 0>(A, B);
-      PageRegs<FP8>& nxt = pick<J % 2 == 0>(B, A);
+      PageRegs<FP8>& cur = kOneBuf ? A : pick<J % 2 == 0>(A, B);
+      PageRegs<FP8>& nxt = kOneBuf ? A : pick<J % 2 == 0>(B, A);
+      VPage& dcur = kOneBuf ? dA : pick<J % 2 == 0>(dA, dB);
+      VPage& dnxt = kOneBuf ? dA : pick<kNj % 2 == 0>(dA, dB);
       const int ni = J + 1 < SPW ? i : i + 1;
-      if (real(kNj, ni)) {
-        const VPage nd = vpage_at(v0s[kNj], k_at(kNj, ni));
-        pick<kNj % 2 == 0>(dA, dB) = nd;
-        load_vpage<FP8>(nxt, nd.r0, nd.r1, nd.b, lane);
+      if (!kOneBuf && real(kNj, ni)) {
+        dnxt = vpage_at(v0s[kNj], k_at(kNj, ni));
+        load_vpage<FP8>(nxt, dnxt.r0, dnxt.r1, dnxt.b, lane);
       }
-      const VPage& dc = pick<J % 2 == 0>(dA, dB);
       const bool rl = real(J, i);
       if (patch && rl && i == 0 && J == j_tok) {
         const int id_tok = pt_lds ? uniform_i32(sm_pt[win.pgl]) : pt[win.pgl];
         uint8_t* rec = const_cast<uint8_t*>(head_base) + (int64_t)id_tok * a.page_bytes;
         put_new_token<FP8>(cur, rec, tok, a.rope_cos != nullptr, p, lane, sm_tok[w]);
       }
-      process_page<G, FP8>(cur, qr, qh, rl ? dc.mask : 0u, rl ? dc.b : 0, a.scale_log2, lane, m_s[J], l_s[J],
+      process_page<G, FP8>(cur, qr, qh, rl ? dcur.mask : 0u, rl ? dcur.b : 0, a.scale_log2, lane, m_s[J], l_s[J],
                            acc_s[J]);
+      if (kOneBuf && real(kNj, ni)) {
+        dnxt = vpage_at(v0s[kNj], k_at(kNj, ni));
+        load_vpage<FP8>(nxt, dnxt.r0, dnxt.r1, dnxt.b, lane);
+      }
     };
     for (int i = 0; i < nw_max; ++i) {
       item(SplitIndex<0>{}, i);
